@@ -1,0 +1,158 @@
+"""CPU oracle for the paged MQA-logits path (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the bench's CPU-baseline leg may import
+this package. It never imports the GPU package, and the GPU package never
+imports it; the two share only the seeded input generator ``pml_synth``.
+
+``oracle.c`` holds the fp64 reference of the scores, the masking and the
+top-k; ``brute.py`` is a second, numpy-only formulation for tiny inputs;
+``schedule.py`` is the specification of the work split that the metadata
+call produces.
+
+Parity unpinned: the pages print no worked example and no numeric value for
+this path, so no stored value comes from them; the pins are the format
+definitions, closed forms, invariants and brute force listed in the tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "oracle.c"
+_LIB = _HERE / "liboracle.so"
+_lib = None
+
+
+def build(force: bool = False) -> Path:
+    """Compile oracle.c with gcc (-O2, OpenMP) into liboracle.so next to it."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(".so.tmp")
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(_SRC), "-o", str(tmp), "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path) -> ctypes.CDLL:
+    L = ctypes.CDLL(str(path))
+    u8p = ctypes.c_void_p
+    L.pml_oracle_fp8_e4m3.restype = ctypes.c_double
+    L.pml_oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+    L.pml_oracle_e2m1.restype = ctypes.c_double
+    L.pml_oracle_e2m1.argtypes = [ctypes.c_uint8]
+    L.pml_oracle_e8m0.restype = ctypes.c_double
+    L.pml_oracle_e8m0.argtypes = [ctypes.c_uint8]
+    L.pml_oracle_paged_logits.restype = None
+    L.pml_oracle_paged_logits.argtypes = [
+        u8p, ctypes.c_int, ctypes.c_int, u8p, u8p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int64, u8p, ctypes.c_int, ctypes.c_int, u8p,
+        ctypes.c_int64, u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
+    L.pml_oracle_ragged_logits.restype = None
+    L.pml_oracle_ragged_logits.argtypes = [
+        u8p, ctypes.c_int, ctypes.c_int, u8p, u8p, u8p, ctypes.c_int, u8p, u8p,
+        u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
+    L.pml_oracle_topk.restype = None
+    L.pml_oracle_topk.argtypes = [u8p, ctypes.c_int, ctypes.c_int64, u8p, u8p, ctypes.c_int, u8p]
+    L.pml_oracle_num_threads.restype = ctypes.c_int
+    return L
+
+
+def lib():
+    """The oracle library; ``use_library`` can point it at another build."""
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def use_library(path) -> None:
+    """Bind the wrappers below to another compiled oracle (the mutation tests do)."""
+    global _lib
+    _lib = _bind(path) if path is not None else None
+
+
+def _np(t, dtype):
+    a = t.numpy() if hasattr(t, "numpy") else np.asarray(t)
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fp8_e4m3(code: int) -> float:
+    return lib().pml_oracle_fp8_e4m3(code)
+
+
+def e2m1(nib: int) -> float:
+    return lib().pml_oracle_e2m1(nib)
+
+
+def e8m0(code: int) -> float:
+    return lib().pml_oracle_e8m0(code)
+
+
+def paged_logits(case, rows=None, col_begin: int = 0, col_end: int | None = None) -> np.ndarray:
+    """fp64 logits of a ``pml_synth.PagedCase`` for the given rows and columns."""
+    q = _np(case.q, np.uint8)
+    w = _np(case.weights, np.float32)
+    kv = _np(case.kv_cache, np.uint8)
+    lens = _np(case.context_lens, np.int32)
+    bt = _np(case.block_table, np.int32)
+    if rows is None:
+        rows = np.arange(case.rows)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if col_end is None:
+        col_end = case.max_ctx
+    out = np.empty((len(rows), col_end - col_begin), dtype=np.float64)
+    if out.size:
+        lib().pml_oracle_paged_logits(
+            _ptr(q), case.H, case.D, _ptr(w), _ptr(kv), case.kv_format, case.block_kv,
+            kv.shape[1], kv.shape[0], _ptr(lens), int(case.lens_2d), case.next_n,
+            _ptr(bt), bt.shape[1] if bt.ndim == 2 else 0, _ptr(rows), len(rows),
+            col_begin, col_end, _ptr(out))
+    return out
+
+
+def ragged_logits(case, rows=None, col_begin: int = 0, col_end: int | None = None) -> np.ndarray:
+    """fp64 logits of a ``pml_synth.RaggedCase`` for the given rows and columns."""
+    q = _np(case.q, np.uint8)
+    w = _np(case.weights, np.float32)
+    k = _np(case.k, np.uint8)
+    ksc = _np(case.k_scale, np.float32)
+    ks = _np(case.ks, np.int32)
+    ke = _np(case.ke, np.int32)
+    if rows is None:
+        rows = np.arange(case.M)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    if col_end is None:
+        col_end = case.N
+    out = np.empty((len(rows), col_end - col_begin), dtype=np.float64)
+    if out.size:
+        lib().pml_oracle_ragged_logits(
+            _ptr(q), case.H, case.D, _ptr(w), _ptr(k), _ptr(ksc), case.N, _ptr(ks), _ptr(ke),
+            _ptr(rows), len(rows), col_begin, col_end, _ptr(out))
+    return out
+
+
+def topk(scores: np.ndarray, ke, k: int, ks=None) -> np.ndarray:
+    """Per-row top-k positions (relative to ks) in ascending order, -1 padded."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    rows = s.shape[0]
+    ke_a = np.ascontiguousarray(ke, dtype=np.int32)
+    ks_a = None if ks is None else np.ascontiguousarray(ks, dtype=np.int32)
+    out = np.empty((rows, k), dtype=np.int32)
+    if rows:
+        lib().pml_oracle_topk(_ptr(s), rows, s.shape[1], None if ks_a is None else _ptr(ks_a),
+                              _ptr(ke_a), k, _ptr(out))
+    return out
+
+
+def num_threads() -> int:
+    return lib().pml_oracle_num_threads()

@@ -1,0 +1,100 @@
+"""Specification of the work split returned by the metadata call (test infrastructure).
+
+The pages fix only the shape of this output: one entry per persistent worker
+plus one ("schedule.shape[0] - 1" is the number of SMs, sparse_attn_indexer
+page, _varlen_decode_rows) and that a row slice needs its own schedule. Its
+content is this library's own definition, stated here in plain Python:
+
+* Rows are grouped as the varlen decode path groups them ("[Bugfix]
+  [GLM-5.3-Flash] ...", Purpose: consecutive equal request indices are one
+  request): with ``indices`` a group is a maximal run of equal consecutive ids;
+  without, a group is the ``next_n`` rows of one batch entry.
+* A group is cut into pieces of at most ``G_MAX`` consecutive rows.
+* A piece's extent is the largest visible length among its rows; it has
+  ``nblk = ceil(extent / block_kv)`` key blocks, each costing ``COST_BASE + g``
+  (g = rows in the piece: one page read plus g rows of scoring).
+* Units (piece, block) are ordered by piece then block. Worker c starts at
+  the unit holding cost offset floor(c * T / W) of the total T; entry W is
+  the end sentinel (num_rows, 0).
+
+Entries are (first row of the piece, block offset within the piece).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+G_MAX = 8
+COST_BASE = 4
+
+
+def visible_lengths(context_lens: np.ndarray, num_rows: int, next_n: int, lens_2d: bool) -> np.ndarray:
+    lens = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    if lens_2d or next_n == 1:
+        v = lens[:num_rows].copy()
+    else:
+        r = np.arange(num_rows)
+        v = lens[r // next_n] - next_n + (r % next_n) + 1
+    return np.maximum(v, 0)
+
+
+def pieces(num_rows: int, next_n: int, indices) -> list[tuple[int, int]]:
+    """(first row, row count) of every piece, in row order."""
+    out = []
+    r = 0
+    while r < num_rows:
+        if indices is not None:
+            end = r
+            while end < num_rows and indices[end] == indices[r]:
+                end += 1
+        else:
+            end = min(num_rows, (r // next_n + 1) * next_n)
+        s = r
+        while s < end:
+            g = min(G_MAX, end - s)
+            out.append((s, g))
+            s += g
+        r = end
+    return out
+
+
+def piece_table(context_lens, num_rows, next_n, lens_2d, indices, block_kv):
+    vis = visible_lengths(context_lens, num_rows, next_n, lens_2d)
+    idx = None if indices is None else np.asarray(indices).reshape(-1)
+    table = []
+    for s, g in pieces(num_rows, next_n, idx):
+        ext = int(vis[s: s + g].max())
+        nblk = -(-ext // block_kv)
+        table.append((s, g, nblk, nblk * (COST_BASE + g)))
+    return table
+
+
+def schedule(context_lens, num_rows: int, next_n: int, lens_2d: bool, indices, block_kv: int,
+             num_workers: int) -> np.ndarray:
+    table = piece_table(context_lens, num_rows, next_n, lens_2d, indices, block_kv)
+    total = sum(t[3] for t in table)
+    out = np.zeros((num_workers + 1, 2), dtype=np.int32)
+    out[num_workers] = (num_rows, 0)
+    for c in range(num_workers):
+        if total == 0:
+            out[c] = (num_rows, 0)
+            continue
+        target = c * total // num_workers
+        cum = 0
+        for s, g, nblk, cost in table:
+            if cum <= target < cum + cost:
+                out[c] = (s, (target - cum) // (COST_BASE + g))
+                break
+            cum += cost
+    return out
+
+
+def units_of_worker(sched: np.ndarray, table, c: int) -> list[tuple[int, int]]:
+    """Enumerate the (first row, block) units worker c processes."""
+    start = tuple(sched[c])
+    end = tuple(sched[c + 1])
+    units = []
+    for s, g, nblk, cost in table:
+        for b in range(nblk):
+            if start <= (s, b) < end:
+                units.append((s, b))
+    return units
