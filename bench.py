@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of the paged MQA-logits hot path on one MI355X.
+
+One step = the whole decode path over one batch of synthetic input:
+schedule (paged_mqa_logits_metadata) -> paged logits (fp8_fp4_paged_mqa_logits)
+-> per-row top-k (top_k_per_row). The workload is the varlen speculative-decode
+batch: 40 requests with contexts U[100K, 128K] tokens and accepted draft lengths
+U{1..6}, flattened into rows that share K reads per request, fp8 K cache with
+block_kv 64, H = 64, D = 128, top-k 2048.
+
+Inputs are resident in HBM before the timed region. Steps rotate over
+independent copies of the key cache (together larger than the 256 MB last-level
+cache), so each step streams its keys from HBM. HIP events on the launch stream
+time every kernel inside the timed region; the JSON line reports the whole-step
+rate plus the logits kernel against the HBM roofline, and a bounded sample of
+the same workload scored by the CPU oracle.
+
+  python bench.py [--steps K] [--warmup W] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import paged_mqa_logits_amd as pml  # noqa: E402
+import pml_synth as syn  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+BYTES_PER_TOKEN = {syn.KV_FP8: 132, syn.KV_FP4: 68}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="key-cache copies rotated over the steps")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="also time the other workloads (one JSON line each on stderr)")
+    return ap.parse_args()
+
+
+class PagedBench:
+    """Device copies of one paged case and the three calls of one step."""
+
+    def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None):
+        d = torch.device("cuda:0")
+        self.case = case
+        self.q = case.q.to(d)
+        self.w = case.weights.to(d)
+        self.lens = case.context_lens.to(d)
+        self.bt = case.block_table.to(d)
+        self.indices = None if case.indices is None else case.indices.to(d)
+        self.kv = [case.kv_cache.to(d) for _ in range(max(1, copies))]
+        self.num_cus = num_cus or pml.default_num_workers()
+        self.sched = torch.empty(self.num_cus + 1, 2, dtype=torch.int32, device=d)
+        self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
+        self.topk = torch.empty(case.rows, case.topk, dtype=torch.int32, device=d)
+        self.req_tokens = int(sum(case.req_ctx))
+        self.pairs = syn.scored_pairs(case)
+
+    def step(self, i: int, ev=None):
+        c = self.case
+        if ev is not None:
+            ev[0].record()
+        pml.paged_mqa_logits_metadata(self.lens, c.block_kv, self.num_cus, indices=self.indices,
+                                      next_n=c.next_n, out=self.sched)
+        if ev is not None:
+            ev[1].record()
+        pml.fp8_fp4_paged_mqa_logits(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt, self.sched,
+                                     c.max_ctx, self.indices, kv_format=c.kv_format, block_kv=c.block_kv,
+                                     next_n=c.next_n, logits=self.logits)
+        if ev is not None:
+            ev[2].record()
+        pml.top_k_per_row(self.logits, self.lens, c.topk, next_n=c.next_n, max_width=c.max_ctx, out=self.topk)
+        if ev is not None:
+            ev[3].record()
+
+
+class RaggedBench:
+    def __init__(self, case: syn.RaggedCase):
+        d = torch.device("cuda:0")
+        self.case = case
+        self.q, self.k, self.ksc = case.q.to(d), case.k.to(d), case.k_scale.to(d)
+        self.w, self.ks, self.ke = case.weights.to(d), case.ks.to(d), case.ke.to(d)
+        self.logits = torch.empty(case.M, pml.logits_ld(case.N), dtype=torch.float32, device=d)
+        self.topk = torch.empty(case.M, case.topk, dtype=torch.int32, device=d)
+        self.pairs = int((case.ke - case.ks).clamp_min(0).sum())
+
+    def step(self, i: int, ev=None):
+        c = self.case
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+        pml.mqa_logits(self.q, self.k, self.ksc, self.w, self.ks, self.ke, logits=self.logits)
+        if ev is not None:
+            ev[2].record()
+        pml.top_k_per_row(self.logits, self.ke, c.topk, ks=self.ks, max_width=c.N, out=self.topk)
+        if ev is not None:
+            ev[3].record()
+
+
+def run_timed(b, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps; per-kernel times from events."""
+    for i in range(warmup):
+        b.step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        b.step(warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    return wall, per  # per: [steps, 3] ms of (schedule, logits, top-k)
+
+
+def cpu_baseline(case: syn.PagedCase, target_s: float) -> dict:
+    """The oracle (as it stands) on a bounded sample of rows of the same workload."""
+    import oracle
+    vis = syn.vis_per_row(case)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(case.rows)
+    # calibrate on one row, then take rows until the estimate reaches target_s
+    t0 = time.perf_counter()
+    oracle.paged_logits(case, rows=order[:1])
+    rate = max(1.0, vis[order[0]]) / max(1e-6, time.perf_counter() - t0)
+    n, acc = 0, 0.0
+    while n < case.rows and acc < target_s * rate:
+        acc += vis[order[n]]
+        n += 1
+    rows = np.sort(order[:max(1, n)])
+    t0 = time.perf_counter()
+    sc = oracle.paged_logits(case, rows=rows)
+    oracle.topk(sc, vis[rows], case.topk)
+    dt = time.perf_counter() - t0
+    pairs = int(vis[rows].sum())
+    return {"value": round(pairs / dt / 1e3, 3), "unit": "K tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {case.rows} rows ({pairs} scored pairs) of the same workload, "
+                      f"fp64 logits + top-k, {dt:.1f} s"}
+
+
+def describe(case: syn.PagedCase) -> dict:
+    return {"rows": case.rows, "requests": len(case.req_ctx), "req_tokens": int(sum(case.req_ctx)),
+            "scored_pairs": syn.scored_pairs(case), "max_ctx": case.max_ctx, "block_kv": case.block_kv,
+            "kv": "fp8" if case.kv_format == syn.KV_FP8 else "mxfp4", "heads": case.H, "head_dim": case.D,
+            "topk": case.topk}
+
+
+def paged_summary(name: str, b: PagedBench, wall: float, per: np.ndarray, steps: int) -> dict:
+    c = b.case
+    t_log = float(per[:, 1].mean()) * 1e-3
+    kbytes = b.req_tokens * BYTES_PER_TOKEN[c.kv_format]
+    return {"workload": name, "ms_per_step": wall / steps * 1e3,
+            "ms_schedule": float(per[:, 0].mean()), "ms_logits": t_log * 1e3, "ms_topk": float(per[:, 2].mean()),
+            "scored_Ktok_s": b.pairs / (wall / steps) / 1e3,
+            "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
+            "logits_mfma_frac": b.pairs * 2 * c.H * c.D / t_log / 1e12 / PEAK_FP8_TFLOPS,
+            "logits_out_bytes": c.rows * c.max_ctx * 4, **describe(c)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pml.lib()  # fail loudly before generating data if the library is missing
+
+    print("[bench] generating the varlen speculative-decode workload", file=sys.stderr, flush=True)
+    case = syn.config_varlen_fp8()
+    b = PagedBench(case, args.copies)
+    print(f"[bench] {case.rows} rows, {len(case.req_ctx)} requests, {b.pairs} scored pairs; timing",
+          file=sys.stderr, flush=True)
+    wall, per = run_timed(b, args.steps, args.warmup)
+    s = paged_summary("varlen_spec_decode_fp8_120k", b, wall, per, args.steps)
+
+    line = {
+        "metric": "scored K tokens/s + achieved HBM GB/s (paged MQA logits + top-k), 1xMI355X",
+        "value": round(s["scored_Ktok_s"], 1),
+        "unit": "K tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "varlen speculative decode: 40 requests, ctx U[100K,128K], accepted lengths "
+                               "U{1..6} flattened to rows, fp8 K cache block_kv 64, H 64, D 128, top-k 2048",
+                   **describe(case), "parallelism": "single GPU", "num_workers": b.num_cus,
+                   "kv_copies_rotated": len(b.kv)},
+        "breakdown_ms": {"schedule": round(s["ms_schedule"], 4), "logits": round(s["ms_logits"], 4),
+                         "topk": round(s["ms_topk"], 4)},
+        "logits_mfma_frac": round(s["logits_mfma_frac"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(s["logits_hbm_GBs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(s["logits_hbm_frac"], 4), "traffic": None,
+                     "kernel": "paged_logits_kernel<fp8, block_kv 64>",
+                     "bytes_per_launch": b.req_tokens * BYTES_PER_TOKEN[case.kv_format]},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    del b
+    torch.cuda.empty_cache()
+
+    if args.all:
+        others = [("uniform_decode_fp8_32k", lambda: PagedBench(syn.config_uniform_decode(), args.copies * 2)),
+                  ("varlen_spec_decode_mxfp4_64k", lambda: PagedBench(syn.config_varlen_fp4(), args.copies * 2)),
+                  ("tiny_decode_fp8", lambda: PagedBench(syn.config_tiny_decode(), 1))]
+        for name, mk in others:
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            ob = mk()
+            w2, p2 = run_timed(ob, args.steps, args.warmup)
+            print(json.dumps(paged_summary(name, ob, w2, p2, args.steps)), file=sys.stderr, flush=True)
+            del ob
+        print("[bench] ragged_prefill_4x8192", file=sys.stderr, flush=True)
+        rb = RaggedBench(syn.config_ragged_prefill())
+        w2, p2 = run_timed(rb, max(3, args.steps // 4), 2)
+        n = max(3, args.steps // 4)
+        t_log = float(p2[:, 1].mean()) * 1e-3
+        print(json.dumps({"workload": "ragged_prefill_4x8192", "ms_per_step": w2 / n * 1e3,
+                          "ms_logits": t_log * 1e3, "ms_topk": float(p2[:, 2].mean()),
+                          "scored_Ktok_s": rb.pairs / (w2 / n) / 1e3,
+                          "logits_mfma_frac": rb.pairs * 2 * 64 * 128 / t_log / 1e12 / PEAK_FP8_TFLOPS,
+                          "logits_write_GBs": rb.case.M * rb.case.N * 4 / t_log / 1e9}), file=sys.stderr, flush=True)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

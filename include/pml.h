@@ -1,0 +1,206 @@
+/*
+ * pml.h - C ABI of the paged MQA-logits library for AMD Instinct MI355X (gfx950).
+ *
+ * The library scores query rows of DeepSeek-style sparse-attention indexers
+ * against an fp8 or MXFP4 key cache and selects the top-k keys per row:
+ *
+ *     logit[r, s] = sum_h w[r,h] * max(0, scale_k[s] * <q[r,h,:], k[s,:]>)
+ *
+ * for the key tokens s that row r may see, and -inf for the rest. The calls
+ * follow the decode path of the vLLM sparse-attention indexer page
+ * ("vllm.model_executor.layers.sparse_attn_indexer", _varlen_decode_rows:
+ * get_paged_mqa_logits_metadata -> fp8_fp4_paged_mqa_logits -> top-k
+ * selector) and its prefill path (mqa_logits over [ks, ke) bounds).
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless stated otherwise. All buffers are
+ *     owned by the caller; the library keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued on it; no call synchronises or allocates memory.
+ *   - Every call returns a status (PML_OK = 0). Arguments are validated on
+ *     the host before anything is launched; on error nothing is launched.
+ *     PML_ERR_HIP means a launch failed; the HIP error stays readable with
+ *     hipGetLastError(). Faults inside a kernel surface at the caller's next
+ *     synchronisation of `stream`.
+ *   - Contracts that depend on device data (lengths within max_ctx, sorted
+ *     bounds, ...) are not checked on the host. Where a kernel can detect a
+ *     violation cheaply it writes NaN instead of reading out of bounds.
+ *   - fp8 means OCP E4M3 ("fn": max 448, no infinity), the native fp8 of gfx950.
+ */
+#ifndef PML_H
+#define PML_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pml_status {
+    PML_OK = 0,
+    PML_ERR_NULL = 1,          /* a required pointer is NULL                          */
+    PML_ERR_SHAPE = 2,         /* unsupported heads / head_dim, or a negative size     */
+    PML_ERR_BLOCK_KV = 3,      /* block_kv is not 32 or 64                             */
+    PML_ERR_VARLEN_NEXT_N = 4, /* indices given together with next_n != 1              */
+    PML_ERR_STRIDE = 5,        /* page stride, table or output leading dim too small   */
+    PML_ERR_ALIGN = 6,         /* a pointer or stride breaks the 16-byte alignment     */
+    PML_ERR_K = 7,             /* top-k k outside [1, 4096]                           */
+    PML_ERR_WORKSPACE = 8,     /* workspace missing or smaller than required           */
+    PML_ERR_FORMAT = 9,        /* kv_format is neither PML_KV_FP8 nor PML_KV_MXFP4      */
+    PML_ERR_UNSUPPORTED = 10,  /* an argument combination this version does not handle */
+    PML_ERR_HIP = 11           /* a kernel launch failed                               */
+};
+
+/* Key-cache formats (sparse_attn_indexer page, _gather_workspace_shapes and
+ * kv_cache_as_quant_view). A page holds block_kv tokens:
+ *   PML_KV_FP8:   values [block_kv][D] fp8, then scales [block_kv] fp32
+ *                 (little-endian); page_bytes = block_kv * (D + 4).
+ *   PML_KV_MXFP4: values [block_kv][D/2] packed e2m1 (element 2i in the low
+ *                 nibble of byte i), then scales [block_kv][D/32] e8m0;
+ *                 page_bytes = block_kv * (D/2 + D/32). No per-token fp32 scale.
+ * Page p starts at kv_cache + p * page_stride_bytes; the stride may exceed
+ * page_bytes (a per-layer view into a larger allocation). fp8 per-token
+ * scales must be non-negative (they are quantisation scales). */
+enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
+
+/* Heads and head dimension this version supports. */
+#define PML_HEADS 64
+#define PML_HEAD_DIM 128
+/* Largest top-k. */
+#define PML_MAX_TOPK 4096
+
+/*
+ * paged_mqa_logits_metadata - split the paged-logits work over persistent
+ * workgroups ("get_paged_mqa_logits_metadata(context_lens, block_kv, num_SMs,
+ * indices=)", [Attention][DSA] Route SM100 sparse-indexer decode ... , Purpose
+ * and Changes; the schedule has num_SMs + 1 entries and a row slice gets its
+ * own schedule, sparse_attn_indexer page, _varlen_decode_rows).
+ *
+ *   context_lens     int32. With indices or next_n == 1: [num_rows], the
+ *                    tokens each row sees. Otherwise [num_rows / next_n]
+ *                    full lengths (row j of entry b sees len[b]-next_n+j+1),
+ *                    or, with context_lens_2d, [num_rows / next_n][next_n]
+ *                    per-row lengths.
+ *   num_rows         flattened query rows (>= 0); a multiple of next_n.
+ *   next_n           rows per batch entry when indices is NULL (>= 1).
+ *   indices          int32 [num_rows] request id per row, or NULL. Rows with
+ *                    equal CONSECUTIVE ids form one group whose key blocks are
+ *                    read once for all of them ("[Bugfix][GLM-5.3-Flash] ...",
+ *                    Purpose). Grouping changes speed, never the result.
+ *                    Requires next_n == 1 (else PML_ERR_VARLEN_NEXT_N).
+ *   block_kv         tokens per cache page: 32 or 64 (else PML_ERR_BLOCK_KV).
+ *   num_CUs          number of persistent workgroups the logits call will
+ *                    launch (>= 1; e.g. 2 per compute unit).
+ *   schedule         int32 [num_CUs + 1][2] output: for each workgroup the
+ *                    (first row of its first row-piece, block offset) where its
+ *                    contiguous share of (row-piece, key-block) units starts;
+ *                    entry num_CUs is (num_rows, 0). A row-piece is at most 8
+ *                    consecutive rows of one group. Units are weighted by
+ *                    (4 + rows in the piece) so shares cost about the same.
+ * The schedule is valid only for the same context_lens, indices, next_n,
+ * block_kv and num_CUs.
+ */
+int paged_mqa_logits_metadata(const int32_t *context_lens, int num_rows, int next_n,
+                              int context_lens_2d, const int32_t *indices, int block_kv,
+                              int num_CUs, int32_t *schedule, void *stream);
+
+/*
+ * fp8_fp4_paged_mqa_logits - score every visible token of a paged key cache
+ * ("fp8_fp4_paged_mqa_logits((q, q_scale), kv_cache, weights, seq_lens,
+ * block_table, schedule, max_model_len, indices)", sparse_attn_indexer page,
+ * _varlen_decode_rows; FP8 q with its per-token scale folded into weights,
+ * forward_cuda).
+ *
+ *   q                fp8 codes [num_rows][num_heads][head_dim], 16-B aligned.
+ *   num_rows, next_n, context_lens, context_lens_2d, indices
+ *                    as for the metadata call (same values it was given).
+ *   num_heads        must be 64; head_dim must be 128 (else PML_ERR_SHAPE).
+ *   kv_cache         paged key cache, 16-B aligned; kv_format PML_KV_FP8 or
+ *                    PML_KV_MXFP4; block_kv 32 or 64.
+ *   page_stride_bytes >= page bytes and a multiple of 16 (else PML_ERR_STRIDE).
+ *   num_pages        pages in kv_cache (>= 1). A visible block whose table
+ *                    entry is outside [0, num_pages) scores NaN.
+ *   weights          fp32 [num_rows][num_heads].
+ *   block_table      int32 [table rows][block_table_ld]; row r reads table row
+ *                    r / next_n (with indices: its own row, and rows of one
+ *                    group must hold the same entries). Entries of blocks a
+ *                    row does not see are never read. block_table_cols
+ *                    (<= ld) bounds the block index; beyond it a block scores NaN.
+ *   schedule, num_CUs the metadata call's output and its num_CUs; the kernel
+ *                    launches num_CUs workgroups.
+ *   max_ctx          output columns (>= every visible length).
+ *   logits           fp32 [num_rows][logits_ld] output, 16-B aligned,
+ *                    logits_ld >= max_ctx and a multiple of 4. Columns
+ *                    [0, vis(r)) get the score, [vis(r), max_ctx) get -inf,
+ *                    [max_ctx, logits_ld) are not written.
+ */
+int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n, int num_heads,
+                             int head_dim, const void *kv_cache, int kv_format, int block_kv,
+                             int64_t page_stride_bytes, int64_t num_pages, const float *weights,
+                             const int32_t *context_lens, int context_lens_2d,
+                             const int32_t *block_table, int64_t block_table_ld,
+                             int block_table_cols, const int32_t *schedule, int num_CUs,
+                             const int32_t *indices, int max_ctx, float *logits,
+                             int64_t logits_ld, void *stream);
+
+/*
+ * mqa_logits - non-paged (ragged prefill) logits: a dense [M][N] matrix whose
+ * row r is scored on keys [cu_seqlen_ks[r], cu_seqlen_ke[r]) and -inf
+ * elsewhere (sparse_attn_indexer page: the dense M*N logits tensor that
+ * prefill chunking bounds, and forward_cpu's per-row lengths ke - ks).
+ *
+ *   q        fp8 codes [M][num_heads][head_dim], 16-B aligned.
+ *   k        fp8 codes [N][head_dim] contiguous keys, 16-B aligned.
+ *   k_scale  fp32 [N] per-key scale (non-negative), 4-B aligned.
+ *   weights  fp32 [M][num_heads], 16-B aligned.
+ *   cu_seqlen_ks, cu_seqlen_ke  int32 [M]; bounds are clamped to [0, N].
+ *   logits   fp32 [M][logits_ld], logits_ld >= N, a multiple of 4, 16-B aligned.
+ *            Columns [0, N) of every row are written; [N, logits_ld) are not.
+ * M <= 524280 (else PML_ERR_SHAPE). M == 0 or N == 0 returns PML_OK and
+ * launches nothing.
+ */
+int mqa_logits(const void *q, int M, int num_heads, int head_dim, const void *k,
+               const float *k_scale, int N, const float *weights, const int32_t *cu_seqlen_ks,
+               const int32_t *cu_seqlen_ke, float *logits, int64_t logits_ld, void *stream);
+
+/*
+ * top_k_per_row - the k largest logits of each row among its valid columns
+ * (the indexer's top-k selector, "selector(logits, seq_lens, next_n, out,
+ * topk_tokens, max_seq_len)", sparse_attn_indexer page, _varlen_decode_rows;
+ * int32 output preset to -1 and request-local positions, forward_cpu).
+ *
+ *   logits     fp32 [num_rows][logits_ld].
+ *   ks         int32 [num_rows] first valid column per row, or NULL (= 0).
+ *   ke         int32 end of the valid columns: [num_rows] when next_n == 1 or
+ *              ks != NULL; else [num_rows / next_n] full lengths and row j of
+ *              entry b ends at ke[b] - next_n + j + 1. Bounds are clamped to
+ *              [0, logits_ld].
+ *   next_n     >= 1; must be 1 when ks is given.
+ *   k          1..4096 (else PML_ERR_K).
+ *   max_width  upper bound of ke - ks over all rows (the selector's
+ *              max_seq_len); sizes the workspace. Wider rows are an error of
+ *              the caller and are cut to max_width.
+ *   out        int32 [num_rows][out_ld], out_ld >= k: per row the selected
+ *              positions minus ks in ascending order, then -1 up to k.
+ *              Order of selection: larger value first, equal values by lower
+ *              position (-0.0 equals +0.0).
+ *   workspace  device scratch of at least top_k_per_row_workspace_size()
+ *              bytes, 16-B aligned (may be NULL when that size is 0).
+ */
+size_t top_k_per_row_workspace_size(int num_rows, int max_width, int k);
+int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
+                  const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
+                  int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Text of a status code (static storage). */
+const char *pml_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pml_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PML_H */

@@ -1,0 +1,245 @@
+"""Python binding of libpml, the gfx950 paged MQA-logits library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (``include/pml.h``). Tensors must already live on the
+GPU; work is enqueued on torch's current stream and nothing synchronises.
+There is no CPU fallback: if ``libpml.so`` is missing the calls raise.
+
+Calls (names follow the indexer pages: get_paged_mqa_logits_metadata,
+fp8_fp4_paged_mqa_logits, mqa_logits and the per-row top-k selector):
+
+* ``paged_mqa_logits_metadata(context_lens, block_kv, num_cus, indices=None, next_n=1)``
+* ``fp8_fp4_paged_mqa_logits(q, kv_cache, weights, context_lens, block_table, schedule,
+  max_model_len, indices=None, ...)``
+* ``mqa_logits(q, k, k_scale, weights, cu_seqlen_ks, cu_seqlen_ke)``
+* ``top_k_per_row(logits, ke, k, ks=None, next_n=1, max_width=None)``
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import torch
+
+KV_FP8 = 0
+KV_MXFP4 = 1
+HEADS = 64
+HEAD_DIM = 128
+MAX_TOPK = 4096
+WORKERS_PER_CU = 2
+
+_LIB_PATH = Path(__file__).resolve().parent / "libpml.so"
+_lib = None
+
+# status codes that mean "bad argument" (ValueError); the rest are RuntimeError
+_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10}
+
+
+class PmlError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class PmlArgError(PmlError, ValueError):
+    pass
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpml.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not _LIB_PATH.exists():
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with paged_mqa_logits_amd.build.build() "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(str(_LIB_PATH))
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.paged_mqa_logits_metadata.argtypes = [P, I, I, I, P, I, I, P, P]
+        L.fp8_fp4_paged_mqa_logits.argtypes = [P, I, I, I, I, P, I, I, I64, I64, P, P, I, P, I64, I, P,
+                                               I, P, I, P, I64, P]
+        if hasattr(L, "mqa_logits"):
+            L.mqa_logits.argtypes = [P, I, I, I, P, P, I, P, P, P, P, I64, P]
+        if hasattr(L, "top_k_per_row"):
+            L.top_k_per_row_workspace_size.argtypes = [I, I, I]
+            L.top_k_per_row_workspace_size.restype = SZ
+            L.top_k_per_row.argtypes = [P, I, I64, P, P, I, I, I, P, I64, P, SZ, P]
+        for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row"):
+            if hasattr(L, name):
+                getattr(L, name).restype = I
+        L.pml_status_string.argtypes = [I]
+        L.pml_status_string.restype = ctypes.c_char_p
+        L.pml_version.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().pml_status_string(status).decode()
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        msg = f"{call}: {status_string(status)} (status {status})"
+        raise (PmlArgError if status in _ARG_ERRORS else PmlError)(status, msg)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t
+
+
+_FP8_TYPES = (torch.uint8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def default_num_workers(device=None) -> int:
+    """Persistent workgroups for the paged-logits call: WORKERS_PER_CU per compute unit."""
+    props = torch.cuda.get_device_properties(device if device is not None else torch.cuda.current_device())
+    return WORKERS_PER_CU * props.multi_processor_count
+
+
+def _rows_of(context_lens: torch.Tensor, next_n: int, indices) -> tuple[int, int]:
+    """(flattened rows, 2-D flag) implied by the lengths and next_n."""
+    if context_lens.dim() == 2:
+        if indices is not None:
+            raise ValueError("2-D context_lens cannot be combined with indices")
+        if context_lens.shape[1] != next_n:
+            raise ValueError("2-D context_lens must be [batch, next_n]")
+        return context_lens.numel(), 1
+    if indices is not None or next_n == 1:
+        return context_lens.numel(), 0
+    return context_lens.numel() * next_n, 0
+
+
+def paged_mqa_logits_metadata(context_lens: torch.Tensor, block_kv: int, num_cus: int | None = None,
+                              indices: torch.Tensor | None = None, next_n: int = 1,
+                              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Work split of the paged-logits call: int32 [num_cus + 1, 2] on the device."""
+    _dev(context_lens, "context_lens", _I32)
+    context_lens = context_lens.contiguous()
+    if indices is not None:
+        indices = _dev(indices, "indices", _I32).contiguous()
+    if num_cus is None:
+        num_cus = default_num_workers(context_lens.device)
+    rows, l2d = _rows_of(context_lens, next_n, indices)
+    if out is None:
+        out = torch.empty(num_cus + 1, 2, dtype=torch.int32, device=context_lens.device)
+    elif out.numel() < 2 * (num_cus + 1) or not out.is_contiguous():
+        raise ValueError("schedule buffer too small or not contiguous")
+    _check(lib().paged_mqa_logits_metadata(_p(context_lens), rows, next_n, l2d, _p(indices), block_kv,
+                                           num_cus, _p(out), _stream()), "paged_mqa_logits_metadata")
+    return out
+
+
+def logits_ld(max_ctx: int) -> int:
+    """Row stride used when the binding allocates the logits (a multiple of 4 floats)."""
+    return max(4, (max_ctx + 3) // 4 * 4)
+
+
+def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                             context_lens: torch.Tensor, block_table: torch.Tensor,
+                             schedule: torch.Tensor, max_model_len: int,
+                             indices: torch.Tensor | None = None, *, kv_format: int = KV_FP8,
+                             block_kv: int = 64, next_n: int = 1,
+                             logits: torch.Tensor | None = None) -> torch.Tensor:
+    """Paged logits fp32 [rows, ld >= max_model_len]; columns past each row's
+    visible length are -inf. ``kv_cache`` is [num_pages, page_stride_bytes] uint8
+    (a row stride larger than the page is allowed)."""
+    _dev(q, "q", _FP8_TYPES)
+    _dev(kv_cache, "kv_cache", (torch.uint8,))
+    _dev(weights, "weights", _F32)
+    _dev(context_lens, "context_lens", _I32)
+    _dev(block_table, "block_table", _I32)
+    _dev(schedule, "schedule", _I32)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [rows, heads, head_dim] tensor")
+    if kv_cache.dim() != 2 or kv_cache.stride(1) != 1:
+        raise ValueError("kv_cache must be [num_pages, page_stride] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit inner stride")
+    weights = weights.contiguous()
+    context_lens = context_lens.contiguous()
+    if indices is not None:
+        indices = _dev(indices, "indices", _I32).contiguous()
+    rows, l2d = _rows_of(context_lens, next_n, indices)
+    if rows != q.shape[0]:
+        raise ValueError(f"q has {q.shape[0]} rows but the lengths describe {rows}")
+    if logits is None:
+        logits = torch.empty(rows, logits_ld(max_model_len), dtype=torch.float32, device=q.device)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit inner stride")
+    num_cus = schedule.shape[0] - 1
+    _check(lib().fp8_fp4_paged_mqa_logits(
+        _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
+        kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
+        block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
+        max_model_len, _p(logits), logits.stride(0), _stream()), "fp8_fp4_paged_mqa_logits")
+    return logits
+
+
+def mqa_logits(q: torch.Tensor, k: torch.Tensor, k_scale: torch.Tensor, weights: torch.Tensor,
+               cu_seqlen_ks: torch.Tensor, cu_seqlen_ke: torch.Tensor,
+               logits: torch.Tensor | None = None) -> torch.Tensor:
+    """Ragged (non-paged) logits fp32 [M, ld >= N]; row r is scored on keys [ks[r], ke[r])."""
+    _dev(q, "q", _FP8_TYPES)
+    _dev(k, "k", _FP8_TYPES)
+    _dev(k_scale, "k_scale", _F32)
+    _dev(weights, "weights", _F32)
+    _dev(cu_seqlen_ks, "cu_seqlen_ks", _I32)
+    _dev(cu_seqlen_ke, "cu_seqlen_ke", _I32)
+    if q.dim() != 3 or not q.is_contiguous() or k.dim() != 2 or not k.is_contiguous():
+        raise ValueError("q must be contiguous [M, heads, head_dim] and k contiguous [N, head_dim]")
+    M, N = q.shape[0], k.shape[0]
+    if logits is None:
+        logits = torch.empty(M, logits_ld(N), dtype=torch.float32, device=q.device)
+    _check(lib().mqa_logits(_p(q), M, q.shape[1], q.shape[2], _p(k), _p(k_scale.contiguous()), N,
+                            _p(weights.contiguous()), _p(cu_seqlen_ks.contiguous()),
+                            _p(cu_seqlen_ke.contiguous()), _p(logits), logits.stride(0), _stream()),
+           "mqa_logits")
+    return logits
+
+
+def top_k_workspace_size(rows: int, max_width: int, k: int) -> int:
+    return int(lib().top_k_per_row_workspace_size(rows, max_width, k))
+
+
+def top_k_per_row(logits: torch.Tensor, ke: torch.Tensor, k: int, ks: torch.Tensor | None = None,
+                  next_n: int = 1, max_width: int | None = None, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """int32 [rows, k]: per row the positions (minus ks) of the k largest logits
+    among columns [ks, ke), ascending, then -1."""
+    _dev(logits, "logits", _F32)
+    _dev(ke, "ke", _I32)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit inner stride")
+    rows = logits.shape[0]
+    if ks is not None:
+        ks = _dev(ks, "ks", _I32).contiguous()
+    if max_width is None:
+        max_width = logits.shape[1]
+    if out is None:
+        out = torch.empty(rows, max(k, 1), dtype=torch.int32, device=logits.device)
+    need = top_k_workspace_size(rows, max_width, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().top_k_per_row(_p(logits), rows, logits.stride(0), _p(ks), _p(ke.contiguous()), next_n, k,
+                               max_width, _p(out), out.stride(0), _p(workspace), wbytes, _stream()),
+           "top_k_per_row")
+    return out

@@ -1,0 +1,93 @@
+"""Helpers of the GPU parity tests: upload seeded cases, call the HIP path
+through the binding and compare with the CPU oracle (test infrastructure)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_mqa_logits_amd as pml
+import pml_synth as syn
+
+SENTINEL = 12345.0  # prefilled into output buffers: any cell left unwritten shows up
+
+# Acceptance of a logit: |gpu - oracle| <= REL * |oracle| + ABS * sum_h |w[r, h]|
+REL = 2e-3
+ABS = 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def banner(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def upload(case: syn.PagedCase) -> dict:
+    d = dev()
+    return dict(
+        q=case.q.to(d), kv=case.kv_cache.to(d), w=case.weights.to(d), lens=case.context_lens.to(d),
+        bt=case.block_table.to(d), indices=None if case.indices is None else case.indices.to(d))
+
+
+def run_paged(case: syn.PagedCase, t: dict | None = None, *, num_cus=None, indices="case",
+              ld=None) -> np.ndarray:
+    """GPU logits [rows, max_ctx] as float32 numpy (checks the sentinel columns past max_ctx)."""
+    t = t or upload(case)
+    idx = t["indices"] if indices == "case" else indices
+    sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, num_cus, indices=idx,
+                                          next_n=case.next_n)
+    ld = ld or pml.logits_ld(case.max_ctx)
+    out = torch.full((case.rows, ld), SENTINEL, dtype=torch.float32, device=dev())
+    pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx, idx,
+                                 kv_format=case.kv_format, block_kv=case.block_kv, next_n=case.next_n,
+                                 logits=out)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.all(o[:, case.max_ctx:] == SENTINEL), "columns past max_ctx were written"
+    return o[:, : case.max_ctx]
+
+
+def abs_tol(weights: torch.Tensor) -> np.ndarray:
+    return ABS * np.abs(weights.double().numpy()).sum(axis=1)
+
+
+def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Tensor, what: str = "") -> None:
+    """The acceptance bar: masked cells exactly -inf, the rest within tolerance."""
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert not np.any(gpu == SENTINEL), f"{what}: unwritten cells"
+    masked = np.isneginf(ref)
+    bad_mask = masked != np.isneginf(gpu)
+    assert not bad_mask.any(), f"{what}: -inf pattern differs at {np.argwhere(bad_mask)[:5]}"
+    assert not np.isnan(ref).any(), f"{what}: oracle produced NaN"
+    fin = ~masked
+    tol = REL * np.abs(ref) + abs_tol(weights_rows)[:, None]
+    err = np.abs(gpu.astype(np.float64) - ref)
+    bad = fin & ~(err <= tol)
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} cells out of tolerance, e.g. {[(tuple(x), gpu[tuple(x)], ref[tuple(x)]) for x in i]}")
+
+
+def exactify_fp8_case(case: syn.PagedCase, seed: int) -> None:
+    """Make every product and partial sum exact in fp32: integer fp8 codes in
+    [-8, 8], power-of-two scales 2^-4..2^2 and weights in (1/8)Z within [-4, 4]
+    (valid key slots only; NaN codes of unused slots are kept)."""
+    g = torch.Generator().manual_seed(seed)
+    qv = torch.randint(-8, 9, case.q.shape, generator=g).float()
+    case.q.copy_(qv.to(torch.float8_e4m3fn).view(torch.uint8))
+    case.weights.copy_(torch.randint(-32, 33, case.weights.shape, generator=g).float() / 8)
+    kv = case.kv_cache.numpy()
+    B, D = case.block_kv, case.D
+    vals = kv[:, : B * D]
+    live = vals != syn.FP8_NAN
+    ints = torch.randint(-8, 9, vals.shape, generator=g).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vals[live] = ints[live]
+    sc = kv[:, B * D: B * D + 4 * B].view(np.float32)
+    e = torch.randint(-4, 3, sc.shape, generator=g).numpy().astype(np.float32)
+    sc[~np.isnan(sc)] = np.exp2(e)[~np.isnan(sc)]
+
+
+def oracle_rows(case, rows) -> np.ndarray:
+    return oracle.paged_logits(case, rows=np.asarray(rows))

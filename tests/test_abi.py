@@ -1,0 +1,77 @@
+"""The C-ABI library loads, exports every call its header declares, and rejects
+bad arguments on the host before launching anything (CPU only: every call here
+returns an error status before it would touch a GPU)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import paged_mqa_logits_amd as pml
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "pml.h"
+
+
+def _declared():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
+              "top_k_per_row_workspace_size", "pml_status_string", "pml_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = pml.lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    assert pml.status_string(0) == "ok"
+    for code in range(1, 12):
+        assert pml.status_string(code) != "unknown status"
+    assert pml.status_string(999) == "unknown status"
+    assert pml.lib().pml_version() >= 10000
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _paged(**kw):
+    a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
+             w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
+             max_ctx=512, out=FAKE, ld=512, stream=None)
+    a.update(kw)
+    return pml.lib().fp8_fp4_paged_mqa_logits(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=32), 2), (dict(D=64), 2), (dict(rows=-1), 2), (dict(cus=0), 2),
+    (dict(fmt=2), 9), (dict(bkv=16), 3), (dict(idx=FAKE, next_n=2, rows=4), 4),
+    (dict(rows=5, next_n=2), 2), (dict(q=None), 1), (dict(bt=None), 1),
+    (dict(stride=64 * 132 - 16), 5), (dict(stride=64 * 132 + 4), 5), (dict(ld=500), 5),
+    (dict(ld=514, max_ctx=513), 5), (dict(pages=0), 5), (dict(bt_cols=9), 5),
+    (dict(fmt=1, bkv=32, stride=32 * 68 - 16), 5),
+    (dict(q=P(0x1001)), 6), (dict(out=P(0x1004)), 6),
+])
+def test_paged_validation(kw, code):
+    assert _paged(**kw) == code
+
+
+def test_paged_zero_rows_is_ok_without_gpu():
+    assert _paged(rows=0) == 0
+
+
+def test_metadata_validation():
+    f = pml.lib().paged_mqa_logits_metadata
+    assert f(FAKE, 4, 1, 0, None, 64, 4, None, None) == 1
+    assert f(FAKE, 4, 1, 0, None, 48, 4, FAKE, None) == 3
+    assert f(FAKE, 4, 2, 0, FAKE, 64, 4, FAKE, None) == 4
+    assert f(FAKE, 5, 2, 0, None, 64, 4, FAKE, None) == 2
+    assert f(FAKE, 4, 1, 0, None, 64, 0, FAKE, None) == 2
+    assert f(None, 4, 1, 0, None, 64, 4, FAKE, None) == 1

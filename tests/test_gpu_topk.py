@@ -1,0 +1,134 @@
+"""Per-row top-k on the GPU.
+
+* On shared input (the same fp32 logits on both sides) the selected set must
+  equal the oracle's bit for bit, ties included.
+* Against the oracle's fp64 logits the spec acceptance holds: every
+  selected index scores at least t_k - tau, every index scoring above t_k + tau
+  is selected, and min(k, width) distinct in-range entries come first.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_mqa_logits_amd as pml
+import pml_synth as syn
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_topk(logits: torch.Tensor, ke: torch.Tensor, k: int, ks=None, next_n=1) -> np.ndarray:
+    res = pml.top_k_per_row(logits, ke, k, ks=ks, next_n=next_n)
+    torch.cuda.synchronize()
+    return res.cpu().numpy()
+
+
+def _shared_input_check(logits_np: np.ndarray, ke: np.ndarray, k: int, ks=None, next_n=1):
+    d = G.dev()
+    lt = torch.from_numpy(np.ascontiguousarray(logits_np, dtype=np.float32)).to(d)
+    ket = torch.from_numpy(np.asarray(ke, dtype=np.int32)).to(d)
+    kst = None if ks is None else torch.from_numpy(np.asarray(ks, dtype=np.int32)).to(d)
+    got = gpu_topk(lt, ket, k, kst, next_n)
+    if next_n > 1:
+        r = np.arange(logits_np.shape[0])
+        ke = np.asarray(ke)[r // next_n] - next_n + (r % next_n) + 1
+    want = oracle.topk(logits_np.astype(np.float32).astype(np.float64), ke, k, ks=ks)
+    np.testing.assert_array_equal(got, want)
+    return got
+
+
+def test_adversarial_rows():
+    rng = np.random.default_rng(800)
+    W = 5000
+    rows = []
+    rows.append(np.zeros(W))                                  # all equal
+    rows.append(np.round(rng.standard_normal(W)))             # many ties
+    r = rng.standard_normal(W)
+    r[::3] = 0.0
+    r[1::3] = -0.0                                            # +-0 are equal
+    rows.append(r)
+    r = rng.standard_normal(W)
+    r[100:] = -np.inf                                         # -inf tail
+    rows.append(r)
+    rows.append(np.full(W, -np.inf))
+    rows.append(rng.standard_normal(W) * 1e-30)               # subnormal-ish spread
+    r = rng.standard_normal(W)
+    r[7] = np.nan                                             # NaN ranks lowest
+    rows.append(r)
+    rows.append(np.arange(W, dtype=np.float64)[::-1].copy())  # descending
+    L = np.stack(rows)
+    n = L.shape[0]
+    G.banner("top-k adversarial")
+    for k, ke in ((1, [W] * n), (64, [W] * n), (2048, [W] * n), (4096, [W] * n),
+                  (100, [100, 99, 101, 50, 0, 100, 5000, 1])):
+        _shared_input_check(L, ke, k)
+
+
+def test_bounds_and_next_n():
+    rng = np.random.default_rng(810)
+    L = rng.standard_normal((12, 9000)).astype(np.float32)
+    ks = rng.integers(0, 3000, 12)
+    ke = ks + rng.integers(0, 6000, 12)
+    ke[0] = ks[0]          # empty
+    ke[1] = ks[1] + 64     # width == k
+    G.banner("top-k ks/ke")
+    _shared_input_check(L, ke, 64, ks=ks)
+    G.banner("top-k next_n=3")
+    _shared_input_check(L, rng.integers(100, 9000, 4), 333, next_n=3)
+
+
+def _acceptance(gpu: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray, k: int, wsum: np.ndarray):
+    for r in range(gpu.shape[0]):
+        n = max(0, int(hi[r] - lo[r]))
+        m = min(k, n)
+        sel = gpu[r, :m]
+        assert np.all(gpu[r, m:] == -1)
+        assert len(np.unique(sel)) == m and np.all((sel >= 0) & (sel < n))
+        if n <= k:
+            continue
+        sc = ref[r, lo[r]: hi[r]]
+        tk = np.sort(sc)[::-1][k - 1]
+        tau = 2e-3 * abs(tk) + 1e-3 * wsum[r]
+        assert np.all(sc[sel] >= tk - tau)
+        must = np.nonzero(sc > tk + tau)[0]
+        assert np.all(np.isin(must, sel))
+
+
+def test_decode_configs_topk():
+    for case, nrows in ((syn.config_tiny_decode(), None), (syn.config_varlen_fp8(), 5)):
+        G.banner(f"top-k decode rows={case.rows} k={case.topk}")
+        t = G.upload(case)
+        sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, None, indices=t["indices"])
+        logits = pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx,
+                                              t["indices"], kv_format=case.kv_format, block_kv=case.block_kv)
+        got = pml.top_k_per_row(logits, t["lens"], case.topk, max_width=case.max_ctx)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy()
+        L = logits.cpu().numpy()[:, : case.max_ctx]
+        vis = syn.vis_per_row(case)
+        # shared input: bit-exact
+        want = oracle.topk(L.astype(np.float64), vis, case.topk)
+        np.testing.assert_array_equal(got, want)
+        # against the fp64 oracle logits on sampled rows
+        rows = np.arange(case.rows) if nrows is None else np.sort(np.random.default_rng(5).choice(case.rows, nrows, replace=False))
+        ref = G.oracle_rows(case, rows)
+        _acceptance(got[rows], ref, np.zeros(len(rows), dtype=np.int64), vis[rows], case.topk,
+                    np.abs(case.weights[rows].double().numpy()).sum(1))
+
+
+def test_prefill_topk_sampled():
+    case = syn.make_ragged_case([3000, 2500], seed=820)
+    d = G.dev()
+    G.banner("top-k prefill")
+    logits = pml.mqa_logits(case.q.to(d), case.k.to(d), case.k_scale.to(d), case.weights.to(d),
+                            case.ks.to(d), case.ke.to(d))
+    got = pml.top_k_per_row(logits, case.ke.to(d), 2048, ks=case.ks.to(d), max_width=case.N)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    L = logits.cpu().numpy()[:, : case.N].astype(np.float64)
+    ks, ke = case.ks.numpy(), case.ke.numpy()
+    np.testing.assert_array_equal(got, oracle.topk(L, ke, 2048, ks=ks))
+    rows = np.array([0, 1, 2047, 2048, 2049, 2999, 3000, 4500, 5499])
+    ref = oracle.ragged_logits(case, rows=rows)
+    _acceptance(got[rows], ref, ks[rows], ke[rows], 2048, np.abs(case.weights[rows].double().numpy()).sum(1))
