@@ -1,5 +1,5 @@
 // fp8_fp4_paged_mqa_logits: score every visible token of a paged fp8 / MXFP4
-// key cache for each query row (the tile pipeline is in logits_core.h).
+// key cache for each query row (scoring core in logits_core.h).
 //
 // Design (gfx950):
 //  * Persistent grid: one workgroup per schedule entry. Each walks its
@@ -7,12 +7,12 @@
 //    rows of one request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a
 //    request are processed together), so each key page is read from HBM once
 //    for all of them.
-//  * Key pages stream HBM -> LDS with direct-to-LDS loads (global_load_lds
-//    _dwordx4), kStages deep, with 16-byte chunks XOR-swizzled per token so the
-//    MFMA operand reads are free of bank conflicts. All per-unit metadata
-//    (schedule, block table, lengths, request ids) comes through the scalar
-//    cache, so the vector-memory counter holds only page loads and logit
-//    stores and the wait before a page never drains the loads behind it.
+//  * The 4 waves take the blocks of the current piece in turn; each loads its
+//    page from HBM straight into VGPRs (double-buffered) and scores it
+//    against every row of the piece, whose q and w sit in LDS. Waves meet at
+//    a barrier only when the piece changes.
+//  * All per-unit metadata (schedule, block table, lengths, request ids) is
+//    read through the scalar cache.
 //  * Columns past each row's last visible block are filled with -inf by the
 //    workgroups after their units (row-strided).
 #include "logits_core.h"
@@ -36,145 +36,118 @@ struct PagedArgs {
     int64_t out_ld;
 };
 
-// Walks one worker's units in order: pieces, then blocks inside a piece.
-// Every field is wave-uniform.
-template <int BKV>
-struct UnitIter {
-    int r0, g, nblk, blk;
-    int end_r, end_b;
-    bool valid;
+// Load block b of the piece whose table row is bt_row; false (and page 0 is
+// read) when the table entry is unusable, then the block scores NaN.
+template <bool FP4, int BKV>
+__device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, int b, KeyRegs<FP4, BKV> &k) {
+    int32_t e = -1;
+    if (b < a.bt_cols) e = sload(a.bt, bt_row * a.bt_ld + b);
+    const bool ok = e >= 0 && e < a.num_pages;
+    load_page<FP4, BKV>(a.kv + (ok ? (int64_t)e : 0) * a.page_stride, k);
+    return ok;
+}
 
-    __device__ __forceinline__ bool in_range() const {
-        return r0 < end_r || (r0 == end_r && blk < end_b);
-    }
-    __device__ __forceinline__ void settle(const RowView &v) {
-        for (;;) {
-            if (!in_range()) {
-                valid = false;
-                return;
+// Score block b against the g staged rows; rows whose visible length ends
+// before the block are skipped (their tail is filled separately).
+template <bool FP4, int BKV>
+__device__ __forceinline__ void score_block(const PagedArgs &a, int g, int b, const KeyRegs<FP4, BKV> &k, bool ok,
+                                            const uint8_t *s_q, const float *s_w, const int *s_vis, Pending &p) {
+    const int col0 = b * BKV;
+    const int s = col0 + out_token<BKV>(lane_id());
+    const float scale = FP4 ? 1.f : __uint_as_float(k.sc[0]);
+    p.mask = 0;
+    p.col0 = col0;
+#pragma unroll
+    for (int i = 0; i < kGMax; ++i) {
+        if (i < g) {
+            const int vis = uni(lds_ld<int>(&s_vis[i]));
+            if (col0 < vis) {
+                float v = score_row<FP4, BKV>(k, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
+                if (!ok) v = __builtin_nanf("");
+                if (s >= vis) v = -__builtin_inff();
+                p.v[i] = v;
+                p.mask |= 1 << i;
             }
-            if (blk < nblk) {
-                valid = true;
-                return;
-            }
-            r0 += g;
-            blk = 0;
-            if (r0 >= v.num_rows) {
-                valid = false;
-                return;
-            }
-            piece_at<BKV>(v, r0, g, nblk);
         }
     }
-    __device__ __forceinline__ void init(const PagedArgs &a, int c) {
-        const int n = a.rows.num_rows;
-        r0 = min(max(sload(a.sched, 2 * c), 0), n);
-        blk = max(sload(a.sched, 2 * c + 1), 0);
-        end_r = min(max(sload(a.sched, 2 * c + 2), 0), n);
-        end_b = max(sload(a.sched, 2 * c + 3), 0);
-        g = 0;
-        nblk = 0;
-        valid = false;
-        if (r0 >= n || !in_range()) return;
-        piece_at<BKV>(a.rows, r0, g, nblk);
-        settle(a.rows);
-    }
-    __device__ __forceinline__ void next(const RowView &v) {
-        ++blk;
-        settle(v);
-    }
-    // Page of the current unit; false when the table entry is unusable (then
-    // page 0 is read and the unit's logits are written as NaN).
-    __device__ __forceinline__ bool page(const PagedArgs &a, const uint8_t *&pg) const {
-        int32_t e = -1;
-        if (blk < a.bt_cols) e = sload(a.bt, (int64_t)(r0 / a.rows.next_n) * a.bt_ld + blk);
-        const bool ok = e >= 0 && e < a.num_pages;
-        pg = a.kv + (ok ? (int64_t)e : 0) * a.page_stride;
-        return ok;
-    }
-};
+}
+
+template <int BKV>
+__device__ __forceinline__ void store_pending(const PagedArgs &a, int r0, const Pending &p) {
+    const int lane = lane_id();
+    const int s = p.col0 + out_token<BKV>(lane);
+    const bool st = out_lane<BKV>(lane) && s < a.max_ctx;
+#pragma unroll
+    for (int i = 0; i < kGMax; ++i)
+        if ((p.mask >> i) & 1)
+            if (st) a.out[(int64_t)(r0 + i) * a.out_ld + s] = p.v[i];
+}
+
+// One step of a wave's block loop: wait for the current block, store the
+// previous block's logits, request the next block, score the current one.
+template <bool FP4, int BKV>
+__device__ __forceinline__ void block_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int blk_hi,
+                                           const KeyRegs<FP4, BKV> &kc, bool okc, int bc, KeyRegs<FP4, BKV> &kn,
+                                           bool &okn, int bn, const uint8_t *s_q, const float *s_w,
+                                           const int *s_vis, Pending &p) {
+    touch<FP4, BKV>(kc);
+    store_pending<BKV>(a, r0, p);
+    if (bn < blk_hi) okn = fetch_block<FP4, BKV>(a, bt_row, bn, kn);
+    score_block<FP4, BKV>(a, g, bc, kc, okc, s_q, s_w, s_vis, p);
+}
 
 template <bool FP4, int BKV>
 __global__ __launch_bounds__(kThreads, 2) void paged_logits_kernel(PagedArgs a) {
-    using C = TileCfg<FP4, BKV>;
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages][C::TILE];
-    __shared__ __attribute__((aligned(16))) float s_red[kGMax][kWaves][BKV];
-    __shared__ int s_lo[kGMax];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
+    __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_vis[kGMax];
 
     const int tid = threadIdx.x;
+    const int wave = uni(tid / kWave);
     const int W = gridDim.x;
     const int c = blockIdx.x;
+    const int n = a.rows.num_rows;
 
-    UnitIter<BKV> ld, cp;
-    ld.init(a, c);
-    cp = ld;
+    int r0 = min(max(sload(a.sched, 2 * c), 0), n);
+    int blk_lo = max(sload(a.sched, 2 * c + 1), 0);
+    const int end_r = min(max(sload(a.sched, 2 * c + 2), 0), n);
+    const int end_b = max(sload(a.sched, 2 * c + 3), 0);
 
-    int issued = 0;
-#pragma unroll
-    for (int k = 0; k < kStages - 1; ++k) {
-        if (ld.valid) {
-            const uint8_t *pg;
-            ld.page(a, pg);
-            issue_page<FP4, BKV>(pg, s_stage[k]);
-            ++issued;
-            ld.next(a.rows);
-        }
-    }
-
-    v8i qa[kGMax];
-    v4f w4[kGMax];
-    int cur_r0 = -1, cur_g = 0;
-
-    for (int u = 0; cp.valid; ++u) {
-        // Page u has landed once at most (kStages - 2) pages issued after it
-        // are still in flight (loads complete in order; stores issued in
-        // between only make the wait stricter).
-        if (issued - (u + 1) >= kStages - 2)
-            wait_vmcnt<(kStages - 2) * C::NLD>();
-        else
-            wait_vmcnt<0>();
-        barrier_lds();
-        if (ld.valid) {
-            const uint8_t *pg;
-            ld.page(a, pg);
-            issue_page<FP4, BKV>(pg, s_stage[(u + kStages - 1) % kStages]);
-            ++issued;
-            ld.next(a.rows);
-        }
-        if (cp.r0 != cur_r0) {
-            cur_r0 = cp.r0;
-            cur_g = cp.g;
-#pragma unroll
-            for (int i = 0; i < kGMax; ++i)
-                if (i < cur_g) load_row<FP4>(a.q, a.w, cur_r0 + i, qa[i], w4[i]);
-            int vis = 0;
-            if (tid < cur_g) vis = a.rows.visible(cur_r0 + tid);
-            // Drain here, on the rare piece change, so that the compiler does
-            // not wait for every load in flight before each use of q and w.
-            // The empty asm statements keep the loads above the wait (the
-            // builtin alone does not order memory operations); the builtin is
-            // the form the compiler's wait tracking understands.
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_waitcnt(kVmcnt0);
-            asm volatile("" ::: "memory");
-            if (tid < cur_g) {
-                lds_write_i32(lds_addr(&s_vis[tid]), vis);
-                lds_write_i32(lds_addr(&s_lo[tid]), 0);
+    while (r0 < n && (r0 < end_r || (r0 == end_r && blk_lo < end_b))) {
+        int g, nblk;
+        piece_at<BKV>(a.rows, r0, g, nblk);
+        const int blk_hi = r0 == end_r ? min(end_b, nblk) : nblk;
+        if (blk_lo < blk_hi) {
+            barrier_lds();  // every wave is done with the previous piece
+            stage_rows(a.q, a.w, r0, g, s_q, s_w);
+            if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
+            barrier_lds();
+            const int64_t bt_row = r0 / a.rows.next_n;
+            int b = blk_lo + wave;
+            if (b < blk_hi) {
+                KeyRegs<FP4, BKV> k0, k1;
+                bool ok0 = fetch_block<FP4, BKV>(a, bt_row, b, k0), ok1 = false;
+                Pending p;
+                p.mask = 0;
+                p.col0 = 0;
+                for (;;) {
+                    const int b1 = b + kWaves;
+                    block_step<FP4, BKV>(a, r0, g, bt_row, blk_hi, k0, ok0, b, k1, ok1, b1, s_q, s_w, s_vis, p);
+                    if (b1 >= blk_hi) break;
+                    const int b2 = b1 + kWaves;
+                    block_step<FP4, BKV>(a, r0, g, bt_row, blk_hi, k1, ok1, b1, k0, ok0, b2, s_q, s_w, s_vis, p);
+                    if (b2 >= blk_hi) break;
+                    b = b2;
+                }
+                store_pending<BKV>(a, r0, p);
             }
         }
-        const uint8_t *unused;
-        const bool ok = cp.page(a, unused);
-        const uint8_t *st = s_stage[u % kStages];
-        score_tile<FP4, BKV>(st, qa, w4, cur_g, s_red);
-        barrier_lds();
-        store_tile<FP4, BKV>(st, s_red, s_lo, s_vis, cur_g, cur_r0, cp.blk * BKV, a.max_ctx, ok, true,
-                             a.out, a.out_ld);
-        cp.next(a.rows);
+        r0 += g;
+        blk_lo = 0;
     }
 
     // -inf past each row's last visible block: rows c, c + W, ...
-    for (int r = c; r < a.rows.num_rows; r += W) {
+    for (int r = c; r < n; r += W) {
         const int vis = a.rows.visible_s(r);
         const int start = min((vis + BKV - 1) / BKV * BKV, a.max_ctx);
         fill_neg_inf(a.out + (int64_t)r * a.out_ld, start, a.max_ctx);

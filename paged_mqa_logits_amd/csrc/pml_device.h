@@ -68,6 +68,13 @@ __device__ __forceinline__ void lds_write_i32(uint32_t addr, int v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
+// Plain (compiler-tracked) loads from LDS through a generic pointer that
+// points into a __shared__ array.
+template <typename T>
+__device__ __forceinline__ T lds_ld(const void *p) {
+    return *(const __attribute__((address_space(3))) T *)(const __attribute__((address_space(3))) void *)p;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(const lds_void *)p;
 }

@@ -5,10 +5,12 @@
 // forward_cpu: per-row lengths ke - ks).
 //
 // Grid (x = chunk of kChunk key blocks, y = piece of kGMax consecutive rows).
-// A workgroup scores the blocks of its chunk that intersect the union of its
-// rows' key ranges with the shared tile pipeline (logits_core.h), and fills the
-// chunk's other columns of its rows with -inf. Nothing is read for masked
-// blocks, so a causal prefill does about half the work of the dense product.
+// A workgroup stages q and w of its rows in LDS; its 4 waves take the chunk's
+// blocks that intersect the union of the rows' key ranges in turn, loading 64
+// keys at a time into VGPRs (double-buffered) and scoring them with the core
+// of logits_core.h. The chunk's other columns of its rows are filled with
+// -inf, and nothing is read for them, so a causal prefill does about half the
+// work of the dense product.
 #include "logits_core.h"
 #include "rows.h"
 
@@ -29,15 +31,54 @@ struct RaggedArgs {
     int64_t out_ld;
 };
 
+__device__ __forceinline__ void ragged_block(int g, int b, const KeyRegs<false, 64> &k, const uint8_t *s_q,
+                                             const float *s_w, const int *s_lo, const int *s_hi, Pending &p) {
+    const int s = b * 64 + lane_id();
+    const float scale = __uint_as_float(k.sc[0]);
+    p.mask = 0;
+    p.col0 = b * 64;
+#pragma unroll
+    for (int i = 0; i < kGMax; ++i) {
+        if (i < g) {
+            const int lo = uni(lds_ld<int>(&s_lo[i]));
+            const int hi = uni(lds_ld<int>(&s_hi[i]));
+            float v = score_row<false, 64>(k, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
+            if (s < lo || s >= hi) v = -__builtin_inff();
+            p.v[i] = v;
+            p.mask |= 1 << i;
+        }
+    }
+}
+
+__device__ __forceinline__ void ragged_store(const RaggedArgs &a, int row0, const Pending &p) {
+    const int s = p.col0 + lane_id();
+#pragma unroll
+    for (int i = 0; i < kGMax; ++i)
+        if ((p.mask >> i) & 1)
+            if (s < a.N) a.out[(int64_t)(row0 + i) * a.out_ld + s] = p.v[i];
+}
+
+// One step of a wave's block loop: wait for the current block, store the
+// previous block's logits, request the next block, score the current one.
+__device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g, int u_hi,
+                                            const KeyRegs<false, 64> &kc, int bc, KeyRegs<false, 64> &kn, int bn,
+                                            const uint8_t *s_q, const float *s_w, const int *s_lo, const int *s_hi,
+                                            Pending &p) {
+    touch<false, 64>(kc);
+    ragged_store(a, row0, p);
+    if (bn < u_hi) load_contig(a.k, a.k_scale, a.N, bn * 64, kn);
+    ragged_block(g, bc, kc, s_q, s_w, s_lo, s_hi, p);
+}
+
 __global__ __launch_bounds__(kThreads, 2) void ragged_logits_kernel(RaggedArgs a) {
     constexpr int BKV = 64;
-    using C = TileCfg<false, BKV>;
-    __shared__ __attribute__((aligned(16))) uint8_t s_stage[kStages][C::TILE];
-    __shared__ __attribute__((aligned(16))) float s_red[kGMax][kWaves][BKV];
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
+    __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_lo[kGMax];
     __shared__ int s_hi[kGMax];
 
     const int tid = threadIdx.x;
+    const int wave = uni(tid / kWave);
     const int N = a.N;
     const int row0 = blockIdx.y * kGMax;
     const int g = uni(min(kGMax, a.M - row0));
@@ -73,50 +114,33 @@ __global__ __launch_bounds__(kThreads, 2) void ragged_logits_kernel(RaggedArgs a
             fill_neg_inf(row, c0 * BKV, cend);
         }
     }
-    const int nunits = u_hi - u_lo;
-    if (nunits <= 0) return;
+    if (u_hi <= u_lo) return;
 
-    v8i qa[kGMax];
-    v4f w4[kGMax];
-#pragma unroll
-    for (int i = 0; i < kGMax; ++i)
-        if (i < g) load_row<false>(a.q, a.w, row0 + i, qa[i], w4[i]);
-    int lo = 0, hi = 0;
+    stage_rows(a.q, a.w, row0, g, s_q, s_w);
     if (tid < g) {
-        lo = min(max(a.ks[row0 + tid], 0), N);
-        hi = min(max(a.ke[row0 + tid], lo), N);
+        const int lo = min(max(a.ks[row0 + tid], 0), N);
+        s_lo[tid] = lo;
+        s_hi[tid] = min(max(a.ke[row0 + tid], lo), N);
     }
-    // Everything above has landed before the first key tile is requested, so
-    // the per-tile waits below count tile loads (and logit stores) only.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    asm volatile("" ::: "memory");
-    if (tid < g) {
-        lds_write_i32(lds_addr(&s_lo[tid]), lo);
-        lds_write_i32(lds_addr(&s_hi[tid]), hi);
-    }
+    barrier_lds();
 
-#pragma unroll
-    for (int k = 0; k < kStages - 1; ++k)
-        if (k < nunits) issue_contig<BKV>(a.k, a.k_scale, N, (u_lo + k) * BKV, s_stage[k]);
-
-    for (int u = 0; u < nunits; ++u) {
-        // tile u has landed once at most (kStages - 2) tiles issued after it are in flight
-        const int ahead = min(nunits, u + kStages - 1) - (u + 1);
-        if (ahead >= kStages - 2)
-            wait_vmcnt<(kStages - 2) * C::NLD>();
-        else
-            wait_vmcnt<0>();
-        barrier_lds();
-        if (u + kStages - 1 < nunits)
-            issue_contig<BKV>(a.k, a.k_scale, N, (u_lo + u + kStages - 1) * BKV,
-                              s_stage[(u + kStages - 1) % kStages]);
-        const uint8_t *st = s_stage[u % kStages];
-        score_tile<false, BKV>(st, qa, w4, g, s_red);
-        barrier_lds();
-        store_tile<false, BKV>(st, s_red, s_lo, s_hi, g, row0, (u_lo + u) * BKV, N, true, false, a.out,
-                               a.out_ld);
+    int b = u_lo + wave;
+    if (b >= u_hi) return;
+    KeyRegs<false, BKV> k0, k1;
+    load_contig(a.k, a.k_scale, N, b * BKV, k0);
+    Pending p;
+    p.mask = 0;
+    p.col0 = 0;
+    for (;;) {
+        const int b1 = b + kWaves;
+        ragged_step(a, row0, g, u_hi, k0, b, k1, b1, s_q, s_w, s_lo, s_hi, p);
+        if (b1 >= u_hi) break;
+        const int b2 = b1 + kWaves;
+        ragged_step(a, row0, g, u_hi, k1, b1, k0, b2, s_q, s_w, s_lo, s_hi, p);
+        if (b2 >= u_hi) break;
+        b = b2;
     }
+    ragged_store(a, row0, p);
 }
 
 }  // namespace pml

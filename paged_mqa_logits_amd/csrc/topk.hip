@@ -4,21 +4,24 @@
 // request-local positions as in the CPU decode path of the sparse_attn_indexer
 // page). Selection order: larger value first, equal values by lower position.
 //
-// One workgroup per row:
-//  1. Radix select on an order-preserving 32-bit key (NaN lowest, -0 == +0):
-//     three histogram passes over digits of 11, 11 and 10 bits find the exact
-//     key T of the k-th selected element and how many elements equal to T are
-//     taken (the lowest-positioned ones).
-//  2. One ordered compaction pass: a block-wide scan of (key > T, key == T)
-//     gives each selected element its output slot, so positions come out
-//     ascending without a sort; the pass stops once k elements are placed.
+// One workgroup per row, radix select on an order-preserving 32-bit key (NaN
+// lowest, -0 == +0) followed by an ordered compaction, so positions come out
+// ascending without a sort:
+//  * A row that fits the LDS candidate list is read once into it.
+//  * A wider row takes three streaming passes: a histogram of the top 11 key
+//    bits fixes the bucket b holding the k-th key; every wave counts, then
+//    appends in position order, the elements whose top digit is >= b (wave
+//    ballots give the order inside a wave, per-wave counts across waves).
+//  * The remaining 11 + 10 key bits are selected inside the list, then one
+//    block scan over it places every selected element.
+//  * If the candidates overflow the list (heavy ties), the selection finishes
+//    with passes over the row itself.
 #include "pml_device.h"
 
 namespace pml {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
 constexpr int kBins = 2048;
+constexpr int kUnroll = 4;  // float4 loads in flight per lane in the streaming passes
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -27,9 +30,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive scan of one uint32 per thread over the whole workgroup; returns
-// the inclusive prefix and writes the workgroup total to *total.
+template <int NT>
+struct TopkCfg {
+    static constexpr int NW = NT / kWave;
+    static constexpr int CAP = NT == 1024 ? 12288 : 8192;  // candidate list entries
+};
+
+// Inclusive scan of one uint32 per thread over the workgroup; *total gets the sum.
+template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t *s_wave, uint32_t *total) {
+    constexpr int NW = NT / kWave;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
 #pragma unroll
@@ -40,20 +50,61 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t *s_wave, uin
     if (lane == kWave - 1) s_wave[wave] = x;
     __syncthreads();
     if (wave == 0) {
-        uint32_t v = lane < kTopkWaves ? s_wave[lane] : 0u;
+        uint32_t v = lane < NW ? s_wave[lane] : 0u;
 #pragma unroll
-        for (int o = 1; o < kTopkWaves; o <<= 1) {
+        for (int o = 1; o < NW; o <<= 1) {
             const uint32_t y = __shfl_up(v, o, kWave);
             if (lane >= o) v += y;
         }
-        if (lane < kTopkWaves) s_wave[kTopkWaves + lane] = v;  // inclusive wave prefix
+        if (lane < NW) s_wave[NW + lane] = v;
     }
     __syncthreads();
-    const uint32_t before = wave > 0 ? s_wave[kTopkWaves + wave - 1] : 0u;
-    *total = s_wave[2 * kTopkWaves - 1];
+    const uint32_t before = wave > 0 ? s_wave[NW + wave - 1] : 0u;
+    *total = s_wave[2 * NW - 1];
     const uint32_t r = x + before;
-    __syncthreads();  // s_wave is reused by the next call
+    __syncthreads();
     return r;
+}
+
+// Exclusive prefix over the wave's lanes of c (0 <= c <= 4), and the wave total.
+__device__ __forceinline__ void wave_prefix4(uint32_t c, uint32_t &pre, uint32_t &tot) {
+    pre = 0;
+    tot = 0;
+#pragma unroll
+    for (int b = 0; b < 3; ++b) {
+        const uint64_t m = __ballot((c >> b) & 1u);
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        pre += below << b;
+        tot += (uint32_t)__popcll(m) << b;
+    }
+}
+
+// Find the bin holding the kk-th largest key among s_hist[0, nbins): writes
+// (bin, count of keys in higher bins) to s_pick.
+template <int NT>
+__device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint32_t kk, uint32_t *s_wave,
+                                         uint32_t *s_pick) {
+    const int per = (nbins + NT - 1) / NT;
+    const int t = threadIdx.x;
+    // thread t owns bins top - t*per - j, j < per (descending)
+    uint32_t own = 0;
+    for (int j = 0; j < per; ++j) {
+        const int b = nbins - 1 - (t * per + j);
+        if (b >= 0) own += s_hist[b];
+    }
+    uint32_t tot;
+    uint32_t above = block_scan<NT>(own, s_wave, &tot) - own;
+    for (int j = 0; j < per; ++j) {
+        const int b = nbins - 1 - (t * per + j);
+        if (b < 0) break;
+        const uint32_t h = s_hist[b];
+        if (above < kk && kk <= above + h) {
+            s_pick[0] = (uint32_t)b;
+            s_pick[1] = above;
+        }
+        above += h;
+    }
+    __syncthreads();
 }
 
 struct TopkArgs {
@@ -68,12 +119,50 @@ struct TopkArgs {
     int64_t out_ld;
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
+// Position-ordered float4 walk of one wave's share [q0, q1) of the row's 16-B
+// groups; f(p, key, valid) is called for the 4 elements of every group in
+// position order across the wave (j, lane, e).
+template <typename F>
+__device__ __forceinline__ void wave_walk(const float *rowbase, int lo, int hi, int q0, int q1, F &&f) {
+    const int lane = lane_id();
+    for (int g = q0; g < q1; g += kWave * kUnroll) {
+        v4f x[kUnroll];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int q = g + j * kWave + lane;
+            x[j] = q < q1 ? *(const v4f *)(rowbase + 4 * (int64_t)q) : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const int q = g + j * kWave + lane;
+            uint32_t key[4];
+            bool ok[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = 4 * q + e;
+                ok[e] = q < q1 && p >= lo && p < hi;
+                key[e] = order_key(x[j][e]);
+            }
+            f(4 * q, key, ok);
+        }
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
+    using Cfg = TopkCfg<NT>;
+    constexpr int NW = Cfg::NW;
+    constexpr int CAP = Cfg::CAP;
     __shared__ uint32_t s_hist[kBins];
-    __shared__ uint32_t s_wave[2 * kTopkWaves];
+    __shared__ uint32_t s_key[CAP];
+    __shared__ int32_t s_pos[CAP];
+    __shared__ uint32_t s_wave[2 * NW];
+    __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
 
     const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
     const int r = blockIdx.x;
     int lo = a.ks ? a.ks[r] : 0;
     int hi;
@@ -88,73 +177,161 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkArgs a) {
     const int n = hi - lo;
     const int k = a.k;
     int32_t *out = a.out + (int64_t)r * a.out_ld;
-    const float *row = a.logits + (int64_t)r * a.ld + lo;
+    const float *rowbase = a.logits + (int64_t)r * a.ld;  // 16-B aligned
 
     if (n <= k) {
-        for (int j = tid; j < k; j += kTopkThreads) out[j] = j < n ? j : -1;
+        for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
         return;
     }
 
-    // 1. radix select of the k-th largest key
-    uint32_t prefix = 0, mask = 0;
-    uint32_t kk = (uint32_t)k;  // elements still to take inside the current prefix bucket
+    uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
+    int first_pass = 0;  // radix digits already fixed: 0, or 1 after the streaming histogram
+    int m = 0;           // entries in the candidate list (position order, positions relative to lo)
+    bool in_list = true;
+
+    // this wave's share of the 16-B groups covering [lo, hi)
+    const int gq0 = lo >> 2, gq1 = (hi + 3) >> 2;
+    const int span = (gq1 - gq0 + NW - 1) / NW;
+    const int wq0 = min(gq0 + wave * span, gq1), wq1 = min(wq0 + span, gq1);
+
+    if (n <= CAP) {
+        for (int i = tid; i < n; i += NT) {
+            s_key[i] = order_key(rowbase[lo + i]);
+            s_pos[i] = i;
+        }
+        m = n;
+        __syncthreads();
+    } else {
+        // pass 1: histogram of the top 11 bits
+        for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
+        __syncthreads();
+        wave_walk(rowbase, lo, hi, wq0, wq1, [&](int, const uint32_t *key, const bool *ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ok[e]) atomicAdd(&s_hist[key[e] >> 21], 1u);
+        });
+        __syncthreads();
+        pick_bin<NT>(s_hist, kBins, kk, s_wave, s_pick);
+        prefix = s_pick[0] << 21;
+        mask = 0x7ffu << 21;
+        kk -= s_pick[1];
+        first_pass = 1;
+        // pass 2: per-wave count of candidates (top digit >= the picked bin)
+        uint32_t cnt = 0;
+        wave_walk(rowbase, lo, hi, wq0, wq1, [&](int, const uint32_t *key, const bool *ok) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += (ok[e] && key[e] >= prefix) ? 1u : 0u;
+            uint32_t pre, tot;
+            wave_prefix4(c, pre, tot);
+            cnt += tot;
+        });
+        if (lane == 0) s_wcnt[wave] = cnt;
+        __syncthreads();
+        uint32_t off = 0, total = 0;
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t c = s_wcnt[w];
+            if (w < wave) off += c;
+            total += c;
+        }
+        if (total <= (uint32_t)CAP) {
+            // pass 3: ordered append of the candidates
+            wave_walk(rowbase, lo, hi, wq0, wq1, [&](int p0, const uint32_t *key, const bool *ok) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c += (ok[e] && key[e] >= prefix) ? 1u : 0u;
+                uint32_t pre, tot;
+                wave_prefix4(c, pre, tot);
+                uint32_t at = off + pre;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (ok[e] && key[e] >= prefix) {
+                        s_key[at] = key[e];
+                        s_pos[at] = p0 + e - lo;
+                        ++at;
+                    }
+                off += tot;
+            });
+            m = (int)total;
+        } else {
+            in_list = false;
+        }
+        __syncthreads();
+    }
+
+    // remaining radix digits (11, 11, 10 bits from the top)
 #pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
+    for (int pass = first_pass; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const uint32_t nbins = pass == 2 ? 1024u : 2048u;
-        for (int b = tid; b < kBins; b += kTopkThreads) s_hist[b] = 0;
+        const int nbins = pass == 2 ? 1024 : 2048;
+        for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         __syncthreads();
-        for (int i = tid; i < n; i += kTopkThreads) {
-            const uint32_t key = order_key(row[i]);
-            if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+        if (in_list) {
+            for (int i = tid; i < m; i += NT) {
+                const uint32_t key = s_key[i];
+                if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+            }
+        } else {
+            for (int i = lo + tid; i < hi; i += NT) {
+                const uint32_t key = order_key(rowbase[i]);
+                if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+            }
         }
         __syncthreads();
-        // counts from the top bin down: thread t owns bins nbins-1-2t and nbins-2-2t
-        const int b1 = (int)nbins - 1 - 2 * tid;
-        const int b0 = b1 - 1;
-        const uint32_t h1 = b1 >= 0 ? s_hist[b1] : 0u;
-        const uint32_t h0 = b0 >= 0 ? s_hist[b0] : 0u;
-        uint32_t tot;
-        const uint32_t incl = block_scan(h1 + h0, s_wave, &tot);
-        const uint32_t gt1 = incl - h1 - h0;  // elements in bins above b1
-        if (b1 >= 0 && gt1 < kk && kk <= gt1 + h1) {
-            s_pick[0] = (uint32_t)b1;
-            s_pick[1] = gt1;
-        }
-        if (b0 >= 0 && gt1 + h1 < kk && kk <= gt1 + h1 + h0) {
-            s_pick[0] = (uint32_t)b0;
-            s_pick[1] = gt1 + h1;
-        }
-        __syncthreads();
+        pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
         prefix |= s_pick[0] << shift;
-        mask |= (nbins - 1) << shift;
+        mask |= (uint32_t)(nbins - 1) << shift;
         kk -= s_pick[1];
         __syncthreads();
     }
     const uint32_t T = prefix;
-    const uint32_t need = kk;  // elements equal to T that are taken (1 <= need)
+    const uint32_t need = kk;  // elements equal to T that are taken (>= 1)
     const uint32_t n_gt = (uint32_t)k - need;
 
-    // 2. ordered compaction
-    uint32_t carry_gt = 0, carry_eq = 0;
-#pragma unroll 1
-    for (int base = 0; base < n; base += kTopkThreads) {
-        const int i = base + tid;
-        uint32_t key = 0;
-        const bool valid = i < n;
-        if (valid) key = order_key(row[i]);
-        const uint32_t gt = valid && key > T;
-        const uint32_t eq = valid && key == T;
+    // ordered compaction: slot = (# greater before) + min(# equal before, need)
+    if (in_list) {
+        const int per = (m + NT - 1) / NT;
+        const int i0 = min(tid * per, m), i1 = min(i0 + per, m);
+        uint32_t gt = 0, eq = 0;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t key = s_key[i];
+            gt += key > T;
+            eq += key == T;
+        }
         uint32_t tot;
         const uint32_t packed = gt | (eq << 16);
-        const uint32_t incl = block_scan(packed, s_wave, &tot);
-        const uint32_t excl = incl - packed;
-        const uint32_t gt_before = carry_gt + (excl & 0xffffu);
-        const uint32_t eq_before = carry_eq + (excl >> 16);
-        if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = i;
-        carry_gt += tot & 0xffffu;
-        carry_eq += tot >> 16;
-        if (carry_gt >= n_gt && carry_eq >= need) break;  // all k placed (uniform)
+        const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
+        uint32_t gb = excl & 0xffffu, eb = excl >> 16;
+        for (int i = i0; i < i1; ++i) {
+            const uint32_t key = s_key[i];
+            if (key > T) {
+                out[gb + min(eb, need)] = s_pos[i];
+                ++gb;
+            } else if (key == T) {
+                if (eb < need) out[gb + eb] = s_pos[i];
+                ++eb;
+            }
+        }
+    } else {
+        uint32_t carry_gt = 0, carry_eq = 0;
+#pragma unroll 1
+        for (int base = 0; base < n; base += NT) {
+            const int i = base + tid;
+            uint32_t key = 0;
+            const bool valid = i < n;
+            if (valid) key = order_key(rowbase[lo + i]);
+            const uint32_t gt = valid && key > T;
+            const uint32_t eq = valid && key == T;
+            uint32_t tot;
+            const uint32_t packed = gt | (eq << 16);
+            const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
+            const uint32_t gt_before = carry_gt + (excl & 0xffffu);
+            const uint32_t eq_before = carry_eq + (excl >> 16);
+            if (gt || (eq && eq_before < need)) out[gt_before + min(eq_before, need)] = i;
+            carry_gt += tot & 0xffffu;
+            carry_eq += tot >> 16;
+            if (carry_gt >= n_gt && carry_eq >= need) break;  // all k placed (uniform)
+        }
     }
 }
 
@@ -179,7 +356,13 @@ extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_l
     if (num_rows == 0) return PML_OK;
     if (!logits || !ke || !out) return PML_ERR_NULL;
     if (out_ld < k) return PML_ERR_STRIDE;
+    if (((uintptr_t)logits & 15) != 0) return PML_ERR_ALIGN;
+    if (logits_ld % 4 != 0) return PML_ERR_STRIDE;
     pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld};
-    hipLaunchKernelGGL(pml::topk_kernel, dim3(num_rows), dim3(pml::kTopkThreads), 0, (hipStream_t)stream, a);
+    hipStream_t st = (hipStream_t)stream;
+    if (max_width <= pml::TopkCfg<256>::CAP)
+        hipLaunchKernelGGL(pml::topk_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(pml::topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }

@@ -78,6 +78,26 @@ def test_bounds_and_next_n():
     _shared_input_check(L, rng.integers(100, 9000, 4), 333, next_n=3)
 
 
+def test_wide_rows_streaming_list_and_fallback():
+    """Rows wider than the in-LDS list: the streaming passes, the in-list path
+    of the wide-row kernel, and the fallback when ties overflow the list."""
+    rng = np.random.default_rng(830)
+    W = 40000
+    rows = [rng.standard_normal(W),                     # streaming, few candidates
+            np.zeros(W),                                # every key equal: list overflows
+            np.round(rng.standard_normal(W) * 2),       # heavy ties
+            np.concatenate([rng.standard_normal(9000), np.full(W - 9000, -np.inf)]),
+            rng.standard_normal(W) * 1e3,
+            np.arange(W, dtype=np.float64)]             # ascending: the top is at the end
+    L = np.stack(rows)
+    G.banner("top-k wide rows")
+    for k, ke in ((1, [W] * 6), (2048, [W] * 6), (4096, [W] * 6),
+                  (2048, [10000, 12288, 12289, 40000, 30001, 39999])):
+        _shared_input_check(L, ke, k)
+    ks = np.array([0, 5, 100, 3, 17, 20000])
+    _shared_input_check(L, np.full(6, W), 777, ks=ks)
+
+
 def _acceptance(gpu: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray, k: int, wsum: np.ndarray):
     for r in range(gpu.shape[0]):
         n = max(0, int(hi[r] - lo[r]))
