@@ -99,6 +99,7 @@ class RaggedBench:
         self.logits = torch.empty(case.M, pml.logits_ld(case.N), dtype=torch.float32, device=d)
         self.topk = torch.empty(case.M, case.topk, dtype=torch.int32, device=d)
         self.pairs = int((case.ke - case.ks).clamp_min(0).sum())
+        self.max_width = int((case.ke - case.ks).clamp_min(0).max())
 
     def step(self, i: int, ev=None):
         c = self.case
@@ -108,7 +109,7 @@ class RaggedBench:
         pml.mqa_logits(self.q, self.k, self.ksc, self.w, self.ks, self.ke, logits=self.logits)
         if ev is not None:
             ev[2].record()
-        pml.top_k_per_row(self.logits, self.ke, c.topk, ks=self.ks, max_width=c.N, out=self.topk)
+        pml.top_k_per_row(self.logits, self.ke, c.topk, ks=self.ks, max_width=self.max_width, out=self.topk)
         if ev is not None:
             ev[3].record()
 

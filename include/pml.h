@@ -170,7 +170,9 @@ int mqa_logits(const void *q, int M, int num_heads, int head_dim, const void *k,
  * topk_tokens, max_seq_len)", sparse_attn_indexer page, _varlen_decode_rows;
  * int32 output preset to -1 and request-local positions, forward_cpu).
  *
- *   logits     fp32 [num_rows][logits_ld].
+ *   logits     fp32 [num_rows][logits_ld], 16-B aligned, logits_ld a multiple
+ *              of 4 (else PML_ERR_ALIGN / PML_ERR_STRIDE), as the logits calls
+ *              write them.
  *   ks         int32 [num_rows] first valid column per row, or NULL (= 0).
  *   ke         int32 end of the valid columns: [num_rows] when next_n == 1 or
  *              ks != NULL; else [num_rows / next_n] full lengths and row j of
@@ -179,14 +181,16 @@ int mqa_logits(const void *q, int M, int num_heads, int head_dim, const void *k,
  *   next_n     >= 1; must be 1 when ks is given.
  *   k          1..4096 (else PML_ERR_K).
  *   max_width  upper bound of ke - ks over all rows (the selector's
- *              max_seq_len); sizes the workspace. Wider rows are an error of
- *              the caller and are cut to max_width.
+ *              max_seq_len). Rows up to 8192 wide take a variant that keeps the
+ *              whole row on chip. Wider rows are an error of the caller and are
+ *              cut to max_width.
  *   out        int32 [num_rows][out_ld], out_ld >= k: per row the selected
  *              positions minus ks in ascending order, then -1 up to k.
  *              Order of selection: larger value first, equal values by lower
  *              position (-0.0 equals +0.0).
  *   workspace  device scratch of at least top_k_per_row_workspace_size()
- *              bytes, 16-B aligned (may be NULL when that size is 0).
+ *              bytes, 16-B aligned (may be NULL when that size is 0; this
+ *              version needs none).
  */
 size_t top_k_per_row_workspace_size(int num_rows, int max_width, int k);
 int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
