@@ -11,12 +11,13 @@
 // shared by the 4 waves. Each wave takes whole key blocks on its own: the
 // block's keys go from HBM straight into VGPRs, already laid out as the B
 // operand of v_mfma_f32_16x16x128_f8f6f4 (lane l holds token l % 16 of a
-// 16-token slice), double-buffered so the next block is in flight while this
-// one is scored. For every row the wave runs 4 head tiles x (BKV / 16) token
+// 16-token slice), three buffers deep so two blocks are in flight while one
+// is scored. For every row the wave runs 4 head tiles x (BKV / 16) token
 // slices of MFMAs, folds ReLU and w into per-lane partial sums in registers,
 // and a transpose-reduce with v_permlane32/16_swap leaves one finished token
-// per lane, stored as a coalesced 4-byte-per-lane row segment. No barrier is
-// taken per block, only at piece changes.
+// per lane; the block's logits wait in LDS and go out as coalesced
+// 4-byte-per-lane row segments one step later. No barrier is taken per
+// block, only at piece changes.
 #pragma once
 
 #include "pml_device.h"
@@ -24,6 +25,8 @@
 namespace pml {
 
 constexpr int kQBytes = PML_HEADS * PML_HEAD_DIM;  // q of one row: 8 KB
+constexpr int kCW = 4;                             // waves per workgroup
+constexpr int kLThreads = kCW * kWave;
 
 template <bool FP4, int BKV>
 struct BlockCfg {
@@ -57,8 +60,10 @@ __device__ __forceinline__ bool out_lane(int lane) {
 }
 
 // Load a cache page (values region [BKV][TOKB], then scales) into registers.
-// The 32 key bytes of lane group g (d = 32g .. 32g+31 for fp8, the 32 fp4
-// values of k-block g for MXFP4) are the lane's k-range; see load_a.
+// Lane group g takes the hardware's k order (see load_a): fp8 bytes
+// 16g .. 16g+15 and 64+16g .. 64+16g+15 of its token, MXFP4 bytes 16g .. 16g+15
+// (the 32 fp4 values of k-block g). Each load instruction then reads one
+// contiguous 64-byte run per token.
 template <bool FP4, int BKV>
 __device__ __forceinline__ void load_page(const uint8_t *pg, KeyRegs<FP4, BKV> &k) {
     using C = BlockCfg<FP4, BKV>;
@@ -67,12 +72,12 @@ __device__ __forceinline__ void load_page(const uint8_t *pg, KeyRegs<FP4, BKV> &
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) {
         const uint8_t *tok = pg + (16 * t + tl) * C::TOKB;
-        if (FP4) {
+        if constexpr (FP4) {
             k.v[t][0] = *(const v4i *)(tok + 16 * grp);
             k.sc[t] = *(const uint32_t *)(pg + C::VBYTES + (16 * t + tl) * 4) >> (8 * grp);
         } else {
-            k.v[t][0] = *(const v4i *)(tok + 32 * grp);
-            k.v[t][1] = *(const v4i *)(tok + 32 * grp + 16);
+            k.v[t][0] = *(const v4i *)(tok + 16 * grp);
+            k.v[t][1] = *(const v4i *)(tok + 64 + 16 * grp);
         }
     }
     if (!FP4) k.sc[0] = *(const uint32_t *)(pg + C::VBYTES + 4 * out_token<BKV>(lane));
@@ -88,8 +93,8 @@ __device__ __forceinline__ void load_contig(const uint8_t *k, const float *k_sca
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint8_t *tok = k + (int64_t)min(t0 + 16 * t + tl, N - 1) * PML_HEAD_DIM;
-        kr.v[t][0] = *(const v4i *)(tok + 32 * grp);
-        kr.v[t][1] = *(const v4i *)(tok + 32 * grp + 16);
+        kr.v[t][0] = *(const v4i *)(tok + 16 * grp);
+        kr.v[t][1] = *(const v4i *)(tok + 64 + 16 * grp);
     }
     kr.sc[0] = __float_as_uint(k_scale[min(t0 + lane, N - 1)]);
 }
@@ -104,36 +109,37 @@ __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int
                                            float *s_w) {
     const int tid = threadIdx.x;
     const int nchunk = g * (kQBytes / 16);
-    for (int i = tid; i < nchunk; i += kThreads) {
+    for (int i = tid; i < nchunk; i += kLThreads) {
         const int row = i / (kQBytes / 16);
         const int rem = i % (kQBytes / 16);
         const int h = rem / 8, c = rem % 8;
         const v4i x = *(const v4i *)(q + (r0 + row) * kQBytes + rem * 16);
         *(v4i *)(s_q + row * kQBytes + q_lds_off(h, c)) = x;
     }
-    for (int i = tid; i < g * PML_HEADS; i += kThreads) s_w[i] = w[r0 * PML_HEADS + i];
+    for (int i = tid; i < g * PML_HEADS; i += kLThreads) s_w[i] = w[r0 * PML_HEADS + i];
 }
 
-// A operand (q of heads 16 ht + lane % 16) of one staged row. fp8 x fp8
-// tiles only need A and B in the same k order, so both take d = 32g .. 32g+31
-// for lane group g. Against fp4 keys q follows the hardware's fp8 order for
-// v_mfma_scale_f32_16x16x128_f8f6f4, as measured on gfx950: an fp8 operand
-// holds k = 16g .. 16g+15 in bytes 0-15 and k = 64+16g .. 64+16g+15 in bytes
-// 16-31, while an fp4 operand holds k = 32g .. 32g+31 in order (low nibble
-// first) and the e8m0 scale of k-block g comes from lane group g.
+// A operand (q of heads 16 ht + lane % 16) of one staged row, in the
+// hardware's k order for v_mfma_scale_f32_16x16x128_f8f6f4 as measured on
+// gfx950: an fp8 operand holds k = 16g .. 16g+15 in bytes 0-15 and
+// k = 64+16g .. 64+16g+15 in bytes 16-31 of lane group g, an fp4 operand holds
+// k = 32g .. 32g+31 in order (low nibble first), and the e8m0 scale of
+// k-block g comes from lane group g. (fp8 x fp8 only needs A and B in the
+// same order; the hardware order also keeps the key loads contiguous.)
 template <bool FP4>
 __device__ __forceinline__ v8i load_a(const uint8_t *s_qrow, int ht) {
     const int lane = lane_id();
     const int h = 16 * ht + (lane & 15), grp = lane >> 4;
-    const int c0 = FP4 ? grp : 2 * grp;
-    const int c1 = FP4 ? 4 + grp : 2 * grp + 1;
+    const int c0 = grp;
+    const int c1 = 4 + grp;
     const v4i lo = lds_ld<v4i>(s_qrow + q_lds_off(h, c0));
     const v4i hi = lds_ld<v4i>(s_qrow + q_lds_off(h, c1));
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Score one staged row against the block in registers; returns this lane's
-// sum over all 64 heads for token out_token(lane) (before the key scale).
+// Score one staged row against the block in registers; returns twice this
+// lane's sum over all 64 heads for token out_token(lane) (before the key
+// scale; the factor 2 is exact and the caller folds 1/2 into the scale).
 template <bool FP4, int BKV>
 __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k, const uint8_t *s_qrow,
                                            const float *s_wrow) {
@@ -150,7 +156,7 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k, const uin
 #pragma unroll
         for (int t = 0; t < C::NT; ++t) {
             v4f d;
-            if (FP4) {
+            if constexpr (FP4) {
                 const v8i b = v8i{k.v[t][0][0], k.v[t][0][1], k.v[t][0][2], k.v[t][0][3], 0, 0, 0, 0};
                 d = mfma_fp8_fp4(a, b, (int)(k.sc[t] & 0xffu));
             } else {
@@ -158,8 +164,10 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k, const uin
                                   k.v[t][1][0], k.v[t][1][1], k.v[t][1][2], k.v[t][1][3]};
                 d = mfma_fp8(a, b);
             }
-            p[t] += w4[0] * fmaxf(d[0], 0.f) + w4[1] * fmaxf(d[1], 0.f) + w4[2] * fmaxf(d[2], 0.f) +
-                    w4[3] * fmaxf(d[3], 0.f);
+            // d + |d| = 2 ReLU(d) is one add with an abs modifier (fmaxf would
+            // canonicalise its input first); the factor 2 is taken out at the end
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p[t] = __builtin_fmaf(w4[i], d[i] + __builtin_fabsf(d[i]), p[t]);
         }
     }
     // lane l holds partial sums of token 16t + l % 16 over heads of lane group
@@ -195,13 +203,37 @@ __device__ __forceinline__ void touch(const KeyRegs<FP4, BKV> &k) {
     for (int j = 0; j < C::NS; ++j) asm volatile("" ::"v"(k.sc[j]));
 }
 
-// Logits of one block for up to kGMax rows, held in registers until the
-// next step stores them (bit i of mask: row i is stored).
-struct Pending {
-    float v[kGMax];
-    int mask;
-    int col0;
+// A 4-byte global store issued as inline asm. The compiler's wait tracking
+// then counts only key-block loads in the vector-memory counter and waits for
+// a block exactly, leaving the blocks behind it in flight; in hardware the
+// store still counts, which can only make those waits stricter (loads
+// complete in order among themselves). A single-dword store reads its data
+// register when it issues, so no hazard guard is needed around it.
+__device__ __forceinline__ void store_f32_async(float *p, float v) {
+    asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+// One block's logits for up to kGMax rows, parked in the wave's own LDS slot
+// until the next step stores them ahead of the key loads it issues.
+template <int BKV>
+struct WaveSlot {
+    float v[kGMax][BKV];
 };
+
+// Store rows (bit i of mask) of the parked block at columns [col0, col0 + BKV),
+// never at or past ncols.
+template <int BKV>
+__device__ __forceinline__ void flush_slot(const WaveSlot<BKV> &sl, int mask, int64_t row0, int col0, int ncols,
+                                           float *out, int64_t out_ld) {
+    const int lane = lane_id();
+    const int s = col0 + lane;
+    const bool st = lane < BKV && s < ncols;
+    for (int m = mask; m; m &= m - 1) {
+        const int i = __builtin_ctz(m);
+        const float v = lds_ld<float>(&sl.v[i][lane % BKV]);
+        if (st) store_f32_async(out + (row0 + i) * out_ld + s, v);
+    }
+}
 
 // Fill columns [c0, c1) of one row with -inf (the whole workgroup).
 __device__ __forceinline__ void fill_neg_inf(float *row, int c0, int c1) {
@@ -211,7 +243,7 @@ __device__ __forceinline__ void fill_neg_inf(float *row, int c0, int c1) {
     const int a4 = min((c0 + 3) & ~3, c1);  // first 16-B aligned column (rows are 16-B aligned)
     const int b4 = max(a4, c1 & ~3);
     if (c0 + tid < a4) row[c0 + tid] = -__builtin_inff();
-    for (int col = a4 + 4 * tid; col < b4; col += 4 * kThreads) *(v4f *)(row + col) = ninf;
+    for (int col = a4 + 4 * tid; col < b4; col += 4 * kLThreads) *(v4f *)(row + col) = ninf;
     if (b4 + tid < c1) row[b4 + tid] = -__builtin_inff();
 }
 

@@ -7,14 +7,20 @@
 //    rows of one request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a
 //    request are processed together), so each key page is read from HBM once
 //    for all of them.
-//  * The 4 waves take the blocks of the current piece in turn; each loads its
-//    page from HBM straight into VGPRs (double-buffered) and scores it
-//    against every row of the piece, whose q and w sit in LDS. Waves meet at
-//    a barrier only when the piece changes.
+//  * The 4 waves take the blocks of the current piece in turn (wave w scores
+//    blocks blk0 + w, blk0 + w + 4, ...). Each loads its pages from HBM
+//    straight into VGPRs, three buffers deep, and scores them against every
+//    row of the piece, whose q and w sit in LDS. Waves meet at a barrier only
+//    when the piece changes.
+//  * Logit stores are issued as inline asm one step after the block is
+//    scored, so the compiler waits for a page exactly and the two pages
+//    behind it stay in flight.
 //  * All per-unit metadata (schedule, block table, lengths, request ids) is
 //    read through the scalar cache.
 //  * Columns past each row's last visible block are filled with -inf by the
 //    workgroups after their units (row-strided).
+#include <type_traits>
+
 #include "logits_core.h"
 #include "rows.h"
 
@@ -47,66 +53,52 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
     return ok;
 }
 
-// Score block b against the g staged rows; rows whose visible length ends
-// before the block are skipped (their tail is filled separately).
-template <bool FP4, int BKV>
-__device__ __forceinline__ void score_block(const PagedArgs &a, int g, int b, const KeyRegs<FP4, BKV> &k, bool ok,
-                                            const uint8_t *s_q, const float *s_w, const int *s_vis, Pending &p) {
-    const int col0 = b * BKV;
-    const int s = col0 + out_token<BKV>(lane_id());
-    const float scale = FP4 ? 1.f : __uint_as_float(k.sc[0]);
-    p.mask = 0;
-    p.col0 = col0;
-#pragma unroll
-    for (int i = 0; i < kGMax; ++i) {
-        if (i < g) {
-            const int vis = uni(lds_ld<int>(&s_vis[i]));
-            if (col0 < vis) {
-                float v = score_row<FP4, BKV>(k, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
-                if (!ok) v = __builtin_nanf("");
-                if (s >= vis) v = -__builtin_inff();
-                p.v[i] = v;
-                p.mask |= 1 << i;
-            }
-        }
-    }
-}
-
-template <int BKV>
-__device__ __forceinline__ void store_pending(const PagedArgs &a, int r0, const Pending &p) {
-    const int lane = lane_id();
-    const int s = p.col0 + out_token<BKV>(lane);
-    const bool st = out_lane<BKV>(lane) && s < a.max_ctx;
-#pragma unroll
-    for (int i = 0; i < kGMax; ++i)
-        if ((p.mask >> i) & 1)
-            if (st) a.out[(int64_t)(r0 + i) * a.out_ld + s] = p.v[i];
-}
-
-// One step of a wave's block loop: wait for the current block, store the
-// previous block's logits, request the next block, score the current one.
-template <bool FP4, int BKV>
-__device__ __forceinline__ void block_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int blk_hi,
-                                           const KeyRegs<FP4, BKV> &kc, bool okc, int bc, KeyRegs<FP4, BKV> &kn,
-                                           bool &okn, int bn, const uint8_t *s_q, const float *s_w,
-                                           const int *s_vis, Pending &p) {
+// One step of a wave's block loop: wait for block b, store the previous
+// block's logits, request block bp (two steps ahead; with PF) into the buffer
+// freed by the previous step, and score block b against the g staged rows
+// into the wave's LDS slot. Rows whose visible length ends before the block are
+// skipped (their tail is filled separately). Lane i of vis_lane holds the
+// visible length of row i.
+template <bool FP4, int BKV, bool PF>
+__device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int b,
+                                          const KeyRegs<FP4, BKV> &kc, bool okc, int bp, KeyRegs<FP4, BKV> &kp,
+                                          bool &okp, const uint8_t *s_q, const float *s_w, int vis_lane,
+                                          WaveSlot<BKV> &sl, int &mask, int &col0p) {
     touch<FP4, BKV>(kc);
-    store_pending<BKV>(a, r0, p);
-    if (bn < blk_hi) okn = fetch_block<FP4, BKV>(a, bt_row, bn, kn);
-    score_block<FP4, BKV>(a, g, bc, kc, okc, s_q, s_w, s_vis, p);
+    flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
+    if constexpr (PF) okp = fetch_block<FP4, BKV>(a, bt_row, bp, kp);
+    const int lane = lane_id();
+    const int col0 = b * BKV;
+    const int tok = out_token<BKV>(lane);
+    const int s = col0 + tok;
+    const float scale = FP4 ? 0.5f : 0.5f * __uint_as_float(kc.sc[0]);  // 1/2: see score_row
+    int m = 0;
+    for (int i = 0; i < g; ++i) {
+        const int vis = __builtin_amdgcn_readlane(vis_lane, i);
+        if (col0 >= vis) continue;
+        float v = score_row<FP4, BKV>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
+        if (!okc) v = __builtin_nanf("");
+        if (s >= vis) v = -__builtin_inff();
+        if (out_lane<BKV>(lane)) lds_st<float>(&sl.v[i][tok], v);
+        m |= 1 << i;
+    }
+    mask = m;
+    col0p = col0;
 }
 
 template <bool FP4, int BKV>
-__global__ __launch_bounds__(kThreads, 2) void paged_logits_kernel(PagedArgs a) {
+__global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_vis[kGMax];
+    __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kCW];
 
     const int tid = threadIdx.x;
     const int wave = uni(tid / kWave);
     const int W = gridDim.x;
     const int c = blockIdx.x;
     const int n = a.rows.num_rows;
+    WaveSlot<BKV> &sl = s_slot[wave];
 
     int r0 = min(max(sload(a.sched, 2 * c), 0), n);
     int blk_lo = max(sload(a.sched, 2 * c + 1), 0);
@@ -122,25 +114,56 @@ __global__ __launch_bounds__(kThreads, 2) void paged_logits_kernel(PagedArgs a) 
             stage_rows(a.q, a.w, r0, g, s_q, s_w);
             if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
             barrier_lds();
+            const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
             const int64_t bt_row = r0 / a.rows.next_n;
-            int b = blk_lo + wave;
-            if (b < blk_hi) {
-                KeyRegs<FP4, BKV> k0, k1;
-                bool ok0 = fetch_block<FP4, BKV>(a, bt_row, b, k0), ok1 = false;
-                Pending p;
-                p.mask = 0;
-                p.col0 = 0;
-                for (;;) {
-                    const int b1 = b + kWaves;
-                    block_step<FP4, BKV>(a, r0, g, bt_row, blk_hi, k0, ok0, b, k1, ok1, b1, s_q, s_w, s_vis, p);
-                    if (b1 >= blk_hi) break;
-                    const int b2 = b1 + kWaves;
-                    block_step<FP4, BKV>(a, r0, g, bt_row, blk_hi, k1, ok1, b1, k0, ok0, b2, s_q, s_w, s_vis, p);
-                    if (b2 >= blk_hi) break;
-                    b = b2;
+            const int b0 = blk_lo + wave;
+            const int nmy = b0 < blk_hi ? (blk_hi - b0 + kCW - 1) / kCW : 0;  // this wave's blocks
+            KeyRegs<FP4, BKV> k0, k1, k2;
+            bool ok0 = false, ok1 = false, ok2 = false;
+            int mask = 0, col0p = 0;
+            // step(kc, j, kp): score this wave's j-th block from kc and, when
+            // kp is given, request block j + 2 into it
+            auto step = [&](const KeyRegs<FP4, BKV> &kc, bool okc, int j, KeyRegs<FP4, BKV> &kp, bool &okp, auto pf) {
+                wave_step<FP4, BKV, decltype(pf)::value>(a, r0, g, bt_row, b0 + kCW * j, kc, okc, b0 + kCW * (j + 2),
+                                                         kp, okp, s_q, s_w, vis_lane, sl, mask, col0p);
+            };
+            constexpr std::true_type PF{};
+            constexpr std::false_type NOPF{};
+            if (nmy >= 3) {
+                // Every step of the main loop requests a block, so the wait at
+                // the top of a step always has the same loads behind it.
+                ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
+                ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + kCW, k1);
+                for (int j = 0;;) {
+                    if (j + 2 >= nmy) {  // blocks j (k0) and j + 1 (k1) remain
+                        step(k0, ok0, j, k2, ok2, NOPF);
+                        step(k1, ok1, j + 1, k2, ok2, NOPF);
+                        break;
+                    }
+                    step(k0, ok0, j, k2, ok2, PF);
+                    ++j;
+                    if (j + 2 >= nmy) {  // k1, k2 remain
+                        step(k1, ok1, j, k0, ok0, NOPF);
+                        step(k2, ok2, j + 1, k0, ok0, NOPF);
+                        break;
+                    }
+                    step(k1, ok1, j, k0, ok0, PF);
+                    ++j;
+                    if (j + 2 >= nmy) {  // k2, k0 remain
+                        step(k2, ok2, j, k1, ok1, NOPF);
+                        step(k0, ok0, j + 1, k1, ok1, NOPF);
+                        break;
+                    }
+                    step(k2, ok2, j, k1, ok1, PF);
+                    ++j;
                 }
-                store_pending<BKV>(a, r0, p);
+            } else if (nmy > 0) {
+                ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
+                if (nmy > 1) ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + kCW, k1);
+                step(k0, ok0, 0, k2, ok2, NOPF);
+                if (nmy > 1) step(k1, ok1, 1, k2, ok2, NOPF);
             }
+            if (nmy > 0) flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
         }
         r0 += g;
         blk_lo = 0;
@@ -156,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_logits_kernel(PagedArgs a) 
 
 template <bool FP4, int BKV>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV>), dim3(W), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV>), dim3(W), dim3(kLThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 

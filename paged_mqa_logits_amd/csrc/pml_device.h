@@ -11,16 +11,18 @@ namespace pml {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
-constexpr int kThreads = 256;   // 4 waves: each owns 16 of the 64 heads
-constexpr int kWaves = kThreads / kWave;
 constexpr int kGMax = 8;        // rows of one piece scored against a shared key block
 constexpr int kCostBase = 4;    // schedule weight of a block: kCostBase + rows
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Wave-uniform copy of x (lane 0's value, in a scalar register).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Workgroup barrier that only orders LDS: waits for this wave's LDS traffic,
 // then s_barrier. Unlike __syncthreads it does not drain outstanding global
@@ -73,6 +75,11 @@ __device__ __forceinline__ void lds_write_i32(uint32_t addr, int v) {
 template <typename T>
 __device__ __forceinline__ T lds_ld(const void *p) {
     return *(const __attribute__((address_space(3))) T *)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_st(void *p, T v) {
+    *(__attribute__((address_space(3))) T *)(__attribute__((address_space(3))) void *)p = v;
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

@@ -7,10 +7,13 @@
 // Grid (x = chunk of kChunk key blocks, y = piece of kGMax consecutive rows).
 // A workgroup stages q and w of its rows in LDS; its 4 waves take the chunk's
 // blocks that intersect the union of the rows' key ranges in turn, loading 64
-// keys at a time into VGPRs (double-buffered) and scoring them with the core
-// of logits_core.h. The chunk's other columns of its rows are filled with
-// -inf, and nothing is read for them, so a causal prefill does about half the
-// work of the dense product.
+// keys at a time into VGPRs (three buffers deep) and scoring them with the
+// core of logits_core.h, as in the paged kernel. The chunk's other columns of
+// its rows are
+// filled with -inf and nothing is read for them, so a causal prefill does
+// about half the work of the dense product.
+#include <type_traits>
+
 #include "logits_core.h"
 #include "rows.h"
 
@@ -31,51 +34,38 @@ struct RaggedArgs {
     int64_t out_ld;
 };
 
-__device__ __forceinline__ void ragged_block(int g, int b, const KeyRegs<false, 64> &k, const uint8_t *s_q,
-                                             const float *s_w, const int *s_lo, const int *s_hi, Pending &p) {
-    const int s = b * 64 + lane_id();
-    const float scale = __uint_as_float(k.sc[0]);
-    p.mask = 0;
-    p.col0 = b * 64;
-#pragma unroll
-    for (int i = 0; i < kGMax; ++i) {
-        if (i < g) {
-            const int lo = uni(lds_ld<int>(&s_lo[i]));
-            const int hi = uni(lds_ld<int>(&s_hi[i]));
-            float v = score_row<false, 64>(k, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
-            if (s < lo || s >= hi) v = -__builtin_inff();
-            p.v[i] = v;
-            p.mask |= 1 << i;
-        }
-    }
-}
-
-__device__ __forceinline__ void ragged_store(const RaggedArgs &a, int row0, const Pending &p) {
-    const int s = p.col0 + lane_id();
-#pragma unroll
-    for (int i = 0; i < kGMax; ++i)
-        if ((p.mask >> i) & 1)
-            if (s < a.N) a.out[(int64_t)(row0 + i) * a.out_ld + s] = p.v[i];
-}
-
-// One step of a wave's block loop: wait for the current block, store the
-// previous block's logits, request the next block, score the current one.
-__device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g, int u_hi,
-                                            const KeyRegs<false, 64> &kc, int bc, KeyRegs<false, 64> &kn, int bn,
-                                            const uint8_t *s_q, const float *s_w, const int *s_lo, const int *s_hi,
-                                            Pending &p) {
+// One step of a wave's block loop (see wave_step of the paged kernel); every
+// row of the piece is stored, -inf outside its [lo, hi) (lane i of lo_lane /
+// hi_lane holds the bounds of row i).
+template <bool PF>
+__device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g, int b,
+                                            const KeyRegs<false, 64> &kc, int bp, KeyRegs<false, 64> &kp,
+                                            const uint8_t *s_q, const float *s_w, int lo_lane, int hi_lane,
+                                            WaveSlot<64> &sl, int &mask, int &col0p) {
     touch<false, 64>(kc);
-    ragged_store(a, row0, p);
-    if (bn < u_hi) load_contig(a.k, a.k_scale, a.N, bn * 64, kn);
-    ragged_block(g, bc, kc, s_q, s_w, s_lo, s_hi, p);
+    flush_slot<64>(sl, mask, row0, col0p, a.N, a.out, a.out_ld);
+    if constexpr (PF) load_contig(a.k, a.k_scale, a.N, bp * 64, kp);
+    const int lane = lane_id();
+    const int s = b * 64 + lane;
+    const float scale = 0.5f * __uint_as_float(kc.sc[0]);  // 1/2: see score_row
+    for (int i = 0; i < g; ++i) {
+        const int lo = __builtin_amdgcn_readlane(lo_lane, i);
+        const int hi = __builtin_amdgcn_readlane(hi_lane, i);
+        float v = score_row<false, 64>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
+        if (s < lo || s >= hi) v = -__builtin_inff();
+        lds_st<float>(&sl.v[i][lane], v);
+    }
+    mask = (1 << g) - 1;
+    col0p = b * 64;
 }
 
-__global__ __launch_bounds__(kThreads, 2) void ragged_logits_kernel(RaggedArgs a) {
+__global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs a) {
     constexpr int BKV = 64;
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_lo[kGMax];
     __shared__ int s_hi[kGMax];
+    __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kCW];
 
     const int tid = threadIdx.x;
     const int wave = uni(tid / kWave);
@@ -124,23 +114,54 @@ __global__ __launch_bounds__(kThreads, 2) void ragged_logits_kernel(RaggedArgs a
     }
     barrier_lds();
 
-    int b = u_lo + wave;
-    if (b >= u_hi) return;
-    KeyRegs<false, BKV> k0, k1;
-    load_contig(a.k, a.k_scale, N, b * BKV, k0);
-    Pending p;
-    p.mask = 0;
-    p.col0 = 0;
-    for (;;) {
-        const int b1 = b + kWaves;
-        ragged_step(a, row0, g, u_hi, k0, b, k1, b1, s_q, s_w, s_lo, s_hi, p);
-        if (b1 >= u_hi) break;
-        const int b2 = b1 + kWaves;
-        ragged_step(a, row0, g, u_hi, k1, b1, k0, b2, s_q, s_w, s_lo, s_hi, p);
-        if (b2 >= u_hi) break;
-        b = b2;
+    const int lo_lane = lds_ld<int>(&s_lo[lane_id() % kGMax]);  // lane i: bounds of row i
+    const int hi_lane = lds_ld<int>(&s_hi[lane_id() % kGMax]);
+    const int b0 = u_lo + wave;
+    if (b0 >= u_hi) return;
+    const int nmy = (u_hi - b0 + kCW - 1) / kCW;  // this wave's blocks
+    WaveSlot<BKV> &sl = s_slot[wave];
+    KeyRegs<false, BKV> k0, k1, k2;
+    int mask = 0, col0p = 0;
+    auto step = [&](const KeyRegs<false, BKV> &kc, int j, KeyRegs<false, BKV> &kp, auto pf) {
+        ragged_step<decltype(pf)::value>(a, row0, g, b0 + kCW * j, kc, b0 + kCW * (j + 2), kp, s_q, s_w, lo_lane, hi_lane,
+                                         sl, mask, col0p);
+    };
+    constexpr std::true_type PF{};
+    constexpr std::false_type NOPF{};
+    if (nmy >= 3) {
+        // every step of the main loop requests a block (see the paged kernel)
+        load_contig(a.k, a.k_scale, N, b0 * BKV, k0);
+        load_contig(a.k, a.k_scale, N, (b0 + kCW) * BKV, k1);
+        for (int j = 0;;) {
+            if (j + 2 >= nmy) {
+                step(k0, j, k2, NOPF);
+                step(k1, j + 1, k2, NOPF);
+                break;
+            }
+            step(k0, j, k2, PF);
+            ++j;
+            if (j + 2 >= nmy) {
+                step(k1, j, k0, NOPF);
+                step(k2, j + 1, k0, NOPF);
+                break;
+            }
+            step(k1, j, k0, PF);
+            ++j;
+            if (j + 2 >= nmy) {
+                step(k2, j, k1, NOPF);
+                step(k0, j + 1, k1, NOPF);
+                break;
+            }
+            step(k2, j, k1, PF);
+            ++j;
+        }
+    } else {
+        load_contig(a.k, a.k_scale, N, b0 * BKV, k0);
+        if (nmy > 1) load_contig(a.k, a.k_scale, N, (b0 + kCW) * BKV, k1);
+        step(k0, 0, k2, NOPF);
+        if (nmy > 1) step(k1, 1, k2, NOPF);
     }
-    ragged_store(a, row0, p);
+    flush_slot<BKV>(sl, mask, row0, col0p, N, a.out, a.out_ld);
 }
 
 }  // namespace pml
@@ -163,6 +184,6 @@ extern "C" int mqa_logits(const void *q, int M, int num_heads, int head_dim, con
     const int nb = (N + 63) / 64;
     const dim3 grid((nb + pml::kChunk - 1) / pml::kChunk, (M + pml::kGMax - 1) / pml::kGMax);
     if (grid.y > 65535) return PML_ERR_SHAPE;
-    hipLaunchKernelGGL(pml::ragged_logits_kernel, grid, dim3(pml::kThreads), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(pml::ragged_logits_kernel, grid, dim3(pml::kLThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }

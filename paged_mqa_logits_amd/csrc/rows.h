@@ -23,7 +23,6 @@ __device__ __forceinline__ T sload(const T *base, int64_t idx) {
     return ((cT *)base)[idx];
 }
 
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 struct RowView {
     const int32_t *lens;
