@@ -38,6 +38,23 @@ import pml_synth as syn  # noqa: E402
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 BYTES_PER_TOKEN = {syn.KV_FP8: 132, syn.KV_FP4: 68}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_logits_fp8_varlen120k_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fp8 decode-logits kernel on this workload, from the
+    committed FETCH_SIZE + WRITE_SIZE summary; None when the kernel sources have changed
+    since the counters were taken (or there is no summary)."""
+    from paged_mqa_logits_amd import profsum
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    for ln in text.splitlines():
+        f = ln.strip("` ").split()
+        if len(f) == 4 and f[0] == "traffic_bytes_per_launch" and f[2] == "digest":
+            return int(f[1]) if f[3] == profsum.source_digest() else None
+    return None
 
 
 def parse():
@@ -48,6 +65,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=3, help="key-cache copies rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after timing, run one device-to-device copy of BYTES bytes (a known-size "
+                         "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (one JSON line each on stderr)")
     return ap.parse_args()
@@ -215,10 +235,19 @@ def main():
                          "topk": round(s["ms_topk"], 4)},
         "logits_mfma_frac": round(s["logits_mfma_frac"], 4),
         "roofline": {"bound": "hbm", "achieved": round(s["logits_hbm_GBs"], 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(s["logits_hbm_frac"], 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(s["logits_hbm_frac"], 4), "traffic": measured_traffic(),
                      "kernel": "paged_logits_kernel<fp8, block_kv 64>",
                      "bytes_per_launch": b.req_tokens * BYTES_PER_TOKEN[case.kv_format]},
     }
+    if args.copy_calibration > 0:
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.copy_calibration} bytes done", file=sys.stderr, flush=True)
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

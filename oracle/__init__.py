@@ -9,9 +9,11 @@ top-k; ``brute.py`` is a second, numpy-only formulation for tiny inputs;
 ``schedule.py`` is the specification of the work split that the metadata
 call produces.
 
-Parity unpinned: the pages print no worked example and no numeric value for
-this path, so no stored value comes from them; the pins are the format
-definitions, closed forms, invariants and brute force listed in the tests.
+The pages print no worked example and no numeric value for this path, so no
+stored value comes from them. Every function here is pinned by something other
+than itself: the fp8 / e2m1 / e8m0 format definitions, hand-worked fixtures
+(tests/golden), closed forms, invariants and the independent numpy brute force
+(tests/test_oracle.py, tests/test_schedule_spec.py).
 """
 from __future__ import annotations
 

@@ -1,0 +1,101 @@
+"""Summaries of rocprofv3 CSV output for the logits kernels.
+
+Reads what ``rocprofv3 --kernel-trace --stats --output-format csv`` and
+``rocprofv3 --pmc <counter> --output-format csv`` write and turns it into the
+short text summaries kept with the library: per-kernel average durations, and
+HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
+same counter reads for a device-to-device copy of known size
+(``bench.py --copy-calibration`` issues one).
+
+  python -m paged_mqa_logits_amd.profsum stats  <kernel_stats.csv>
+  python -m paged_mqa_logits_amd.profsum pmc    <counter_collection.csv> <counter> <copy_bytes>
+  python -m paged_mqa_logits_amd.profsum digest
+
+``digest`` prints a hash of the decode-logits kernel sources; a traffic
+figure is only valid for the sources it was measured on.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import sys
+from collections import defaultdict
+from pathlib import Path
+
+CSRC = Path(__file__).resolve().parent / "csrc"
+LOGITS_SOURCES = ("pml_device.h", "rows.h", "logits_core.h", "paged_logits.hip")
+COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
+
+
+def source_digest() -> str:
+    """sha256 (first 16 hex digits) over the decode-logits kernel sources."""
+    h = hashlib.sha256()
+    for name in LOGITS_SOURCES:
+        h.update(name.encode())
+        h.update((CSRC / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def kernel_stats(path: str) -> list[dict]:
+    """Rows of a *_kernel_stats.csv: name, calls, average / min / max in us, share of time."""
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            out.append({"name": r["Name"], "calls": int(r["Calls"]),
+                        "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                        "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return out
+
+
+def counter_means(path: str, counter: str) -> dict[str, tuple[int, float]]:
+    """Kernel name -> (dispatches, mean counter value per dispatch) from a counter_collection.csv."""
+    per = defaultdict(dict)  # name -> dispatch -> summed value
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = per[r["Kernel_Name"]]
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {k: (len(v), sum(v.values()) / len(v)) for k, v in per.items()}
+
+
+def calibrated(path: str, counter: str, copy_bytes: int) -> tuple[float, dict[str, tuple[int, float, float]]]:
+    """(scale, kernel -> (dispatches, KiB per dispatch, calibrated bytes per dispatch)).
+
+    scale = copy_bytes / (KiB the copy kernel's dispatches read for `counter` x 1024),
+    taken from the largest copy dispatch (the calibration copy)."""
+    m = counter_means(path, counter)
+    copies = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and COPY_KERNEL in r["Kernel_Name"]:
+                copies.append(float(r["Counter_Value"]))
+    if not copies:
+        raise SystemExit(f"no {COPY_KERNEL} dispatch with {counter} in {path}")
+    scale = copy_bytes / (max(copies) * 1024.0)
+    return scale, {k: (n, v, v * 1024.0 * scale) for k, (n, v) in m.items()}
+
+
+def _main(argv: list[str]) -> None:
+    if not argv or argv[0] not in ("stats", "pmc", "digest"):
+        print(__doc__)
+        raise SystemExit(2)
+    if argv[0] == "digest":
+        print(source_digest())
+    elif argv[0] == "stats":
+        print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'time%':>7s}")
+        for r in kernel_stats(argv[1]):
+            print(f"{r['name'][:90]:90s} {r['calls']:6d} {r['avg_us']:10.2f} {r['min_us']:10.2f} "
+                  f"{r['max_us']:10.2f} {r['pct']:7.2f}")
+    else:
+        path, counter, nbytes = argv[1], argv[2], int(argv[3])
+        scale, rows = calibrated(path, counter, nbytes)
+        print(f"{counter}: copy calibration {nbytes} bytes -> scale {scale:.4f}")
+        print(f"{'kernel':90s} {'n':>4s} {'KiB/dispatch':>14s} {'bytes/dispatch':>16s}")
+        for k, (n, kib, b) in sorted(rows.items(), key=lambda kv: -kv[1][2]):
+            print(f"{k[:90]:90s} {n:4d} {kib:14.1f} {b:16.0f}")
+    print(f"logits sources digest {source_digest()}")
+
+
+if __name__ == "__main__":
+    _main(sys.argv[1:])
