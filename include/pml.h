@@ -97,7 +97,7 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
  *                    contiguous share of (row-piece, key-block) units starts;
  *                    entry num_CUs is (num_rows, 0). A row-piece is at most 8
  *                    consecutive rows of one group. Units are weighted by
- *                    (4 + rows in the piece) so shares cost about the same.
+ *                    (1 + rows in the piece) so shares cost about the same.
  * The schedule is valid only for the same context_lens, indices, next_n,
  * block_kv and num_CUs.
  */

@@ -24,7 +24,7 @@ from __future__ import annotations
 import numpy as np
 
 G_MAX = 8
-COST_BASE = 4
+COST_BASE = 1
 
 
 def visible_lengths(context_lens: np.ndarray, num_rows: int, next_n: int, lens_2d: bool) -> np.ndarray:

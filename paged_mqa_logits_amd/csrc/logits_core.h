@@ -104,19 +104,36 @@ __device__ __forceinline__ void load_contig(const uint8_t *k, const float *k_sca
 // read land in distinct banks.
 __device__ __forceinline__ int q_lds_off(int h, int c) { return h * PML_HEAD_DIM + ((c ^ (h & 7)) << 4); }
 
-// Stage q and w of rows r0 .. r0 + g - 1 into LDS (the whole workgroup).
+// Stage q and w of rows r0 .. r0 + g - 1 into LDS (the whole workgroup). All
+// loads are issued before the first LDS store, so staging costs one memory
+// latency rather than one per round of the thread loop.
 __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int64_t r0, int g, uint8_t *s_q,
                                            float *s_w) {
+    constexpr int kChunks = kQBytes / 16;                     // 16-B chunks per row
+    constexpr int kPer = kGMax * kChunks / kLThreads;         // chunks per thread, at most
+    constexpr int kWPer = (kGMax * PML_HEADS + kLThreads - 1) / kLThreads;
     const int tid = threadIdx.x;
-    const int nchunk = g * (kQBytes / 16);
-    for (int i = tid; i < nchunk; i += kLThreads) {
-        const int row = i / (kQBytes / 16);
-        const int rem = i % (kQBytes / 16);
-        const int h = rem / 8, c = rem % 8;
-        const v4i x = *(const v4i *)(q + (r0 + row) * kQBytes + rem * 16);
-        *(v4i *)(s_q + row * kQBytes + q_lds_off(h, c)) = x;
+    const int nchunk = g * kChunks;
+    const uint8_t *src = q + r0 * kQBytes;
+    v4i x[kPer];
+    float wv[kWPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (tid + k * kLThreads < nchunk) x[k] = *(const v4i *)(src + (tid + k * kLThreads) * 16);
+#pragma unroll
+    for (int k = 0; k < kWPer; ++k)
+        if (tid + k * kLThreads < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * kLThreads];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * kLThreads;
+        if (i < nchunk) {
+            const int row = i / kChunks, rem = i % kChunks;
+            *(v4i *)(s_q + row * kQBytes + q_lds_off(rem / 8, rem % 8)) = x[k];
+        }
     }
-    for (int i = tid; i < g * PML_HEADS; i += kLThreads) s_w[i] = w[r0 * PML_HEADS + i];
+#pragma unroll
+    for (int k = 0; k < kWPer; ++k)
+        if (tid + k * kLThreads < g * PML_HEADS) s_w[tid + k * kLThreads] = wv[k];
 }
 
 // A operand (q of heads 16 ht + lane % 16) of one staged row, in the
@@ -203,14 +220,17 @@ __device__ __forceinline__ void touch(const KeyRegs<FP4, BKV> &k) {
     for (int j = 0; j < C::NS; ++j) asm volatile("" ::"v"(k.sc[j]));
 }
 
-// A 4-byte global store issued as inline asm. The compiler's wait tracking
-// then counts only key-block loads in the vector-memory counter and waits for
-// a block exactly, leaving the blocks behind it in flight; in hardware the
-// store still counts, which can only make those waits stricter (loads
-// complete in order among themselves). A single-dword store reads its data
-// register when it issues, so no hazard guard is needed around it.
+// Global stores issued as inline asm. The compiler's wait tracking then
+// counts only key-block loads in the vector-memory counter and waits for a
+// block exactly, leaving the blocks behind it in flight; in hardware the
+// stores still count, which can only make those waits stricter (loads
+// complete in order among themselves). A store reads its data registers when
+// it issues, so no hazard guard is needed around it.
 __device__ __forceinline__ void store_f32_async(float *p, float v) {
     asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_v4f_async(float *p, v4f v) {
+    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
 
 // One block's logits for up to kGMax rows, parked in the wave's own LDS slot
@@ -221,17 +241,32 @@ struct WaveSlot {
 };
 
 // Store rows (bit i of mask) of the parked block at columns [col0, col0 + BKV),
-// never at or past ncols.
+// never at or past ncols. Each lane moves 4 consecutive columns of one row, so
+// one 16-byte store instruction covers 64 * 4 / BKV rows; a 4-column group
+// that crosses ncols is stored column by column.
 template <int BKV>
 __device__ __forceinline__ void flush_slot(const WaveSlot<BKV> &sl, int mask, int64_t row0, int col0, int ncols,
                                            float *out, int64_t out_ld) {
+    constexpr int kLanesPerRow = BKV / 4;
+    constexpr int kRowsPer = kWave / kLanesPerRow;  // rows per instruction: 4 (BKV 64) or 8 (BKV 32)
     const int lane = lane_id();
-    const int s = col0 + lane;
-    const bool st = lane < BKV && s < ncols;
-    for (int m = mask; m; m &= m - 1) {
-        const int i = __builtin_ctz(m);
-        const float v = lds_ld<float>(&sl.v[i][lane % BKV]);
-        if (st) store_f32_async(out + (row0 + i) * out_ld + s, v);
+    const int c4 = 4 * (lane % kLanesPerRow);
+    const int s = col0 + c4;
+#pragma unroll
+    for (int m = 0; m < kGMax; m += kRowsPer) {
+        if ((mask >> m) == 0) break;
+        const int i = m + lane / kLanesPerRow;
+        if (i < kGMax && ((mask >> i) & 1)) {
+            const v4f v = lds_ld<v4f>(&sl.v[i][c4]);
+            float *p = out + (row0 + i) * out_ld + s;
+            if (s + 4 <= ncols) {
+                store_v4f_async(p, v);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (s + j < ncols) store_f32_async(p + j, v[j]);
+            }
+        }
     }
 }
 

@@ -7,8 +7,8 @@
 //    rows of one request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a
 //    request are processed together), so each key page is read from HBM once
 //    for all of them.
-//  * The 4 waves take the blocks of the current piece in turn (wave w scores
-//    blocks blk0 + w, blk0 + w + 4, ...). Each loads its pages from HBM
+//  * The 4 waves split the current piece's blocks into contiguous quarters.
+//    Each loads its pages from HBM
 //    straight into VGPRs, three buffers deep, and scores them against every
 //    row of the piece, whose q and w sit in LDS. Waves meet at a barrier only
 //    when the piece changes.
@@ -116,15 +116,18 @@ __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a)
             barrier_lds();
             const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
             const int64_t bt_row = r0 / a.rows.next_n;
-            const int b0 = blk_lo + wave;
-            const int nmy = b0 < blk_hi ? (blk_hi - b0 + kCW - 1) / kCW : 0;  // this wave's blocks
+            // this wave's blocks: a contiguous quarter of [blk_lo, blk_hi), so
+            // its block-table entries share scalar-cache lines
+            const int per = (blk_hi - blk_lo) / kCW, rem = (blk_hi - blk_lo) % kCW;
+            const int b0 = blk_lo + wave * per + min(wave, rem);
+            const int nmy = per + (wave < rem ? 1 : 0);
             KeyRegs<FP4, BKV> k0, k1, k2;
             bool ok0 = false, ok1 = false, ok2 = false;
             int mask = 0, col0p = 0;
             // step(kc, j, kp): score this wave's j-th block from kc and, when
             // kp is given, request block j + 2 into it
             auto step = [&](const KeyRegs<FP4, BKV> &kc, bool okc, int j, KeyRegs<FP4, BKV> &kp, bool &okp, auto pf) {
-                wave_step<FP4, BKV, decltype(pf)::value>(a, r0, g, bt_row, b0 + kCW * j, kc, okc, b0 + kCW * (j + 2),
+                wave_step<FP4, BKV, decltype(pf)::value>(a, r0, g, bt_row, b0 + j, kc, okc, b0 + j + 2,
                                                          kp, okp, s_q, s_w, vis_lane, sl, mask, col0p);
             };
             constexpr std::true_type PF{};
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a)
                 // Every step of the main loop requests a block, so the wait at
                 // the top of a step always has the same loads behind it.
                 ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
-                ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + kCW, k1);
+                ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + 1, k1);
                 for (int j = 0;;) {
                     if (j + 2 >= nmy) {  // blocks j (k0) and j + 1 (k1) remain
                         step(k0, ok0, j, k2, ok2, NOPF);
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a)
                 }
             } else if (nmy > 0) {
                 ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
-                if (nmy > 1) ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + kCW, k1);
+                if (nmy > 1) ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + 1, k1);
                 step(k0, ok0, 0, k2, ok2, NOPF);
                 if (nmy > 1) step(k1, ok1, 1, k2, ok2, NOPF);
             }

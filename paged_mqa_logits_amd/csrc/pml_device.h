@@ -17,7 +17,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kGMax = 8;        // rows of one piece scored against a shared key block
-constexpr int kCostBase = 4;    // schedule weight of a block: kCostBase + rows
+constexpr int kCostBase = 1;    // schedule weight of a block: kCostBase + rows
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -60,15 +60,29 @@ struct RowView {
 
 // Rows and key-block count of the piece starting at row r0 (r0 < num_rows,
 // wave-uniform). The piece extent is the largest visible length of its rows.
+// The lengths and ids of all kGMax candidate rows are requested up front (rows
+// past the end re-read row r0), so their scalar loads overlap.
 template <int BKV>
 __device__ __forceinline__ void piece_at(const RowView &v, int r0, int &g, int &nblk) {
-    int gg = 1;
-    int e = v.visible_s(r0);
+    int vis[kGMax];
+    bool same[kGMax];
+    const int id0 = v.indices ? sload(v.indices, r0) : 0;
+#pragma unroll
+    for (int i = 0; i < kGMax; ++i) {
+        const int r = r0 + i < v.num_rows ? r0 + i : r0;
+        vis[i] = v.visible_s(r);
+        same[i] = r0 + i < v.num_rows &&
+                  (v.indices ? sload(v.indices, r) == id0 : r / v.next_n == r0 / v.next_n);
+    }
+    int gg = 1, e = vis[0];
+    bool go = true;
+#pragma unroll
     for (int i = 1; i < kGMax; ++i) {
-        const int r = r0 + i;
-        if (r >= v.num_rows || !v.same_group_s(r, r0)) break;
-        e = max(e, v.visible_s(r));
-        gg = i + 1;
+        go = go && same[i];
+        if (go) {
+            e = max(e, vis[i]);
+            gg = i + 1;
+        }
     }
     g = uni(gg);
     nblk = uni((e + BKV - 1) / BKV);
