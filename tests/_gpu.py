@@ -65,6 +65,9 @@ def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Te
     tol = REL * np.abs(ref) + abs_tol(weights_rows)[:, None]
     err = np.abs(gpu.astype(np.float64) - ref)
     bad = fin & ~(err <= tol)
+    if fin.any():
+        ratio = float(np.max(np.where(fin, err / tol, 0.0)))
+        print(f"[gpu-check] {what or 'logits'}: max err/tol {ratio:.3g} over {int(fin.sum())} cells", flush=True)
     if bad.any():
         i = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} cells out of tolerance, e.g. {[(tuple(x), gpu[tuple(x)], ref[tuple(x)]) for x in i]}")
