@@ -8,10 +8,20 @@
 // lowest, -0 == +0) followed by an ordered compaction, so positions come out
 // ascending without a sort:
 //  * A row that fits the LDS candidate list is read once into it.
-//  * A wider row takes three streaming passes: a histogram of the top 11 key
-//    bits fixes the bucket b holding the k-th key; every wave counts, then
-//    appends in position order, the elements whose top digit is >= b (wave
-//    ballots give the order inside a wave, per-wave counts across waves).
+//  * A row of 64K columns or more first takes a sampled pass: a histogram of the top 11 key
+//    bits over one 1-KB chunk in 8 picks a bucket b with a margin (about
+//    1.5 k keys at or above it); then one streaming pass appends, in position
+//    order, every element whose top digit is >= b into its wave's region of
+//    the list (wave ballots order a wave's elements; each wave's span of the
+//    row is contiguous), and the regions are packed together. Any key outside
+//    the list is then below every key in it, so if the list holds at least k
+//    keys the top k are among them and the selection finishes in the list.
+//    One CU streams a row at only ~25 GB/s, which is why the row is read
+//    about 1.1 times rather than three.
+//  * Narrower rows, and rows where the sample misjudges (fewer than k
+//    candidates, or a region overflows), take the exact streaming passes: a
+//    full histogram fixes b, then every wave counts, then appends, the
+//    candidates.
 //  * The remaining 11 + 10 key bits are selected inside the list, then one
 //    block scan over it places every selected element.
 //  * If the candidates overflow the list (heavy ties), the selection finishes
@@ -34,7 +44,11 @@ template <int NT>
 struct TopkCfg {
     static constexpr int NW = NT / kWave;
     static constexpr int CAP = NT == 1024 ? 12288 : 8192;  // candidate list entries
+    static constexpr int RCAP = CAP / NW;                   // one wave's region of the list
 };
+constexpr int kSampleDiv = 8;       // the sampled pass reads one 1-KB chunk in 8
+constexpr int kSampledMin = 65536;  // rows at least this wide take the sampled path (narrower
+                                    // rows stream fast enough that its extra list pass does not pay)
 
 // Inclusive scan of one uint32 per thread over the workgroup; *total gets the sum.
 template <int NT>
@@ -202,7 +216,101 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         m = n;
         __syncthreads();
     } else {
-        // pass 1: histogram of the top 11 bits
+        constexpr int RCAP = Cfg::RCAP;
+        bool exact = true;
+        if (n >= kSampledMin) {
+        // sampled pass: top-digit histogram of one 64-group chunk (1 KB, one
+        // coalesced load per wave) in every kSampleDiv chunks of the wave's span
+        // (chunk 8i + i % 8, so the sample is not periodic in the row)
+        for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
+        if (tid == 0) s_pick[0] = 0;  // bucket 0 (the whole row) if the sample runs short
+        __syncthreads();
+        {
+            const int nchunk = (wq1 - wq0 + kWave - 1) / kWave;
+            const int nsamp = (nchunk + kSampleDiv - 1) / kSampleDiv;
+            for (int i0 = 0; i0 < nsamp; i0 += kUnroll) {
+                v4f x[kUnroll];
+                int gq[kUnroll];
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+                    const int i = i0 + j;
+                    gq[j] = wq0 + kWave * (i * kSampleDiv + i % kSampleDiv) + lane;
+                    x[j] = (i < nsamp && gq[j] < wq1) ? *(const v4f *)(rowbase + 4 * (int64_t)gq[j])
+                                                      : v4f{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int j = 0; j < kUnroll; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int p = 4 * gq[j] + e;
+                        if (i0 + j < nsamp && gq[j] < wq1 && p >= lo && p < hi)
+                            atomicAdd(&s_hist[order_key(x[j][e]) >> 21], 1u);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        // the bucket of the t-th largest sampled key, t = 1.5 k / kSampleDiv + 16
+        pick_bin<NT>(s_hist, kBins, (uint32_t)(3 * k) / (2 * kSampleDiv) + 16, s_wave, s_pick);
+        const uint32_t sprefix = s_pick[0] << 21;
+        // one pass: ordered append into the wave's region [wave * RCAP, +RCAP)
+        uint32_t cnt = 0;
+        wave_walk(rowbase, lo, hi, wq0, wq1, [&](int p0, const uint32_t *key, const bool *ok) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c += (ok[e] && key[e] >= sprefix) ? 1u : 0u;
+            uint32_t pre, tot;
+            wave_prefix4(c, pre, tot);
+            uint32_t at = cnt + pre;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (ok[e] && key[e] >= sprefix) {
+                    if (at < (uint32_t)RCAP) {
+                        s_key[wave * RCAP + at] = key[e];
+                        s_pos[wave * RCAP + at] = p0 + e - lo;
+                    }
+                    ++at;
+                }
+            cnt += tot;
+        });
+        if (lane == 0) s_wcnt[wave] = cnt;
+        __syncthreads();
+        uint32_t base = 0, total = 0, over = 0;
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t c = s_wcnt[w];
+            if (w < wave) base += c;
+            total += c;
+            over |= c > (uint32_t)RCAP;
+        }
+        if (!over && total >= (uint32_t)k) {
+            // pack the regions: every wave lifts its entries, then puts them at base
+            constexpr int kPer = RCAP / kWave;
+            uint32_t kv[kPer];
+            int32_t pv[kPer];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const uint32_t i = lane + u * kWave;
+                if (i < cnt) {
+                    kv[u] = s_key[wave * RCAP + i];
+                    pv[u] = s_pos[wave * RCAP + i];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+                const uint32_t i = lane + u * kWave;
+                if (i < cnt) {
+                    s_key[base + i] = kv[u];
+                    s_pos[base + i] = pv[u];
+                }
+            }
+            m = (int)total;  // all three digits are selected inside the list
+        }
+        __syncthreads();
+        exact = over || total < (uint32_t)k;
+        }  // sampled path
+        if (exact) {
+        // exact passes. pass 1: histogram of the top 11 bits
         for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         __syncthreads();
         wave_walk(rowbase, lo, hi, wq0, wq1, [&](int, const uint32_t *key, const bool *ok) {
@@ -257,6 +365,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             in_list = false;
         }
         __syncthreads();
+        }  // exact passes
     }
 
     // remaining radix digits (11, 11, 10 bits from the top)

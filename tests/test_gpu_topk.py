@@ -79,8 +79,10 @@ def test_bounds_and_next_n():
 
 
 def test_wide_rows_streaming_list_and_fallback():
-    """Rows wider than the in-LDS list: the streaming passes, the in-list path
-    of the wide-row kernel, and the fallback when ties overflow the list."""
+    """Rows wider than the in-LDS list: the multi-workgroup segments, the
+    in-list path of the wide-row kernel for the narrower rows of the launch,
+    the streaming passes when one segment's candidates overflow its slot, and
+    the passes over the row when ties overflow the list."""
     rng = np.random.default_rng(830)
     W = 40000
     rows = [rng.standard_normal(W),                     # streaming, few candidates
@@ -89,13 +91,41 @@ def test_wide_rows_streaming_list_and_fallback():
             np.concatenate([rng.standard_normal(9000), np.full(W - 9000, -np.inf)]),
             rng.standard_normal(W) * 1e3,
             np.arange(W, dtype=np.float64)]             # ascending: the top is at the end
+    r = rng.standard_normal(W)
+    r[17000:19100] = 50.0                               # one segment's candidates overflow its slot
+    rows.append(r)
     L = np.stack(rows)
     G.banner("top-k wide rows")
-    for k, ke in ((1, [W] * 6), (2048, [W] * 6), (4096, [W] * 6),
-                  (2048, [10000, 12288, 12289, 40000, 30001, 39999])):
+    for k, ke in ((1, [W] * 7), (2048, [W] * 7), (4096, [W] * 7),
+                  (2048, [10000, 12288, 12289, 40000, 30001, 39999, 40000])):
         _shared_input_check(L, ke, k)
-    ks = np.array([0, 5, 100, 3, 17, 20000])
-    _shared_input_check(L, np.full(6, W), 777, ks=ks)
+    ks = np.array([0, 5, 100, 3, 17, 20000, 1])
+    _shared_input_check(L, np.full(7, W), 777, ks=ks)
+
+
+def test_sampled_path_rows():
+    """Rows of 64K columns or more: a sampled bucket, then one append pass into
+    per-wave regions (fast path); a cluster of large values that overflows one
+    wave's region, and heavy ties, fall back to the exact passes."""
+    rng = np.random.default_rng(840)
+    W = 70000
+    rows = [rng.standard_normal(W),                       # fast path
+            np.arange(W, dtype=np.float64),               # ascending: all candidates at the end
+            np.zeros(W),                                  # ties: region overflow, then list overflow
+            np.round(rng.standard_normal(W) * 3)]         # coarse ties
+    r = rng.standard_normal(W)
+    r[30000:36000:4] = 1000.0                            # 1500 large values inside one wave's span
+    rows.append(r)
+    r = rng.standard_normal(W) * 1e-3
+    r[::5000] = 5.0                                      # 14 isolated large values among tiny ones
+    rows.append(r)
+    L = np.stack(rows)
+    n = L.shape[0]
+    G.banner("top-k sampled path")
+    for k, ke in ((1, [W] * n), (2048, [W] * n), (4096, [W] * n), (100, [65536, 65535, W, 69999, 66000, W])):
+        _shared_input_check(L, ke, k)
+    ks = np.array([0, 3, 4000, 1, 2, 0])
+    _shared_input_check(L, np.full(n, W), 2048, ks=ks)
 
 
 def _acceptance(gpu: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray, k: int, wsum: np.ndarray):
