@@ -8,110 +8,176 @@
 // kCostBase + g; worker c starts at the unit holding cost offset
 // floor(c * T / W) of the total T and entry W is (num_rows, 0).
 //
-// One workgroup of 1024 threads walks the rows in chunks twice: first for the
-// total cost, then for each piece's cost prefix, writing the entries of the
-// workers whose start falls inside that piece.
+// One workgroup of 1024 threads walks the rows in chunks of 1024: every
+// thread loads its row's visible length and group-end flag into LDS (plus a
+// halo of kGMax rows), a max-scan finds each row's group start, the thread of
+// a piece's first row reads the piece's rows and extent from LDS, and a
+// sum-scan of the piece costs gives each piece's offset; the thread of a
+// piece then writes the entries of the workers whose start falls inside it.
+// Up to 1024 rows take one walk; more take two (the total first).
 #include "rows.h"
 
 namespace pml {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedWaves = kSchedThreads / kWave;
+constexpr int kHalo = kGMax;  // rows past a chunk that a piece starting in it may cover
 
+// Block-wide inclusive scan: wave shuffles, then one pass over the wave totals.
 template <typename T, typename Op>
-__device__ T block_inclusive_scan(T x, T *s, Op op) {
-    const int tid = threadIdx.x;
-    s[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-        T y = tid >= off ? s[tid - off] : x;
-        __syncthreads();
-        if (tid >= off) {
-            x = op(x, y);
-            s[tid] = x;
-        }
-        __syncthreads();
+__device__ __forceinline__ T block_scan_incl(T x, T *s_w, Op op, T ident) {
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const T y = __shfl_up(x, off, kWave);
+        if (lane >= off) x = op(x, y);
     }
-    return x;
+    if (lane == kWave - 1) s_w[wave] = x;
+    __syncthreads();
+    T pre = ident;
+    for (int w = 0; w < wave; ++w) pre = op(pre, s_w[w]);
+    __syncthreads();
+    return op(pre, x);
 }
 
-__device__ __forceinline__ int rows_of_piece(const RowView &v, int r0) {
-    int g = 1;
-    while (g < kGMax && r0 + g < v.num_rows && v.same_group(r0 + g, r0)) ++g;
-    return g;
-}
+struct SchedShared {
+    int vis[kSchedThreads + kHalo];    // visible length of rows base + i
+    int last[kSchedThreads + kHalo];   // row base + i ends its group (or is past the end)
+    int wi[kSchedWaves];
+    long long wl[kSchedWaves];
+    int run_carry;
+    long long cost_carry;
+};
 
-// One walk over the rows. With write == false it returns the total cost; with
-// write == true it writes the entries of workers starting inside each piece.
-__device__ long long walk_rows(const RowView &v, int block_kv, int W, int32_t *sched, bool write,
-                               long long total, int *s_int, long long *s_ll, int *s_run_carry,
-                               long long *s_cost_carry) {
+// Cost of the piece starting at row base + tid (0 if no piece starts there)
+// and its row count, for the chunk of rows starting at base.
+__device__ __forceinline__ long long chunk_cost(const RowView &v, int block_kv, int base, SchedShared &sh, int &g) {
     const int tid = threadIdx.x;
-    auto imax = [](int a, int b) { return a > b ? a : b; };
-    auto ladd = [](long long a, long long b) { return a + b; };
-    if (tid == 0) {
-        *s_run_carry = 0;
-        *s_cost_carry = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base < v.num_rows; base += kSchedThreads) {
-        const int r = base + tid;
-        const bool live = r < v.num_rows;
-        int start_here = -1;
-        if (live && (r == 0 || !v.same_group(r, r - 1))) start_here = r;
-        int run = block_inclusive_scan(start_here, s_int, imax);
-        run = imax(run, *s_run_carry);  // first row of the group holding r
-        long long cost = 0;
-        int g = 0;
-        if (live && (r - run) % kGMax == 0) {  // r starts a piece
-            g = rows_of_piece(v, r);
-            int e = 0;
-            for (int i = 0; i < g; ++i) e = imax(e, v.visible(r + i));
-            cost = (long long)((e + block_kv - 1) / block_kv) * (kCostBase + g);
+    const int n = v.num_rows;
+    for (int i = tid; i < kSchedThreads + kHalo; i += kSchedThreads) {
+        const int rr = base + i;
+        int vis = 0, last = 1;
+        if (rr < n) {
+            vis = v.visible(rr);
+            last = rr + 1 >= n || !v.same_group(rr + 1, rr);
         }
-        const long long incl = block_inclusive_scan(cost, s_ll, ladd);
-        if (write && cost > 0) {
-            const long long cum = *s_cost_carry + incl - cost;
-            // workers c whose start offset floor(c*T/W) lies in [cum, cum + cost)
-            long long c_lo = (cum * W + total - 1) / total;
-            long long c_hi = ((cum + cost) * W + total - 1) / total - 1;
-            if (c_hi > W - 1) c_hi = W - 1;
-            for (long long c = c_lo; c <= c_hi; ++c) {
-                const long long t = c * total / W;
-                sched[2 * c] = r;
-                sched[2 * c + 1] = (int)((t - cum) / (kCostBase + g));
+        sh.vis[i] = vis;
+        sh.last[i] = last;
+    }
+    const int r = base + tid;
+    const bool live = r < n;
+    const int start_here = (live && (r == 0 || !v.same_group(r, r - 1))) ? r : -1;
+    auto imax = [](int x, int y) { return x > y ? x : y; };
+    int run = block_scan_incl(start_here, sh.wi, imax, -1);  // (its barriers publish vis / last)
+    run = imax(run, sh.run_carry);                          // first row of the group holding r
+    g = 0;
+    long long cost = 0;
+    if (live && (r - run) % kGMax == 0) {  // r starts a piece: rows up to its group's end, at most kGMax
+        int e = 0;
+        bool go = true;
+#pragma unroll
+        for (int i = 0; i < kGMax; ++i)
+            if (go) {
+                e = imax(e, sh.vis[tid + i]);
+                g = i + 1;
+                go = !sh.last[tid + i];
             }
-        }
-        __syncthreads();
-        if (tid == kSchedThreads - 1) {
-            *s_run_carry = run;
-            *s_cost_carry += incl;
-        }
-        __syncthreads();
+        cost = (long long)((e + block_kv - 1) / block_kv) * (kCostBase + g);
     }
-    return *s_cost_carry;
+    __syncthreads();
+    if (tid == kSchedThreads - 1) sh.run_carry = run;
+    return cost;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int block_kv, int W,
-                                                                  int32_t *sched) {
-    __shared__ int s_int[kSchedThreads];
-    __shared__ long long s_ll[kSchedThreads];
-    __shared__ int s_run_carry;
-    __shared__ long long s_cost_carry;
-    const long long total = walk_rows(v, block_kv, W, sched, false, 0, s_int, s_ll, &s_run_carry,
-                                      &s_cost_carry);
+// Entries of the workers whose start offset floor(c * T / W) falls inside
+// [cum, cum + cost), the piece starting at row r with g rows.
+__device__ __forceinline__ void write_entries(int32_t *sched, int W, long long total, long long cum, long long cost,
+                                              int r, int g) {
+    long long c = (cum * W + total - 1) / total;
+    long long c_hi = ((cum + cost) * W + total - 1) / total - 1;
+    if (c_hi > W - 1) c_hi = W - 1;
+    if (c > c_hi) return;
+    // t = floor(c * T / W), stepped without a division per entry
+    const long long dq = total / W, dr = total % W;
+    long long t = c * total / W, rem = c * total % W;
+    for (; c <= c_hi; ++c) {
+        sched[2 * c] = r;
+        sched[2 * c + 1] = (int)((t - cum) / (kCostBase + g));
+        t += dq;
+        rem += dr;
+        if (rem >= W) {
+            rem -= W;
+            ++t;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int block_kv, int W, int32_t *sched) {
+    __shared__ SchedShared sh;
+    const int tid = threadIdx.x;
+    const int n = v.num_rows;
+    auto ladd = [](long long x, long long y) { return x + y; };
+    if (tid == 0) {
+        sh.run_carry = 0;
+        sh.cost_carry = 0;
+    }
+    __syncthreads();
+    if (n <= kSchedThreads) {
+        // one chunk: costs, total and entries in a single walk
+        int g;
+        const long long cost = chunk_cost(v, block_kv, 0, sh, g);
+        const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+        if (tid == kSchedThreads - 1) sh.cost_carry = incl;
+        __syncthreads();
+        const long long total = sh.cost_carry;
+        if (total == 0) {
+            for (int c = tid; c <= W; c += kSchedThreads) {
+                sched[2 * c] = n;
+                sched[2 * c + 1] = 0;
+            }
+            return;
+        }
+        if (tid == 0) {
+            sched[2 * W] = n;
+            sched[2 * W + 1] = 0;
+        }
+        if (cost > 0) write_entries(sched, W, total, incl - cost, cost, tid, g);
+        return;
+    }
+    // several chunks: the total first, then the entries
+    for (int base = 0; base < n; base += kSchedThreads) {
+        int g;
+        const long long cost = chunk_cost(v, block_kv, base, sh, g);
+        const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+        if (tid == kSchedThreads - 1) sh.cost_carry += incl;
+        __syncthreads();
+    }
+    const long long total = sh.cost_carry;
     __syncthreads();
     if (total == 0) {
-        for (int c = threadIdx.x; c <= W; c += kSchedThreads) {
-            sched[2 * c] = v.num_rows;
+        for (int c = tid; c <= W; c += kSchedThreads) {
+            sched[2 * c] = n;
             sched[2 * c + 1] = 0;
         }
         return;
     }
-    if (threadIdx.x == 0) {
-        sched[2 * W] = v.num_rows;
+    if (tid == 0) {
+        sched[2 * W] = n;
         sched[2 * W + 1] = 0;
+        sh.run_carry = 0;
+        sh.cost_carry = 0;
     }
-    walk_rows(v, block_kv, W, sched, true, total, s_int, s_ll, &s_run_carry, &s_cost_carry);
+    __syncthreads();
+    for (int base = 0; base < n; base += kSchedThreads) {
+        int g;
+        const long long cost = chunk_cost(v, block_kv, base, sh, g);
+        const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+        const long long carry = sh.cost_carry;
+        if (cost > 0) write_entries(sched, W, total, carry + incl - cost, cost, base + threadIdx.x, g);
+        __syncthreads();
+        if (tid == kSchedThreads - 1) sh.cost_carry = carry + incl;
+        __syncthreads();
+    }
 }
 
 }  // namespace pml
