@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=3, help="key-cache copies rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after timing, run one device-to-device copy of BYTES bytes (a known-size "
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -150,6 +152,31 @@ def run_timed(b, steps: int, warmup: int):
     return wall, per  # per: [steps, 3] ms of (schedule, logits, top-k)
 
 
+def capture_steps(b) -> list:
+    """One HIP graph per key-cache copy holding the whole step (schedule, logits,
+    top-k). The calls allocate nothing and never synchronise, so they capture."""
+    graphs = []
+    for i in range(len(b.kv)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            b.step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def run_graphs(graphs: list, steps: int, warmup: int) -> float:
+    """Warm up, then time exactly `steps` replays (rotating over the copies); wall seconds."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[(warmup + i) % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(case: syn.PagedCase, target_s: float) -> dict:
     """The oracle (as it stands) on a bounded sample of rows of the same workload."""
     import oracle
@@ -211,7 +238,13 @@ def main():
     b = PagedBench(case, args.copies)
     print(f"[bench] {case.rows} rows, {len(case.req_ctx)} requests, {b.pairs} scored pairs; timing",
           file=sys.stderr, flush=True)
+    # per-kernel times: eager launches bracketed by HIP events on the launch stream
     wall, per = run_timed(b, args.steps, args.warmup)
+    timing = "eager launches"
+    if not args.no_graph:
+        # whole-step throughput: the same steps replayed as HIP graphs (no launch gaps)
+        wall = run_graphs(capture_steps(b), args.steps, args.warmup)
+        timing = "HIP-graph replay of the step; per-kernel times from eager launches with HIP events"
     s = paged_summary("varlen_spec_decode_fp8_120k", b, wall, per, args.steps)
 
     line = {
@@ -227,6 +260,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp8",
         "data": "synthetic",
+        "timing": timing,
         "config": {"workload": "varlen speculative decode: 40 requests, ctx U[100K,128K], accepted lengths "
                                "U{1..6} flattened to rows, fp8 K cache block_kv 64, H 64, D 128, top-k 2048",
                    **describe(case), "parallelism": "single GPU", "num_workers": b.num_cus,
@@ -262,6 +296,8 @@ def main():
             print(f"[bench] {name}", file=sys.stderr, flush=True)
             ob = mk()
             w2, p2 = run_timed(ob, args.steps, args.warmup)
+            if not args.no_graph:
+                w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
             print(json.dumps(paged_summary(name, ob, w2, p2, args.steps)), file=sys.stderr, flush=True)
             del ob
         print("[bench] ragged_prefill_4x8192", file=sys.stderr, flush=True)

@@ -1,0 +1,60 @@
+"""The decode step (schedule -> logits -> top-k) captured in a HIP graph.
+
+The calls allocate nothing, never synchronise and clear nothing with memset,
+so a captured step must reproduce the eager step bit for bit on every replay,
+also with other work on the stream between the replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_mqa_logits_amd as pml
+import pml_synth as syn
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+
+def test_captured_step_matches_eager_on_every_replay():
+    case = syn.make_paged_case([3000, 700, 5000, 64], [3, 1, 6, 2], seed=900, max_ctx=5120)
+    other = syn.make_paged_case([4000, 100], [2, 5], seed=901, max_ctx=5120)
+    d = G.dev()
+    t = G.upload(case)
+    u = G.upload(other)
+    W = pml.default_num_workers()
+    sched = torch.empty(W + 1, 2, dtype=torch.int32, device=d)
+    logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
+    topk = torch.empty(case.rows, 64, dtype=torch.int32, device=d)
+
+    def step(x, c):
+        pml.paged_mqa_logits_metadata(x["lens"], c.block_kv, W, indices=x["indices"], out=sched)
+        pml.fp8_fp4_paged_mqa_logits(x["q"], x["kv"], x["w"], x["lens"], x["bt"], sched, c.max_ctx, x["indices"],
+                                     kv_format=c.kv_format, block_kv=c.block_kv, logits=logits)
+        pml.top_k_per_row(logits, x["lens"], 64, max_width=c.max_ctx, out=topk)
+
+    G.banner("graph capture of the decode step")
+    step(t, case)
+    torch.cuda.synchronize()
+    want = (sched.clone(), logits.clone(), topk.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(t, case)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        # other eager work on the same buffers between replays
+        sched.fill_(-7)
+        logits.fill_(123.0)
+        topk.fill_(-5)
+        if rep % 2:
+            oth = torch.empty(other.rows, pml.logits_ld(other.max_ctx), dtype=torch.float32, device=d)
+            pml.fp8_fp4_paged_mqa_logits(u["q"], u["kv"], u["w"], u["lens"], u["bt"],
+                                         pml.paged_mqa_logits_metadata(u["lens"], other.block_kv, W,
+                                                                       indices=u["indices"]),
+                                         other.max_ctx, u["indices"], kv_format=other.kv_format,
+                                         block_kv=other.block_kv, logits=oth)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(sched, want[0]), f"replay {rep}: schedule differs"
+        np.testing.assert_array_equal(logits.cpu().numpy(), want[1].cpu().numpy(), err_msg=f"replay {rep}")
+        assert torch.equal(topk, want[2]), f"replay {rep}: top-k differs"
