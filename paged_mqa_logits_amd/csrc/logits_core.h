@@ -11,8 +11,8 @@
 // shared by the 4 waves. Each wave takes whole key blocks on its own: the
 // block's keys go from HBM straight into VGPRs, already laid out as the B
 // operand of v_mfma_f32_16x16x128_f8f6f4 (lane l holds token l % 16 of a
-// 16-token slice), three buffers deep so two blocks are in flight while one
-// is scored. For every row the wave runs 4 head tiles x (BKV / 16) token
+// 16-token slice), two buffers deep so one block is in flight while one is
+// scored. For every row the wave runs 4 head tiles x (BKV / 16) token
 // slices of MFMAs, folds ReLU and w into per-lane partial sums in registers,
 // and a transpose-reduce with v_permlane32/16_swap leaves one finished token
 // per lane; the block's logits wait in LDS and go out as coalesced
@@ -157,8 +157,10 @@ __device__ __forceinline__ v8i load_a(const uint8_t *s_qrow, int ht) {
 // Score one staged row against the block in registers; returns twice this
 // lane's sum over all 64 heads for token out_token(lane) (before the key
 // scale; the factor 2 is exact and the caller folds 1/2 into the scale).
+constexpr int kPipe = 2;  // MFMAs issued ahead of the epilogue that reads them
+
 template <bool FP4, int BKV>
-__device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k, const uint8_t *s_qrow,
+__device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const uint8_t *s_qrow,
                                            const float *s_wrow) {
     using C = BlockCfg<FP4, BKV>;
     const int lane = lane_id();
@@ -166,25 +168,45 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k, const uin
     float p[C::NT];
 #pragma unroll
     for (int t = 0; t < C::NT; ++t) p[t] = 0.f;
+    // all LDS operands of the row first: one wait instead of one per head tile
+    v8i av[4];
+    v4f wv[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-        const v8i a = load_a<FP4>(s_qrow, ht);
-        const v4f w4 = lds_ld<v4f>(s_wrow + 16 * ht + 4 * grp);
+        av[ht] = load_a<FP4>(s_qrow, ht);
+        wv[ht] = lds_ld<v4f>(s_wrow + 16 * ht + 4 * grp);
+    }
+    // MFMA k = (head tile k / NT, slice k % NT) is issued kPipe steps before
+    // its epilogue, so the matrix core works while the VALU folds earlier
+    // results and few wait states are padded between an MFMA and its reader.
+    // The MFMA intrinsics have no side effects, so empty volatile asm
+    // statements pin the order: each MFMA takes its (unit) A scale from a
+    // register the asm before it rewrites, and each epilogue reads its
+    // result only after the asm that follows the next MFMAs.
+    constexpr int NK = 4 * C::NT;
+    v4f d[NK];
+    int unit = 127;  // e8m0 1.0
 #pragma unroll
-        for (int t = 0; t < C::NT; ++t) {
-            v4f d;
+    for (int k = 0; k < NK + kPipe; ++k) {
+        if (k < NK) {
+            const int ht = k / C::NT, t = k % C::NT;
+            asm volatile("" : "+v"(unit));
             if constexpr (FP4) {
-                const v8i b = v8i{k.v[t][0][0], k.v[t][0][1], k.v[t][0][2], k.v[t][0][3], 0, 0, 0, 0};
-                d = mfma_fp8_fp4(a, b, (int)(k.sc[t] & 0xffu));
+                const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3], 0, 0, 0, 0};
+                d[k] = mfma_scaled<4>(av[ht], b, unit, (int)(k_.sc[t] & 0xffu));
             } else {
-                const v8i b = v8i{k.v[t][0][0], k.v[t][0][1], k.v[t][0][2], k.v[t][0][3],
-                                  k.v[t][1][0], k.v[t][1][1], k.v[t][1][2], k.v[t][1][3]};
-                d = mfma_fp8(a, b);
+                const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3],
+                                  k_.v[t][1][0], k_.v[t][1][1], k_.v[t][1][2], k_.v[t][1][3]};
+                d[k] = mfma_scaled<0>(av[ht], b, unit, 127);
             }
+        }
+        if (k >= kPipe) {
+            const int e = k - kPipe, ht = e / C::NT, t = e % C::NT;
+            asm volatile("" : "+v"(d[e]));
             // d + |d| = 2 ReLU(d) is one add with an abs modifier (fmaxf would
             // canonicalise its input first); the factor 2 is taken out at the end
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[t] = __builtin_fmaf(w4[i], d[i] + __builtin_fabsf(d[i]), p[t]);
+            for (int i = 0; i < 4; ++i) p[t] = __builtin_fmaf(wv[ht][i], d[e][i] + __builtin_fabsf(d[e][i]), p[t]);
         }
     }
     // lane l holds partial sums of token 16t + l % 16 over heads of lane group

@@ -8,19 +8,17 @@
 //    request are processed together), so each key page is read from HBM once
 //    for all of them.
 //  * The 4 waves split the current piece's blocks into contiguous quarters.
-//    Each loads its pages from HBM
-//    straight into VGPRs, three buffers deep, and scores them against every
-//    row of the piece, whose q and w sit in LDS. Waves meet at a barrier only
-//    when the piece changes.
+//    Each loads its pages from HBM straight into VGPRs, two buffers deep
+//    (one block in flight while one is scored), and scores them against
+//    every row of the piece, whose q and w sit in LDS. Waves meet at a
+//    barrier only when the piece changes.
 //  * Logit stores are issued as inline asm one step after the block is
-//    scored, so the compiler waits for a page exactly and the two pages
-//    behind it stay in flight.
+//    scored, so the compiler waits for a page exactly and the page behind
+//    it stays in flight.
 //  * All per-unit metadata (schedule, block table, lengths, request ids) is
 //    read through the scalar cache.
 //  * Columns past each row's last visible block are filled with -inf by the
 //    workgroups after their units (row-strided).
-#include <type_traits>
-
 #include "logits_core.h"
 #include "rows.h"
 
@@ -54,8 +52,8 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 }
 
 // One step of a wave's block loop: wait for block b, store the previous
-// block's logits, request block bp (two steps ahead; with PF) into the buffer
-// freed by the previous step, and score block b against the g staged rows
+// block's logits, request block bp (kDepth steps ahead; with PF) into the
+// buffer freed by the previous step, and score block b against the g staged rows
 // into the wave's LDS slot. Rows whose visible length ends before the block are
 // skipped (their tail is filled separately). Lane i of vis_lane holds the
 // visible length of row i.
@@ -85,6 +83,9 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
     mask = m;
     col0p = col0;
 }
+
+constexpr int kDepth = 1;          // key blocks in flight per wave while one is scored
+constexpr int kBufs = kDepth + 1;  // key-block buffers per wave
 
 template <bool FP4, int BKV>
 __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a) {
@@ -121,50 +122,25 @@ __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a)
             const int per = (blk_hi - blk_lo) / kCW, rem = (blk_hi - blk_lo) % kCW;
             const int b0 = blk_lo + wave * per + min(wave, rem);
             const int nmy = per + (wave < rem ? 1 : 0);
-            KeyRegs<FP4, BKV> k0, k1, k2;
-            bool ok0 = false, ok1 = false, ok2 = false;
+            // kDepth blocks in flight: step s waits for block s, then requests
+            // block s + kDepth (near the end of the range the last block again,
+            // an L2 hit, so every step has the same loads behind its wait)
+            KeyRegs<FP4, BKV> kb[kBufs];
+            bool okb[kBufs];
             int mask = 0, col0p = 0;
-            // step(kc, j, kp): score this wave's j-th block from kc and, when
-            // kp is given, request block j + 2 into it
-            auto step = [&](const KeyRegs<FP4, BKV> &kc, bool okc, int j, KeyRegs<FP4, BKV> &kp, bool &okp, auto pf) {
-                wave_step<FP4, BKV, decltype(pf)::value>(a, r0, g, bt_row, b0 + j, kc, okc, b0 + j + 2,
-                                                         kp, okp, s_q, s_w, vis_lane, sl, mask, col0p);
-            };
-            constexpr std::true_type PF{};
-            constexpr std::false_type NOPF{};
-            if (nmy >= 3) {
-                // Every step of the main loop requests a block, so the wait at
-                // the top of a step always has the same loads behind it.
-                ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
-                ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + 1, k1);
-                for (int j = 0;;) {
-                    if (j + 2 >= nmy) {  // blocks j (k0) and j + 1 (k1) remain
-                        step(k0, ok0, j, k2, ok2, NOPF);
-                        step(k1, ok1, j + 1, k2, ok2, NOPF);
-                        break;
+            if (nmy > 0) {
+                const int last = nmy - 1;
+#pragma unroll
+                for (int u = 0; u < kDepth; ++u) okb[u] = fetch_block<FP4, BKV>(a, bt_row, b0 + min(u, last), kb[u]);
+                for (int j = 0; j < nmy; j += kBufs) {
+#pragma unroll
+                    for (int u = 0; u < kBufs; ++u) {
+                        if (j + u >= nmy) break;
+                        wave_step<FP4, BKV, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u],
+                                                  b0 + min(j + u + kDepth, last), kb[(u + kDepth) % kBufs],
+                                                  okb[(u + kDepth) % kBufs], s_q, s_w, vis_lane, sl, mask, col0p);
                     }
-                    step(k0, ok0, j, k2, ok2, PF);
-                    ++j;
-                    if (j + 2 >= nmy) {  // k1, k2 remain
-                        step(k1, ok1, j, k0, ok0, NOPF);
-                        step(k2, ok2, j + 1, k0, ok0, NOPF);
-                        break;
-                    }
-                    step(k1, ok1, j, k0, ok0, PF);
-                    ++j;
-                    if (j + 2 >= nmy) {  // k2, k0 remain
-                        step(k2, ok2, j, k1, ok1, NOPF);
-                        step(k0, ok0, j + 1, k1, ok1, NOPF);
-                        break;
-                    }
-                    step(k2, ok2, j, k1, ok1, PF);
-                    ++j;
                 }
-            } else if (nmy > 0) {
-                ok0 = fetch_block<FP4, BKV>(a, bt_row, b0, k0);
-                if (nmy > 1) ok1 = fetch_block<FP4, BKV>(a, bt_row, b0 + 1, k1);
-                step(k0, ok0, 0, k2, ok2, NOPF);
-                if (nmy > 1) step(k1, ok1, 1, k2, ok2, NOPF);
             }
             if (nmy > 0) flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
         }

@@ -97,16 +97,12 @@ __device__ __forceinline__ void dma4(const void *gsrc, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
 }
 
-// D = A(16x128 fp8) * B(128x16 fp8), fresh accumulator.
-__device__ __forceinline__ v4f mfma_fp8(const v8i &a, const v8i &b) {
+// D = A(16x128 fp8, e8m0 scale per row and 32-block of k) * B(128x16 fp8 when
+// FMT_B == 0, e2m1 when FMT_B == 4, e8m0 scale per column and 32-block).
+template <int FMT_B>
+__device__ __forceinline__ v4f mfma_scaled(const v8i &a, const v8i &b, int a_scale, int b_scale) {
     v4f z = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
-}
-
-// D = A(16x128 fp8, unit scale) * B(128x16 e2m1, e8m0 scale per lane's 32-block).
-__device__ __forceinline__ v4f mfma_fp8_fp4(const v8i &a, const v8i &b, int b_scale) {
-    v4f z = {0.f, 0.f, 0.f, 0.f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 4, 0, 127, 0, b_scale);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, FMT_B, 0, a_scale, 0, b_scale);
 }
 
 // Exchange halves between two registers (gfx950 v_permlane32_swap / 16_swap).
