@@ -88,7 +88,7 @@ class PagedBench:
         self.indices = None if case.indices is None else case.indices.to(d)
         self.kv = [case.kv_cache.to(d) for _ in range(max(1, copies))]
         self.num_cus = num_cus or pml.default_num_workers()
-        self.sched = torch.empty(self.num_cus + 1, 2, dtype=torch.int32, device=d)
+        self.sched = torch.empty(pml.schedule_rows(self.num_cus), 2, dtype=torch.int32, device=d)
         self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
         self.topk = torch.empty(case.rows, case.topk, dtype=torch.int32, device=d)
         self.req_tokens = int(sum(case.req_ctx))

@@ -71,11 +71,11 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
 #define PML_MAX_TOPK 4096
 
 /*
- * paged_mqa_logits_metadata - split the paged-logits work over persistent
+ * paged_mqa_logits_metadata - split the paged-logits work for persistent
  * workgroups ("get_paged_mqa_logits_metadata(context_lens, block_kv, num_SMs,
  * indices=)", [Attention][DSA] Route SM100 sparse-indexer decode ... , Purpose
- * and Changes; the schedule has num_SMs + 1 entries and a row slice gets its
- * own schedule, sparse_attn_indexer page, _varlen_decode_rows).
+ * and Changes; the schedule is sized by the number of SMs and a row slice gets
+ * its own schedule, sparse_attn_indexer page, _varlen_decode_rows).
  *
  *   context_lens     int32. With indices or next_n == 1: [num_rows], the
  *                    tokens each row sees. Otherwise [num_rows / next_n]
@@ -91,19 +91,30 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
  *                    Requires next_n == 1 (else PML_ERR_VARLEN_NEXT_N).
  *   block_kv         tokens per cache page: 32 or 64 (else PML_ERR_BLOCK_KV).
  *   num_CUs          number of persistent workgroups the logits call will
- *                    launch (>= 1; e.g. 2 per compute unit).
- *   schedule         int32 [num_CUs + 1][2] output: for each workgroup the
- *                    (first row of its first row-piece, block offset) where its
- *                    contiguous share of (row-piece, key-block) units starts;
- *                    entry num_CUs is (num_rows, 0). A row-piece is at most 8
- *                    consecutive rows of one group. Units are weighted by
- *                    (1 + rows in the piece) so shares cost about the same.
+ *                    launch (1 .. 2^20, else PML_ERR_SHAPE; e.g. 2 per
+ *                    compute unit).
+ *   schedule         int32 [paged_mqa_logits_schedule_rows(num_CUs)][2]
+ *                    output, 16-B aligned (else PML_ERR_ALIGN). The
+ *                    (row-piece, key-block) units, ordered by piece then
+ *                    block, are cut into C = 8 * num_CUs chunks of about equal
+ *                    cost. Entry c < C is the (first row of its row-piece,
+ *                    block offset) where chunk c starts; entry C is
+ *                    (num_rows, 0). The entries after it hold the logits
+ *                    call's work counters, which this call sets to zero. A
+ *                    row-piece is at most 8 consecutive rows of one group.
+ *                    Units are weighted by (2 + rows in the piece) so chunks
+ *                    cost about the same.
  * The schedule is valid only for the same context_lens, indices, next_n,
  * block_kv and num_CUs.
  */
 int paged_mqa_logits_metadata(const int32_t *context_lens, int num_rows, int next_n,
                               int context_lens_2d, const int32_t *indices, int block_kv,
                               int num_CUs, int32_t *schedule, void *stream);
+
+/* Rows of [2] int32 entries in the schedule for num_CUs workgroups (host
+ * only, no GPU call): 8 * num_CUs + 129. -1 when num_CUs is outside
+ * 1 .. 2^20. */
+int paged_mqa_logits_schedule_rows(int num_CUs);
 
 /*
  * fp8_fp4_paged_mqa_logits - score every visible token of a paged key cache
@@ -127,8 +138,16 @@ int paged_mqa_logits_metadata(const int32_t *context_lens, int num_rows, int nex
  *                    group must hold the same entries). Entries of blocks a
  *                    row does not see are never read. block_table_cols
  *                    (<= ld) bounds the block index; beyond it a block scores NaN.
- *   schedule, num_CUs the metadata call's output and its num_CUs; the kernel
- *                    launches num_CUs workgroups.
+ *   schedule, num_CUs the metadata call's output and its num_CUs (schedule
+ *                    16-B aligned); the kernel launches num_CUs workgroups.
+ *                    Workgroup w first takes chunks [7w, 7w + 7); the last
+ *                    num_CUs chunks are dealt out at run time through the
+ *                    schedule's work counters, so that workgroups slowed by
+ *                    their neighbours take fewer. Every call advances the
+ *                    counters by a fixed amount and reads them modulo it, so
+ *                    one schedule serves any number of calls queued one after
+ *                    another; calls that share a schedule must not run at the
+ *                    same time (calls on one stream never do).
  *   max_ctx          output columns (>= every visible length).
  *   logits           fp32 [num_rows][logits_ld] output, 16-B aligned,
  *                    logits_ld >= max_ctx and a multiple of 4. Columns
@@ -140,7 +159,7 @@ int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n, int num_he
                              int64_t page_stride_bytes, int64_t num_pages, const float *weights,
                              const int32_t *context_lens, int context_lens_2d,
                              const int32_t *block_table, int64_t block_table_ld,
-                             int block_table_cols, const int32_t *schedule, int num_CUs,
+                             int block_table_cols, int32_t *schedule, int num_CUs,
                              const int32_t *indices, int max_ctx, float *logits,
                              int64_t logits_ld, void *stream);
 

@@ -1,8 +1,8 @@
 """Specification of the work split returned by the metadata call (test infrastructure).
 
-The pages fix only the shape of this output: one entry per persistent worker
-plus one ("schedule.shape[0] - 1" is the number of SMs, sparse_attn_indexer
-page, _varlen_decode_rows) and that a row slice needs its own schedule. Its
+The pages size this output by the number of persistent workers (the caller
+reads the SM count back from the schedule's first dimension, sparse_attn_indexer
+page, _varlen_decode_rows) and give a row slice a schedule of its own. The
 content is this library's own definition, stated here in plain Python:
 
 * Rows are grouped as the varlen decode path groups them ("[Bugfix]
@@ -12,10 +12,13 @@ content is this library's own definition, stated here in plain Python:
 * A group is cut into pieces of at most ``G_MAX`` consecutive rows.
 * A piece's extent is the largest visible length among its rows; it has
   ``nblk = ceil(extent / block_kv)`` key blocks, each costing ``COST_BASE + g``
-  (g = rows in the piece: one page read plus g rows of scoring).
-* Units (piece, block) are ordered by piece then block. Worker c starts at
-  the unit holding cost offset floor(c * T / W) of the total T; entry W is
-  the end sentinel (num_rows, 0).
+  (g = rows in the piece: a page read and the fixed work of a step, then g
+  rows of scoring; a one-row block takes about a third of a six-row one).
+* Units (piece, block) are ordered by piece then block and cut into C chunks
+  (a fixed number per logits workgroup). Chunk c starts at the unit holding
+  cost offset floor(c * T / C) of the total T; entry C is the end sentinel
+  (num_rows, 0). The device output appends the logits call's work counters,
+  which start at zero.
 
 Entries are (first row of the piece, block offset within the piece).
 """
@@ -24,7 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 G_MAX = 8
-COST_BASE = 1
+COST_BASE = 2
 
 
 def visible_lengths(context_lens: np.ndarray, num_rows: int, next_n: int, lens_2d: bool) -> np.ndarray:
@@ -69,27 +72,28 @@ def piece_table(context_lens, num_rows, next_n, lens_2d, indices, block_kv):
 
 
 def schedule(context_lens, num_rows: int, next_n: int, lens_2d: bool, indices, block_kv: int,
-             num_workers: int) -> np.ndarray:
+             num_chunks: int) -> np.ndarray:
     table = piece_table(context_lens, num_rows, next_n, lens_2d, indices, block_kv)
     total = sum(t[3] for t in table)
-    out = np.zeros((num_workers + 1, 2), dtype=np.int32)
-    out[num_workers] = (num_rows, 0)
-    for c in range(num_workers):
-        if total == 0:
-            out[c] = (num_rows, 0)
-            continue
-        target = c * total // num_workers
-        cum = 0
-        for s, g, nblk, cost in table:
-            if cum <= target < cum + cost:
-                out[c] = (s, (target - cum) // (COST_BASE + g))
-                break
-            cum += cost
+    out = np.zeros((num_chunks + 1, 2), dtype=np.int32)
+    out[num_chunks] = (num_rows, 0)
+    if total == 0:
+        out[:] = (num_rows, 0)
+        return out
+    # targets grow with c, so one forward walk over the pieces finds them all
+    p, cum = 0, 0
+    for c in range(num_chunks):
+        target = c * total // num_chunks
+        while not (cum <= target < cum + table[p][3]):
+            cum += table[p][3]
+            p += 1
+        s, g, nblk, cost = table[p]
+        out[c] = (s, (target - cum) // (COST_BASE + g))
     return out
 
 
-def units_of_worker(sched: np.ndarray, table, c: int) -> list[tuple[int, int]]:
-    """Enumerate the (first row, block) units worker c processes."""
+def units_of_chunk(sched: np.ndarray, table, c: int) -> list[tuple[int, int]]:
+    """Enumerate the (first row, block) units of chunk c."""
     start = tuple(sched[c])
     end = tuple(sched[c + 1])
     units = []

@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(str(_LIB_PATH))
         P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.paged_mqa_logits_metadata.argtypes = [P, I, I, I, P, I, I, P, P]
+        L.paged_mqa_logits_schedule_rows.argtypes = [I]
+        L.paged_mqa_logits_schedule_rows.restype = I
         L.fp8_fp4_paged_mqa_logits.argtypes = [P, I, I, I, I, P, I, I, I64, I64, P, P, I, P, I64, I, P,
                                                I, P, I, P, I64, P]
         if hasattr(L, "mqa_logits"):
@@ -130,7 +132,9 @@ def _rows_of(context_lens: torch.Tensor, next_n: int, indices) -> tuple[int, int
 def paged_mqa_logits_metadata(context_lens: torch.Tensor, block_kv: int, num_cus: int | None = None,
                               indices: torch.Tensor | None = None, next_n: int = 1,
                               out: torch.Tensor | None = None) -> torch.Tensor:
-    """Work split of the paged-logits call: int32 [num_cus + 1, 2] on the device."""
+    """Work split of the paged-logits call for num_cus workgroups: int32
+    [schedule_rows(num_cus), 2] on the device (chunk entries, end entry, work
+    counters)."""
     _dev(context_lens, "context_lens", _I32)
     context_lens = context_lens.contiguous()
     if indices is not None:
@@ -138,13 +142,31 @@ def paged_mqa_logits_metadata(context_lens: torch.Tensor, block_kv: int, num_cus
     if num_cus is None:
         num_cus = default_num_workers(context_lens.device)
     rows, l2d = _rows_of(context_lens, next_n, indices)
+    n = schedule_rows(num_cus)
     if out is None:
-        out = torch.empty(num_cus + 1, 2, dtype=torch.int32, device=context_lens.device)
-    elif out.numel() < 2 * (num_cus + 1) or not out.is_contiguous():
-        raise ValueError("schedule buffer too small or not contiguous")
+        out = torch.empty(n, 2, dtype=torch.int32, device=context_lens.device)
+    elif out.shape != (n, 2) or not out.is_contiguous():
+        raise ValueError(f"schedule buffer must be a contiguous [{n}, 2] tensor")
     _check(lib().paged_mqa_logits_metadata(_p(context_lens), rows, next_n, l2d, _p(indices), block_kv,
                                            num_cus, _p(out), _stream()), "paged_mqa_logits_metadata")
     return out
+
+
+def schedule_rows(num_cus: int) -> int:
+    """Rows of the [rows, 2] schedule tensor for num_cus logits workgroups."""
+    n = lib().paged_mqa_logits_schedule_rows(int(num_cus))
+    if n < 0:
+        raise ValueError(f"num_cus {num_cus} outside 1 .. 2^20")
+    return n
+
+
+def schedule_workers(schedule: torch.Tensor) -> int:
+    """Workgroups a schedule tensor was made for (the inverse of schedule_rows)."""
+    per = schedule_rows(2) - schedule_rows(1)
+    W = (schedule.shape[0] - schedule_rows(1)) // per + 1
+    if schedule.dim() != 2 or schedule.shape[1] != 2 or W < 1 or schedule_rows(W) != schedule.shape[0]:
+        raise ValueError(f"schedule of shape {tuple(schedule.shape)} is not a metadata output")
+    return W
 
 
 def logits_ld(max_ctx: int) -> int:
@@ -184,7 +206,9 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
         logits = torch.empty(rows, logits_ld(max_model_len), dtype=torch.float32, device=q.device)
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with unit inner stride")
-    num_cus = schedule.shape[0] - 1
+    num_cus = schedule_workers(schedule)
+    if not schedule.is_contiguous():
+        raise ValueError("schedule must be contiguous")
     _check(lib().fp8_fp4_paged_mqa_logits(
         _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
         kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),

@@ -107,11 +107,12 @@ __device__ __forceinline__ int q_lds_off(int h, int c) { return h * PML_HEAD_DIM
 // Stage q and w of rows r0 .. r0 + g - 1 into LDS (the whole workgroup). All
 // loads are issued before the first LDS store, so staging costs one memory
 // latency rather than one per round of the thread loop.
+template <int NTH = kLThreads>
 __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int64_t r0, int g, uint8_t *s_q,
                                            float *s_w) {
-    constexpr int kChunks = kQBytes / 16;                     // 16-B chunks per row
-    constexpr int kPer = kGMax * kChunks / kLThreads;         // chunks per thread, at most
-    constexpr int kWPer = (kGMax * PML_HEADS + kLThreads - 1) / kLThreads;
+    constexpr int kChunks = kQBytes / 16;               // 16-B chunks per row
+    constexpr int kPer = kGMax * kChunks / NTH;         // chunks per thread, at most
+    constexpr int kWPer = (kGMax * PML_HEADS + NTH - 1) / NTH;
     const int tid = threadIdx.x;
     const int nchunk = g * kChunks;
     const uint8_t *src = q + r0 * kQBytes;
@@ -119,13 +120,13 @@ __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int
     float wv[kWPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k)
-        if (tid + k * kLThreads < nchunk) x[k] = *(const v4i *)(src + (tid + k * kLThreads) * 16);
+        if (tid + k * NTH < nchunk) x[k] = *(const v4i *)(src + (tid + k * NTH) * 16);
 #pragma unroll
     for (int k = 0; k < kWPer; ++k)
-        if (tid + k * kLThreads < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * kLThreads];
+        if (tid + k * NTH < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * NTH];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-        const int i = tid + k * kLThreads;
+        const int i = tid + k * NTH;
         if (i < nchunk) {
             const int row = i / kChunks, rem = i % kChunks;
             *(v4i *)(s_q + row * kQBytes + q_lds_off(rem / 8, rem % 8)) = x[k];
@@ -133,7 +134,7 @@ __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int
     }
 #pragma unroll
     for (int k = 0; k < kWPer; ++k)
-        if (tid + k * kLThreads < g * PML_HEADS) s_w[tid + k * kLThreads] = wv[k];
+        if (tid + k * NTH < g * PML_HEADS) s_w[tid + k * NTH] = wv[k];
 }
 
 // A operand (q of heads 16 ht + lane % 16) of one staged row, in the
@@ -154,10 +155,48 @@ __device__ __forceinline__ v8i load_a(const uint8_t *s_qrow, int ht) {
     return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Lane l holds partial sums p[t] of token 16t + l % 16 over the heads of lane
+// group l / 16; transpose slices against lane groups and add, leaving token
+// out_token(l)'s total in lane l.
+template <bool FP4, int BKV>
+__device__ __forceinline__ float reduce_slices(float *p) {  // p[BlockCfg::NT]
+    using C = BlockCfg<FP4, BKV>;
+    if (C::NT == 4) {
+        swap32(p[0], p[2 % C::NT]);
+        swap32(p[1 % C::NT], p[3 % C::NT]);
+        float x = p[0] + p[2 % C::NT];
+        float y = p[1 % C::NT] + p[3 % C::NT];
+        swap16(x, y);
+        return x + y;
+    } else {
+        swap32(p[0], p[1 % C::NT]);
+        float x = p[0] + p[1 % C::NT];
+        float y = x;
+        swap16(x, y);
+        return x + y;
+    }
+}
+
 // Score one staged row against the block in registers; returns twice this
 // lane's sum over all 64 heads for token out_token(lane) (before the key
 // scale; the factor 2 is exact and the caller folds 1/2 into the scale).
 constexpr int kPipe = 2;  // MFMAs issued ahead of the epilogue that reads them
+
+// MFMA of one 16-token slice t. fp8 x fp8 takes the unscaled opcode: the
+// scaled form costs an extra VALU instruction per MFMA (it loads the scales),
+// measured as about a fifth more SIMD time for MFMA plus epilogue. MXFP4 keys
+// need their e8m0 block scales, with A at unit scale (`unit` = 127).
+template <bool FP4, int BKV>
+__device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i &a, int t, int unit) {
+    if constexpr (FP4) {
+        const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3], 0, 0, 0, 0};
+        return mfma_scaled<4>(a, b, unit, (int)(k_.sc[t] & 0xffu));
+    } else {
+        const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3],
+                          k_.v[t][1][0], k_.v[t][1][1], k_.v[t][1][2], k_.v[t][1][3]};
+        return mfma_fp8(a, b);
+    }
+}
 
 template <bool FP4, int BKV>
 __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const uint8_t *s_qrow,
@@ -180,25 +219,21 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
     // its epilogue, so the matrix core works while the VALU folds earlier
     // results and few wait states are padded between an MFMA and its reader.
     // The MFMA intrinsics have no side effects, so empty volatile asm
-    // statements pin the order: each MFMA takes its (unit) A scale from a
-    // register the asm before it rewrites, and each epilogue reads its
-    // result only after the asm that follows the next MFMAs.
+    // statements pin the order: each MFMA takes an operand (its A tile, or
+    // for MXFP4 the unit A scale) that the asm before it claims to rewrite,
+    // and each epilogue reads its result only after the asm that follows the
+    // next MFMAs.
     constexpr int NK = 4 * C::NT;
     v4f d[NK];
     int unit = 127;  // e8m0 1.0
 #pragma unroll
     for (int k = 0; k < NK + kPipe; ++k) {
         if (k < NK) {
-            const int ht = k / C::NT, t = k % C::NT;
-            asm volatile("" : "+v"(unit));
-            if constexpr (FP4) {
-                const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3], 0, 0, 0, 0};
-                d[k] = mfma_scaled<4>(av[ht], b, unit, (int)(k_.sc[t] & 0xffu));
-            } else {
-                const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3],
-                                  k_.v[t][1][0], k_.v[t][1][1], k_.v[t][1][2], k_.v[t][1][3]};
-                d[k] = mfma_scaled<0>(av[ht], b, unit, 127);
-            }
+            if constexpr (FP4)
+                asm volatile("" : "+v"(unit));
+            else
+                asm volatile("" : "+v"(av[k / C::NT]));
+            d[k] = mfma_slice<FP4, BKV>(k_, av[k / C::NT], k % C::NT, unit);
         }
         if (k >= kPipe) {
             const int e = k - kPipe, ht = e / C::NT, t = e % C::NT;
@@ -209,22 +244,7 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
             for (int i = 0; i < 4; ++i) p[t] = __builtin_fmaf(wv[ht][i], d[e][i] + __builtin_fabsf(d[e][i]), p[t]);
         }
     }
-    // lane l holds partial sums of token 16t + l % 16 over heads of lane group
-    // l / 16; the swaps transpose slices against lane groups and add
-    if (C::NT == 4) {
-        swap32(p[0], p[2 % C::NT]);
-        swap32(p[1 % C::NT], p[3 % C::NT]);
-        float x = p[0] + p[2 % C::NT];
-        float y = p[1 % C::NT] + p[3 % C::NT];
-        swap16(x, y);
-        return x + y;
-    } else {
-        swap32(p[0], p[1 % C::NT]);
-        float x = p[0] + p[1 % C::NT];
-        float y = x;
-        swap16(x, y);
-        return x + y;
-    }
+    return reduce_slices<FP4, BKV>(p);
 }
 
 // An empty use of the block's registers. The compiler places its wait for
@@ -292,7 +312,8 @@ __device__ __forceinline__ void flush_slot(const WaveSlot<BKV> &sl, int mask, in
     }
 }
 
-// Fill columns [c0, c1) of one row with -inf (the whole workgroup).
+// Fill columns [c0, c1) of one row with -inf (the whole workgroup of NTH threads).
+template <int NTH = kLThreads>
 __device__ __forceinline__ void fill_neg_inf(float *row, int c0, int c1) {
     if (c0 >= c1) return;
     const int tid = threadIdx.x;
@@ -300,7 +321,7 @@ __device__ __forceinline__ void fill_neg_inf(float *row, int c0, int c1) {
     const int a4 = min((c0 + 3) & ~3, c1);  // first 16-B aligned column (rows are 16-B aligned)
     const int b4 = max(a4, c1 & ~3);
     if (c0 + tid < a4) row[c0 + tid] = -__builtin_inff();
-    for (int col = a4 + 4 * tid; col < b4; col += 4 * kLThreads) *(v4f *)(row + col) = ninf;
+    for (int col = a4 + 4 * tid; col < b4; col += 4 * NTH) *(v4f *)(row + col) = ninf;
     if (b4 + tid < c1) row[b4 + tid] = -__builtin_inff();
 }
 

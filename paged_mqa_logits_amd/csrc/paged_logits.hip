@@ -2,11 +2,14 @@
 // key cache for each query row (scoring core in logits_core.h).
 //
 // Design (gfx950):
-//  * Persistent grid: one workgroup per schedule entry. Each walks its
-//    contiguous run of (row-piece, key-block) units. A row-piece is up to 8
-//    rows of one request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a
-//    request are processed together), so each key page is read from HBM once
-//    for all of them.
+//  * Persistent grid of num_CUs workgroups. The schedule cuts the ordered
+//    (row-piece, key-block) units into chunks of about equal cost, several
+//    per workgroup; workgroups take chunks in turn from a device-wide counter
+//    and walk each one's contiguous run of units, so the grid stays balanced
+//    whatever slows one workgroup down. A row-piece is up to 8 rows of one
+//    request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a request are
+//    processed together), so each key page is read from HBM once for all of
+//    them.
 //  * The 4 waves split the current piece's blocks into contiguous quarters.
 //    Each loads its pages from HBM straight into VGPRs, two buffers deep
 //    (one block in flight while one is scored), and scores them against
@@ -15,8 +18,8 @@
 //  * Logit stores are issued as inline asm one step after the block is
 //    scored, so the compiler waits for a page exactly and the page behind
 //    it stays in flight.
-//  * All per-unit metadata (schedule, block table, lengths, request ids) is
-//    read through the scalar cache.
+//  * All per-unit metadata (chunk entries, block table, lengths, request ids)
+//    is read through the scalar cache; the counters only by vector atomics.
 //  * Columns past each row's last visible block are filled with -inf by the
 //    workgroups after their units (row-strided).
 #include "logits_core.h"
@@ -34,7 +37,8 @@ struct PagedArgs {
     const int32_t *bt;
     int64_t bt_ld;
     int bt_cols;
-    const int32_t *sched;
+    const int32_t *sched;  // chunk entries (read through the scalar cache)
+    int32_t *ctr;          // 64-bit work counters, kPoolStride int32 apart
     int max_ctx;
     float *out;
     int64_t out_ld;
@@ -52,7 +56,7 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 }
 
 // One step of a wave's block loop: wait for block b, store the previous
-// block's logits, request block bp (kDepth steps ahead; with PF) into the
+// block's logits, request block bp (the depth ahead; with PF) into the
 // buffer freed by the previous step, and score block b against the g staged rows
 // into the wave's LDS slot. Rows whose visible length ends before the block are
 // skipped (their tail is filled separately). Lane i of vis_lane holds the
@@ -84,15 +88,107 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
     col0p = col0;
 }
 
+constexpr int kPW = kCW;            // waves per workgroup
+constexpr int kPThreads = kPW * kWave;
 constexpr int kDepth = 1;          // key blocks in flight per wave while one is scored
 constexpr int kBufs = kDepth + 1;  // key-block buffers per wave
+constexpr int kDrawAhead = 2;      // steps before a range ends at which the next chunk is drawn
+
+// A draw from a work counter. Thread 0 issues the atomic; the value is read
+// after the range, by which time it has usually arrived (a loaded round trip
+// to memory takes about as long as two block steps).
+struct Draw {
+    unsigned long long *ctr;
+    unsigned long long v;
+    bool done;
+    __device__ __forceinline__ void issue() {
+        if (threadIdx.x == 0) v = atomicAdd(ctr, 1ull);
+        done = true;
+    }
+};
+
+// One piece (the whole workgroup): stage its rows, then every wave scores its
+// blocks [b0, b0 + nmy). kDepth blocks are in flight per wave while one is
+// scored: step s waits for block s, then requests block s + kDepth (near the
+// end of the range the last block again, an L2 hit, so every step has the same
+// loads behind its wait). The first blocks are requested before q is staged,
+// so the two memory round trips overlap. With draw_here, the wave issues the
+// draw DrawAhead steps before its blocks end.
+template <bool FP4, int BKV>
+__device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int64_t bt_row, int b0, int nmy,
+                                          uint8_t *s_q, float *s_w, int *s_vis, WaveSlot<BKV> &sl, Draw &dr,
+                                          bool draw_here) {
+    constexpr int NB = kBufs;
+    const int tid = threadIdx.x;
+    const int last = nmy - 1;
+    KeyRegs<FP4, BKV> kb[NB];
+    bool okb[NB];
+    if (nmy > 0) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) okb[u] = fetch_block<FP4, BKV>(a, bt_row, b0 + min(u, last), kb[u]);
+    }
+    stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w);
+    if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
+    barrier_lds();
+    const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
+    if (nmy > 0) {
+        int mask = 0, col0p = 0;
+        for (int j = 0; j < nmy; j += NB) {
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                if (j + u >= nmy) break;
+                if (draw_here && j + u == max(nmy - kDrawAhead, 0)) dr.issue();
+                wave_step<FP4, BKV, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
+                                          kb[(u + kDepth) % NB], okb[(u + kDepth) % NB], s_q, s_w, vis_lane, sl, mask,
+                                          col0p);
+            }
+        }
+        flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
+    }
+}
+
+// The units from chunk e0's start to chunk e1's start (the whole workgroup).
+// Wave 0 issues the draw kDrawAhead steps before its share of the last piece
+// ends; a range too short for that leaves it to the caller.
+template <bool FP4, int BKV>
+__device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, uint8_t *s_q, float *s_w, int *s_vis,
+                                           WaveSlot<BKV> &sl, Draw &dr) {
+    const int tid = threadIdx.x;
+    const int wave = uni(tid / kWave);
+    const int n = a.rows.num_rows;
+    int r0 = min(max(sload(a.sched, 2 * e0), 0), n);
+    int blk_lo = max(sload(a.sched, 2 * e0 + 1), 0);
+    const int end_r = min(max(sload(a.sched, 2 * e1), 0), n);
+    const int end_b = max(sload(a.sched, 2 * e1 + 1), 0);
+    while (r0 < n && (r0 < end_r || (r0 == end_r && blk_lo < end_b))) {
+        int g, nblk;
+        piece_at<BKV>(a.rows, r0, g, nblk);
+        const int blk_hi = r0 == end_r ? min(end_b, nblk) : nblk;
+        const int rn = r0 + g;  // the next piece, if the range goes on
+        const bool last_piece = !(rn < n && (rn < end_r || (rn == end_r && end_b > 0)));
+        if (blk_lo < blk_hi) {
+            barrier_lds();  // every wave is done with the previous piece
+            const int64_t bt_row = r0 / a.rows.next_n;
+            // this wave's blocks: a contiguous quarter of [blk_lo, blk_hi), so
+            // its block-table entries share scalar-cache lines
+            const int per = (blk_hi - blk_lo) / kPW, rem = (blk_hi - blk_lo) % kPW;
+            const int b0 = blk_lo + wave * per + min(wave, rem);
+            const int nmy = per + (wave < rem ? 1 : 0);
+            const bool draw_here = last_piece && wave == 0 && !dr.done;
+            run_piece<FP4, BKV>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
+        }
+        r0 = rn;
+        blk_lo = 0;
+    }
+}
 
 template <bool FP4, int BKV>
-__global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a) {
+__global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_vis[kGMax];
-    __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kCW];
+    __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kPW];
+    __shared__ unsigned s_take[2];
 
     const int tid = threadIdx.x;
     const int wave = uni(tid / kWave);
@@ -101,64 +197,46 @@ __global__ __launch_bounds__(kLThreads, 2) void paged_logits_kernel(PagedArgs a)
     const int n = a.rows.num_rows;
     WaveSlot<BKV> &sl = s_slot[wave];
 
-    int r0 = min(max(sload(a.sched, 2 * c), 0), n);
-    int blk_lo = max(sload(a.sched, 2 * c + 1), 0);
-    const int end_r = min(max(sload(a.sched, 2 * c + 2), 0), n);
-    const int end_b = max(sload(a.sched, 2 * c + 3), 0);
-
-    while (r0 < n && (r0 < end_r || (r0 == end_r && blk_lo < end_b))) {
-        int g, nblk;
-        piece_at<BKV>(a.rows, r0, g, nblk);
-        const int blk_hi = r0 == end_r ? min(end_b, nblk) : nblk;
-        if (blk_lo < blk_hi) {
-            barrier_lds();  // every wave is done with the previous piece
-            stage_rows(a.q, a.w, r0, g, s_q, s_w);
-            if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
-            barrier_lds();
-            const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
-            const int64_t bt_row = r0 / a.rows.next_n;
-            // this wave's blocks: a contiguous quarter of [blk_lo, blk_hi), so
-            // its block-table entries share scalar-cache lines
-            const int per = (blk_hi - blk_lo) / kCW, rem = (blk_hi - blk_lo) % kCW;
-            const int b0 = blk_lo + wave * per + min(wave, rem);
-            const int nmy = per + (wave < rem ? 1 : 0);
-            // kDepth blocks in flight: step s waits for block s, then requests
-            // block s + kDepth (near the end of the range the last block again,
-            // an L2 hit, so every step has the same loads behind its wait)
-            KeyRegs<FP4, BKV> kb[kBufs];
-            bool okb[kBufs];
-            int mask = 0, col0p = 0;
-            if (nmy > 0) {
-                const int last = nmy - 1;
-#pragma unroll
-                for (int u = 0; u < kDepth; ++u) okb[u] = fetch_block<FP4, BKV>(a, bt_row, b0 + min(u, last), kb[u]);
-                for (int j = 0; j < nmy; j += kBufs) {
-#pragma unroll
-                    for (int u = 0; u < kBufs; ++u) {
-                        if (j + u >= nmy) break;
-                        wave_step<FP4, BKV, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u],
-                                                  b0 + min(j + u + kDepth, last), kb[(u + kDepth) % kBufs],
-                                                  okb[(u + kDepth) % kBufs], s_q, s_w, vis_lane, sl, mask, col0p);
-                    }
-                }
-            }
-            if (nmy > 0) flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
-        }
-        r0 += g;
-        blk_lo = 0;
+    // The workgroup first runs its own chunks [kStaticChunks * c,
+    // kStaticChunks * (c + 1)). The other D = (kChunksPerCU - kStaticChunks) * W
+    // chunks are dealt out from npool counters: pool x holds chunks
+    // kStaticChunks * W + x + npool * t (t < Dx) and serves the Wx workgroups
+    // c with c % npool == x. Every such workgroup draws until it gets a value
+    // t >= Dx, so one call advances the counter by exactly Dx + Wx and the next
+    // call starts where this one ended: t is taken modulo Dx + Wx, and the
+    // counter never needs a reset.
+    const int npool = min(W, kPools);
+    const int x = c % npool;
+    const int D = (kChunksPerCU - kStaticChunks) * W;
+    const unsigned Wx = (unsigned)((W - x + npool - 1) / npool);
+    const unsigned Dx = D > x ? (unsigned)((D - x + npool - 1) / npool) : 0u;
+    Draw dr;
+    dr.ctr = (unsigned long long *)(a.ctr + kPoolStride * x);
+    dr.v = 0;
+    int e0 = kStaticChunks * c, e1 = kStaticChunks * (c + 1);
+    for (int par = 0;; par ^= 1) {
+        dr.done = false;
+        run_chunks<FP4, BKV>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
+        if (!dr.done) dr.issue();
+        if (tid == 0) lds_st<unsigned>(&s_take[par], (unsigned)(dr.v % (Dx + Wx)));
+        barrier_lds();  // (also: every wave is done reading s_take[par ^ 1])
+        const unsigned t = __builtin_amdgcn_readfirstlane(lds_ld<unsigned>(&s_take[par]));
+        if (t >= Dx) break;
+        e0 = kStaticChunks * W + x + npool * (int)t;
+        e1 = e0 + 1;
     }
 
     // -inf past each row's last visible block: rows c, c + W, ...
     for (int r = c; r < n; r += W) {
         const int vis = a.rows.visible_s(r);
         const int start = min((vis + BKV - 1) / BKV * BKV, a.max_ctx);
-        fill_neg_inf(a.out + (int64_t)r * a.out_ld, start, a.max_ctx);
+        fill_neg_inf<kPThreads>(a.out + (int64_t)r * a.out_ld, start, a.max_ctx);
     }
 }
 
 template <bool FP4, int BKV>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV>), dim3(W), dim3(kLThreads), 0, st, a);
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV>), dim3(W), dim3(kPThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
@@ -172,7 +250,7 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
                                         const float *weights, const int32_t *context_lens,
                                         int context_lens_2d, const int32_t *block_table,
                                         int64_t block_table_ld, int block_table_cols,
-                                        const int32_t *schedule, int num_CUs,
+                                        int32_t *schedule, int num_CUs,
                                         const int32_t *indices, int max_ctx, float *logits,
                                         int64_t logits_ld, void *stream) {
     if (num_rows < 0 || next_n < 1 || num_CUs < 1 || max_ctx < 0) return PML_ERR_SHAPE;
@@ -184,13 +262,14 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
     if (num_rows == 0) return PML_OK;
     if (!q || !kv_cache || !weights || !context_lens || !block_table || !schedule || !logits)
         return PML_ERR_NULL;
+    if (paged_mqa_logits_schedule_rows(num_CUs) < 0) return PML_ERR_SHAPE;
     if (num_pages < 1 || block_table_cols < 0 || block_table_ld < block_table_cols)
         return PML_ERR_STRIDE;
     const int64_t pb = kv_format == PML_KV_FP8 ? (int64_t)block_kv * (head_dim + 4)
                                                : (int64_t)block_kv * (head_dim / 2 + head_dim / 32);
     if (page_stride_bytes < pb || page_stride_bytes % 16 != 0) return PML_ERR_STRIDE;
     if (logits_ld < max_ctx || logits_ld % 4 != 0) return PML_ERR_STRIDE;
-    if (!al16(q) || !al16(kv_cache) || !al16(weights) || !al16(logits)) return PML_ERR_ALIGN;
+    if (!al16(q) || !al16(kv_cache) || !al16(weights) || !al16(logits) || !al16(schedule)) return PML_ERR_ALIGN;
     pml::PagedArgs a;
     a.q = (const uint8_t *)q;
     a.w = weights;
@@ -202,6 +281,7 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
     a.bt_ld = block_table_ld;
     a.bt_cols = block_table_cols;
     a.sched = schedule;
+    a.ctr = schedule + 2 * (pml::kChunksPerCU * num_CUs + 1);
     a.max_ctx = max_ctx;
     a.out = logits;
     a.out_ld = logits_ld;

@@ -17,7 +17,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kGMax = 8;        // rows of one piece scored against a shared key block
-constexpr int kCostBase = 1;    // schedule weight of a block: kCostBase + rows
+constexpr int kCostBase = 2;    // schedule weight of a block: kCostBase + rows
+constexpr int kChunksPerCU = 8;   // schedule chunks per logits workgroup
+constexpr int kStaticChunks = 7;  // of which each workgroup's own run covers this many
+constexpr int kPools = 8;                 // counters the remaining chunks are handed out from
+constexpr int kPoolStride = 32;           // int32 between counters (one 128-byte line each)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
@@ -95,6 +99,12 @@ __device__ __forceinline__ void dma16(const void *gsrc, void *lds_wave_base) {
 // 4 bytes per lane from global memory straight into LDS (lane i at +4 i).
 __device__ __forceinline__ void dma4(const void *gsrc, void *lds_wave_base) {
     __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
+}
+
+// D = A(16x128 fp8) * B(128x16 fp8), fresh accumulator (unscaled opcode).
+__device__ __forceinline__ v4f mfma_fp8(const v8i &a, const v8i &b) {
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
 }
 
 // D = A(16x128 fp8, e8m0 scale per row and 32-block of k) * B(128x16 fp8 when

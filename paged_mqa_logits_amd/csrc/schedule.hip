@@ -1,19 +1,25 @@
-// paged_mqa_logits_metadata: split (row-piece, key-block) units over the
-// persistent workgroups of the paged-logits kernel.
+// paged_mqa_logits_metadata: split (row-piece, key-block) units into chunks
+// that the persistent workgroups of the paged-logits kernel take in turn.
 //
-// The pages fix only that the schedule has one entry per persistent worker plus
-// one and that a row slice needs its own ("vllm.model_executor.layers.
+// The pages fix only that the schedule is sized by the number of persistent
+// workers and that a row slice needs its own ("vllm.model_executor.layers.
 // sparse_attn_indexer", _varlen_decode_rows). Content (this library's): units
 // are ordered by piece then block; a block of a piece with g rows costs
-// kCostBase + g; worker c starts at the unit holding cost offset
-// floor(c * T / W) of the total T and entry W is (num_rows, 0).
+// kCostBase + g. The work is cut into C = kChunksPerCU * num_CUs chunks:
+// chunk c starts at the unit holding cost offset floor(c * T / C) of the
+// total T, and entry C is (num_rows, 0). After it come kPools 64-bit work
+// counters of the logits call, one per 128-byte line, set to zero here.
+// Logits workgroup w first runs chunks [kStaticChunks * w, kStaticChunks *
+// (w + 1)) as one range; the remaining chunks are handed out through the
+// counters, so a workgroup that runs slow (on a compute unit shared with heavy
+// work, say) takes fewer of them.
 //
-// One workgroup of 1024 threads walks the rows in chunks of 1024: every
+// One workgroup of 1024 threads walks the rows in tiles of 1024: every
 // thread loads its row's visible length and group-end flag into LDS (plus a
 // halo of kGMax rows), a max-scan finds each row's group start, the thread of
 // a piece's first row reads the piece's rows and extent from LDS, and a
-// sum-scan of the piece costs gives each piece's offset; the thread of a
-// piece then writes the entries of the workers whose start falls inside it.
+// sum-scan of the piece costs gives each piece's offset, and each chunk that
+// starts in the tile finds its piece by a binary search over those offsets.
 // Up to 1024 rows take one walk; more take two (the total first).
 #include "rows.h"
 
@@ -21,7 +27,7 @@ namespace pml {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / kWave;
-constexpr int kHalo = kGMax;  // rows past a chunk that a piece starting in it may cover
+constexpr int kHalo = kGMax;  // rows past a tile that a piece starting in it may cover
 
 // Block-wide inclusive scan: wave shuffles, then one pass over the wave totals.
 template <typename T, typename Op>
@@ -43,6 +49,8 @@ __device__ __forceinline__ T block_scan_incl(T x, T *s_w, Op op, T ident) {
 struct SchedShared {
     int vis[kSchedThreads + kHalo];    // visible length of rows base + i
     int last[kSchedThreads + kHalo];   // row base + i ends its group (or is past the end)
+    long long incl[kSchedThreads];     // cost of the pieces before row base + i + 1 (all tiles)
+    int gs[kSchedThreads];             // rows of the piece starting at row base + i
     int wi[kSchedWaves];
     long long wl[kSchedWaves];
     int run_carry;
@@ -50,8 +58,8 @@ struct SchedShared {
 };
 
 // Cost of the piece starting at row base + tid (0 if no piece starts there)
-// and its row count, for the chunk of rows starting at base.
-__device__ __forceinline__ long long chunk_cost(const RowView &v, int block_kv, int base, SchedShared &sh, int &g) {
+// and its row count, for the tile of rows starting at base.
+__device__ __forceinline__ long long tile_cost(const RowView &v, int block_kv, int base, SchedShared &sh, int &g) {
     const int tid = threadIdx.x;
     const int n = v.num_rows;
     for (int i = tid; i < kSchedThreads + kHalo; i += kSchedThreads) {
@@ -89,26 +97,45 @@ __device__ __forceinline__ long long chunk_cost(const RowView &v, int block_kv, 
     return cost;
 }
 
-// Entries of the workers whose start offset floor(c * T / W) falls inside
-// [cum, cum + cost), the piece starting at row r with g rows.
-__device__ __forceinline__ void write_entries(int32_t *sched, int W, long long total, long long cum, long long cost,
-                                              int r, int g) {
-    long long c = (cum * W + total - 1) / total;
-    long long c_hi = ((cum + cost) * W + total - 1) / total - 1;
-    if (c_hi > W - 1) c_hi = W - 1;
-    if (c > c_hi) return;
-    // t = floor(c * T / W), stepped without a division per entry
-    const long long dq = total / W, dr = total % W;
-    long long t = c * total / W, rem = c * total % W;
-    for (; c <= c_hi; ++c) {
-        sched[2 * c] = r;
-        sched[2 * c + 1] = (int)((t - cum) / (kCostBase + g));
-        t += dq;
-        rem += dr;
-        if (rem >= W) {
-            rem -= W;
-            ++t;
+// Start offset of chunk c: floor(c * T / C) = c * qC + floor(c * rC / C)
+// with T = qC * C + rC, so no product passes 2^63 (c <= C <= 2^23).
+__device__ __forceinline__ long long chunk_start(long long c, long long qC, long long rC, int C) {
+    return c * qC + c * rC / C;
+}
+
+// First chunk c whose start offset is at least x (0 <= x <= T): a double
+// estimate of x * C / T, then exact steps (at most a couple).
+__device__ __forceinline__ long long first_chunk_at(long long x, long long T, long long qC, long long rC, int C) {
+    long long c = (long long)((double)x * (double)C / (double)T);
+    c = c < 0 ? 0 : (c > C ? C : c);
+    while (c > 0 && chunk_start(c - 1, qC, rC, C) >= x) --c;
+    while (c < C && chunk_start(c, qC, rC, C) < x) ++c;
+    return c;
+}
+
+// Entries of the chunks that start inside this tile, whose pieces cost
+// [carry, carry + tile_total) of the total T. Chunk c starts at offset
+// t = chunk_start(c); the piece holding t starts at the first row whose
+// running cost sh.incl exceeds t (a binary search over the tile), and t's
+// block is (t - that piece's start offset) / (kCostBase + g).
+__device__ __forceinline__ void write_tile(int32_t *sched, int C, long long T, long long carry, long long tile_total,
+                                           int base, const SchedShared &sh) {
+    const long long qC = T / C, rC = T % C;
+    const long long lo = first_chunk_at(carry, T, qC, rC, C);
+    const long long hi = first_chunk_at(carry + tile_total, T, qC, rC, C);
+    for (long long c = lo + threadIdx.x; c < hi; c += kSchedThreads) {
+        const long long t = chunk_start(c, qC, rC, C);
+        int l = 0, h = kSchedThreads - 1;
+        while (l < h) {
+            const int m = (l + h) >> 1;
+            if (sh.incl[m] > t)
+                h = m;
+            else
+                l = m + 1;
         }
+        const long long start = l ? sh.incl[l - 1] : carry;
+        sched[2 * c] = base + l;
+        sched[2 * c + 1] = (int)((unsigned)(t - start) / (unsigned)(kCostBase + sh.gs[l]));  // < piece cost < 2^31
     }
 }
 
@@ -121,62 +148,67 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         sh.run_carry = 0;
         sh.cost_carry = 0;
     }
+    if (tid < kPools * kPoolStride) sched[2 * W + 2 + tid] = 0;  // work counters (64-bit) and their padding
     __syncthreads();
+    long long total;
     if (n <= kSchedThreads) {
-        // one chunk: costs, total and entries in a single walk
+        // one tile: costs, total and entries in a single walk
         int g;
-        const long long cost = chunk_cost(v, block_kv, 0, sh, g);
+        const long long cost = tile_cost(v, block_kv, 0, sh, g);
         const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+        sh.incl[tid] = incl;
+        sh.gs[tid] = g;
         if (tid == kSchedThreads - 1) sh.cost_carry = incl;
         __syncthreads();
-        const long long total = sh.cost_carry;
-        if (total == 0) {
-            for (int c = tid; c <= W; c += kSchedThreads) {
-                sched[2 * c] = n;
-                sched[2 * c + 1] = 0;
+        total = sh.cost_carry;
+        if (total > 0) {
+            if (tid == 0) {
+                sched[2 * W] = n;
+                sched[2 * W + 1] = 0;
+            }
+            write_tile(sched, W, total, 0, total, 0, sh);
+            return;
+        }
+    } else {
+        // several tiles: the total first, then the entries
+        for (int base = 0; base < n; base += kSchedThreads) {
+            int g;
+            const long long cost = tile_cost(v, block_kv, base, sh, g);
+            const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+            if (tid == kSchedThreads - 1) sh.cost_carry += incl;
+            __syncthreads();
+        }
+        total = sh.cost_carry;
+        __syncthreads();
+        if (total > 0) {
+            if (tid == 0) {
+                sched[2 * W] = n;
+                sched[2 * W + 1] = 0;
+                sh.run_carry = 0;
+                sh.cost_carry = 0;
+            }
+            __syncthreads();
+            for (int base = 0; base < n; base += kSchedThreads) {
+                int g;
+                const long long cost = tile_cost(v, block_kv, base, sh, g);
+                const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
+                const long long carry = sh.cost_carry;
+                sh.incl[tid] = carry + incl;
+                sh.gs[tid] = g;
+                __syncthreads();
+                const long long tile_total = sh.incl[kSchedThreads - 1] - carry;
+                write_tile(sched, W, total, carry, tile_total, base, sh);
+                __syncthreads();
+                if (tid == kSchedThreads - 1) sh.cost_carry = carry + tile_total;
+                __syncthreads();
             }
             return;
         }
-        if (tid == 0) {
-            sched[2 * W] = n;
-            sched[2 * W + 1] = 0;
-        }
-        if (cost > 0) write_entries(sched, W, total, incl - cost, cost, tid, g);
-        return;
     }
-    // several chunks: the total first, then the entries
-    for (int base = 0; base < n; base += kSchedThreads) {
-        int g;
-        const long long cost = chunk_cost(v, block_kv, base, sh, g);
-        const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
-        if (tid == kSchedThreads - 1) sh.cost_carry += incl;
-        __syncthreads();
-    }
-    const long long total = sh.cost_carry;
-    __syncthreads();
-    if (total == 0) {
-        for (int c = tid; c <= W; c += kSchedThreads) {
-            sched[2 * c] = n;
-            sched[2 * c + 1] = 0;
-        }
-        return;
-    }
-    if (tid == 0) {
-        sched[2 * W] = n;
-        sched[2 * W + 1] = 0;
-        sh.run_carry = 0;
-        sh.cost_carry = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base < n; base += kSchedThreads) {
-        int g;
-        const long long cost = chunk_cost(v, block_kv, base, sh, g);
-        const long long incl = block_scan_incl(cost, sh.wl, ladd, 0LL);
-        const long long carry = sh.cost_carry;
-        if (cost > 0) write_entries(sched, W, total, carry + incl - cost, cost, base + threadIdx.x, g);
-        __syncthreads();
-        if (tid == kSchedThreads - 1) sh.cost_carry = carry + incl;
-        __syncthreads();
+    // nothing to score: every entry is the end
+    for (int c = tid; c <= W; c += kSchedThreads) {
+        sched[2 * c] = n;
+        sched[2 * c + 1] = 0;
     }
 }
 
@@ -187,13 +219,20 @@ extern "C" int paged_mqa_logits_metadata(const int32_t *context_lens, int num_ro
                                          int block_kv, int num_CUs, int32_t *schedule,
                                          void *stream) {
     if (!schedule) return PML_ERR_NULL;
+    if ((uintptr_t)schedule % 16) return PML_ERR_ALIGN;
     if (num_rows < 0 || next_n < 1 || num_CUs < 1) return PML_ERR_SHAPE;
     if (num_rows > 0 && !context_lens) return PML_ERR_NULL;
     if (num_rows % next_n != 0) return PML_ERR_SHAPE;
     if (indices && next_n != 1) return PML_ERR_VARLEN_NEXT_N;
     if (block_kv != 32 && block_kv != 64) return PML_ERR_BLOCK_KV;
+    if (paged_mqa_logits_schedule_rows(num_CUs) < 0) return PML_ERR_SHAPE;
     pml::RowView v{context_lens, indices, context_lens_2d ? 1 : 0, next_n, num_rows};
     hipLaunchKernelGGL(pml::schedule_kernel, dim3(1), dim3(pml::kSchedThreads), 0,
-                       (hipStream_t)stream, v, block_kv, num_CUs, schedule);
+                       (hipStream_t)stream, v, block_kv, pml::kChunksPerCU * num_CUs, schedule);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
+}
+
+extern "C" int paged_mqa_logits_schedule_rows(int num_CUs) {
+    if (num_CUs < 1 || num_CUs > (1 << 20)) return -1;
+    return pml::kChunksPerCU * num_CUs + 1 + pml::kPools * pml::kPoolStride / 2;
 }

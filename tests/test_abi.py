@@ -30,6 +30,19 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
 
 
+def test_schedule_rows():
+    L = pml.lib()
+    for W in (1, 7, 512, 1 << 20):
+        assert L.paged_mqa_logits_schedule_rows(W) == 8 * W + 129
+        assert pml.schedule_rows(W) == 8 * W + 129
+    for W in (0, -3, (1 << 20) + 1):
+        assert L.paged_mqa_logits_schedule_rows(W) == -1
+    import torch
+    assert pml.schedule_workers(torch.empty(pml.schedule_rows(37), 2)) == 37
+    with pytest.raises(ValueError):
+        pml.schedule_workers(torch.empty(pml.schedule_rows(37) + 1, 2))
+
+
 def test_status_strings_and_version():
     assert pml.status_string(0) == "ok"
     for code in range(1, 12):
@@ -51,13 +64,13 @@ def _paged(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(H=32), 2), (dict(D=64), 2), (dict(rows=-1), 2), (dict(cus=0), 2),
+    (dict(H=32), 2), (dict(D=64), 2), (dict(rows=-1), 2), (dict(cus=0), 2), (dict(cus=(1 << 20) + 1), 2),
     (dict(fmt=2), 9), (dict(bkv=16), 3), (dict(idx=FAKE, next_n=2, rows=4), 4),
     (dict(rows=5, next_n=2), 2), (dict(q=None), 1), (dict(bt=None), 1),
     (dict(stride=64 * 132 - 16), 5), (dict(stride=64 * 132 + 4), 5), (dict(ld=500), 5),
     (dict(ld=514, max_ctx=513), 5), (dict(pages=0), 5), (dict(bt_cols=9), 5),
     (dict(fmt=1, bkv=32, stride=32 * 68 - 16), 5),
-    (dict(q=P(0x1001)), 6), (dict(out=P(0x1004)), 6),
+    (dict(q=P(0x1001)), 6), (dict(out=P(0x1004)), 6), (dict(sched=P(0x1008)), 6),
 ])
 def test_paged_validation(kw, code):
     assert _paged(**kw) == code
@@ -74,4 +87,6 @@ def test_metadata_validation():
     assert f(FAKE, 4, 2, 0, FAKE, 64, 4, FAKE, None) == 4
     assert f(FAKE, 5, 2, 0, None, 64, 4, FAKE, None) == 2
     assert f(FAKE, 4, 1, 0, None, 64, 0, FAKE, None) == 2
+    assert f(FAKE, 4, 1, 0, None, 64, (1 << 20) + 1, FAKE, None) == 2
     assert f(None, 4, 1, 0, None, 64, 4, FAKE, None) == 1
+    assert f(FAKE, 4, 1, 0, None, 64, 4, P(0x1008), None) == 6

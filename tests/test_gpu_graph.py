@@ -22,7 +22,7 @@ def test_captured_step_matches_eager_on_every_replay():
     t = G.upload(case)
     u = G.upload(other)
     W = pml.default_num_workers()
-    sched = torch.empty(W + 1, 2, dtype=torch.int32, device=d)
+    sched = torch.empty(pml.schedule_rows(W), 2, dtype=torch.int32, device=d)
     logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
     topk = torch.empty(case.rows, 64, dtype=torch.int32, device=d)
 

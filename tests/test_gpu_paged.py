@@ -27,8 +27,11 @@ def _sched_case(lens, next_n, indices, bkv, W, lens_2d=False):
     it = None if indices is None else torch.as_tensor(np.asarray(indices), dtype=torch.int32).to(d)
     got = pml.paged_mqa_logits_metadata(lt, bkv, W, indices=it, next_n=next_n).cpu().numpy()
     rows = lt.numel() if (lens_2d or indices is not None or next_n == 1) else lt.numel() * next_n
-    want = spec.schedule(np.asarray(lens), rows, next_n, lens_2d, indices, bkv, W)
-    np.testing.assert_array_equal(got, want)
+    C = 8 * W  # chunks
+    assert pml.schedule_rows(W) == C + 129
+    want = spec.schedule(np.asarray(lens), rows, next_n, lens_2d, indices, bkv, C)
+    np.testing.assert_array_equal(got[: C + 1], want)
+    assert not got[C + 1:].any()  # work counters start at zero
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -140,6 +143,35 @@ def test_grouping_and_worker_count_do_not_change_bits():
         np.testing.assert_array_equal(G.run_paged(case, t, num_cus=W), base)
 
 
+def test_schedule_reuse_across_calls():
+    """One schedule serves call after call (every layer of a step): its chunk
+    entries stay as the metadata call wrote them, each logits call advances
+    the work counters by the same amount, and the logits are the same bits."""
+    case = syn.make_paged_case([9000, 4100, 700, 12000], [3, 1, 6, 2], seed=520, max_ctx=12288)
+    t = G.upload(case)
+    G.banner("work counters: reuse of one schedule")
+    W = 37
+    C = 8 * W
+    sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, W, indices=t["indices"])
+    entries = sched[: C + 1].clone()
+    ctr0 = sched[C + 1:].clone().view(torch.int64)
+    assert not ctr0.any()
+    outs, ctrs = [], []
+    for _ in range(3):
+        out = torch.full((case.rows, pml.logits_ld(case.max_ctx)), G.SENTINEL, dtype=torch.float32, device=G.dev())
+        pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx, t["indices"],
+                                     kv_format=case.kv_format, block_kv=case.block_kv, logits=out)
+        torch.cuda.synchronize()
+        assert torch.equal(sched[: C + 1], entries), "chunk entries changed by the logits call"
+        ctrs.append(sched[C + 1:].clone().view(torch.int64).cpu())
+        outs.append(out[:, : case.max_ctx].cpu().numpy())
+    assert ctrs[0].any()
+    assert torch.equal(ctrs[1], 2 * ctrs[0]) and torch.equal(ctrs[2], 3 * ctrs[0])
+    G.assert_logits_close(outs[0], oracle.paged_logits(case), case.weights)
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
 def test_plain_decode_equals_varlen_arange():
     ctx = [5000, 17, 640, 2049]
     a = syn.make_paged_case(ctx, [1] * 4, seed=510, varlen=False, next_n=1, max_ctx=5120)
@@ -210,7 +242,7 @@ def test_no_rows_is_a_no_op():
     d = G.dev()
     lens = torch.zeros(0, dtype=torch.int32, device=d)
     sched = pml.paged_mqa_logits_metadata(lens, 64, 8)
-    assert sched.cpu().numpy().tolist() == [[0, 0]] * 9
+    assert sched.cpu().numpy().tolist() == [[0, 0]] * pml.schedule_rows(8)
     out = pml.fp8_fp4_paged_mqa_logits(torch.zeros(0, 64, 128, dtype=torch.uint8, device=d),
                                        torch.zeros(1, 64 * 132, dtype=torch.uint8, device=d),
                                        torch.zeros(0, 64, device=d), lens,

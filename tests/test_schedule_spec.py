@@ -1,5 +1,5 @@
 """The work-split specification covers every (piece, block) unit exactly once
-and balances cost across workers (CPU only; brute-force enumeration)."""
+and balances cost across chunks (CPU only; brute-force enumeration)."""
 import numpy as np
 import pytest
 
@@ -19,7 +19,7 @@ def _check(lens, num_rows, next_n, lens_2d, indices, bkv, W):
     total = sum(t[3] for t in table)
     unit_cost = {s: S.COST_BASE + g for s, g, nblk, cost in table}
     for c in range(W):
-        units = S.units_of_worker(sched, table, c)
+        units = S.units_of_chunk(sched, table, c)
         seen += units
         load = sum(unit_cost[s] for s, b in units)
         assert load <= total / W + S.COST_BASE + S.G_MAX + 1e-9
@@ -43,7 +43,7 @@ def test_hand_example():
     table = S.piece_table(lens, 4, 1, False, idx, 64)
     assert table == [(0, 3, 3, 3 * (S.COST_BASE + 3)), (3, 1, 1, S.COST_BASE + 1)]
     sched = _check(lens, 4, 1, False, idx, 64, 2)
-    # total = 21 + 5 = 26; worker 1 starts at offset 13 -> piece 0, block 13 // 7 = 1
+    # (COST_BASE 2) total = 15 + 3 = 18; chunk 1 starts at offset 9 -> piece 0, block 9 // 5 = 1
     assert sched.tolist() == [[0, 0], [0, 1], [4, 0]]
 
 
