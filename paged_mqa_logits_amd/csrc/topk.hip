@@ -16,8 +16,11 @@
 //    row is contiguous), and the regions are packed together. Any key outside
 //    the list is then below every key in it, so if the list holds at least k
 //    keys the top k are among them and the selection finishes in the list.
-//    One CU streams a row at only ~25 GB/s, which is why the row is read
-//    about 1.1 times rather than three.
+//    The row is read about 1.1 times rather than three. The pass is bound by
+//    instruction issue, one row per CU: when the bucket lies above -inf its
+//    test is one float compare per element, every element is stored without
+//    a branch (non-candidates to a spare slot per lane), and order keys are
+//    formed only for the list, when the regions are packed.
 //  * Narrower rows, and rows where the sample misjudges (fewer than k
 //    candidates, or a region overflows), take the exact streaming passes: a
 //    full histogram fixes b, then every wave counts, then appends, the
@@ -133,33 +136,66 @@ struct TopkArgs {
     int64_t out_ld;
 };
 
-// Position-ordered float4 walk of one wave's share [q0, q1) of the row's 16-B
-// groups; f(p, key, valid) is called for the 4 elements of every group in
-// position order across the wave (j, lane, e).
+// Float4 walk of one wave's share [q0, q1) of the row's 16-B groups:
+// f(q, x, all_in) gets every group index q (lanes at or past q1 included: they
+// must check q < q1, unless the wave-uniform all_in says the whole round lies
+// below q1) with its 4 values, in position order across the wave (round, j,
+// lane).
+//
+// Two register buffers of kUnroll groups per lane alternate: the next round's
+// loads are issued before the current round is processed, so a wave always
+// has a round in flight. Loads are unconditional, with addresses clamped to
+// the share's last group, which keeps the compiler's wait counts exact:
+// processing a round waits for that round only.
+template <typename F>
+__device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int q1, F &&f) {
+    if (q0 >= q1) return;
+    const int lane = lane_id();
+    const int qlast = q1 - 1;
+    constexpr int kStep = kWave * kUnroll;
+    auto load = [&](v4f *x, int g) {
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            x[j] = *(const v4f *)(rowbase + 4 * (int64_t)min(g + j * kWave + lane, qlast));
+    };
+    auto process = [&](const v4f *x, int g) {
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) f(g + j * kWave + lane, x[j], g + kStep <= q1);
+    };
+    v4f xa[kUnroll], xb[kUnroll];
+    load(xa, q0);
+    for (int g = q0;; g += 2 * kStep) {
+        load(xb, g + kStep);
+        process(xa, g);
+        if (g + kStep >= q1) break;
+        load(xa, g + 2 * kStep);
+        process(xb, g + kStep);
+        if (g + 2 * kStep >= q1) break;
+    }
+}
+
+// The same walk with order keys and validity: f(p, key, valid) for the 4
+// elements at positions p .. p + 3.
 template <typename F>
 __device__ __forceinline__ void wave_walk(const float *rowbase, int lo, int hi, int q0, int q1, F &&f) {
-    const int lane = lane_id();
-    for (int g = q0; g < q1; g += kWave * kUnroll) {
-        v4f x[kUnroll];
+    wave_walk_raw(rowbase, q0, q1, [&](int q, const v4f &x, bool) {
+        uint32_t key[4];
+        bool ok[4];
 #pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int q = g + j * kWave + lane;
-            x[j] = q < q1 ? *(const v4f *)(rowbase + 4 * (int64_t)q) : v4f{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 4; ++e) {
+            const int p = 4 * q + e;
+            ok[e] = q < q1 && p >= lo && p < hi;
+            key[e] = order_key(x[e]);
         }
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-            const int q = g + j * kWave + lane;
-            uint32_t key[4];
-            bool ok[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int p = 4 * q + e;
-                ok[e] = q < q1 && p >= lo && p < hi;
-                key[e] = order_key(x[j][e]);
-            }
-            f(4 * q, key, ok);
-        }
-    }
+        f(4 * q, key, ok);
+    });
+}
+
+// Float whose order key is `prefix`, for prefix >= 0x00800000 (above the key of
+// -inf): for every non-NaN f, order_key(f) >= prefix exactly when f >= it
+// (-0 and +0 compare equal both ways; NaN fails both tests).
+__device__ __forceinline__ float key_floor_float(uint32_t prefix) {
+    return (prefix & 0x80000000u) ? __uint_as_float(prefix & 0x7fffffffu) : __uint_as_float(~prefix);
 }
 
 template <int NT>
@@ -253,26 +289,65 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         // the bucket of the t-th largest sampled key, t = 1.5 k / kSampleDiv + 16
         pick_bin<NT>(s_hist, kBins, (uint32_t)(3 * k) / (2 * kSampleDiv) + 16, s_wave, s_pick);
         const uint32_t sprefix = s_pick[0] << 21;
-        // one pass: ordered append into the wave's region [wave * RCAP, +RCAP)
+        // one pass: ordered append into the wave's region [wave * RCAP, +RCAP).
+        // Above the key of -inf the bucket test is one float compare per
+        // element; keys are formed only for the (few) candidates.
         uint32_t cnt = 0;
-        wave_walk(rowbase, lo, hi, wq0, wq1, [&](int p0, const uint32_t *key, const bool *ok) {
-            uint32_t c = 0;
+        const bool raw = sprefix >= 0x00800000u;  // the list holds float bits until the pack
+        if (raw) {
+            // Branch-free: every element is stored, a candidate at its slot of
+            // the region and any other element at this lane's spare slot in the
+            // (now idle) histogram; the order keys are formed in the pack.
+            const float tf = key_floor_float(sprefix);
+            const uint32_t spare = (uint32_t)tid;
+            const int qa = (lo + 3) >> 2, qb = hi >> 2;  // groups [qa, qb) lie inside [lo, hi)
+            wave_walk_raw(rowbase, wq0, wq1, [&](int q, const v4f &x, bool all_in) {
+                const int p0 = 4 * q;
+                bool c[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) c += (ok[e] && key[e] >= sprefix) ? 1u : 0u;
-            uint32_t pre, tot;
-            wave_prefix4(c, pre, tot);
-            uint32_t at = cnt + pre;
+                for (int e = 0; e < 4; ++e) c[e] = x[e] >= tf;
+                // wave-uniform: do all 64 groups of this step lie inside the row and the share?
+                const int qw = __builtin_amdgcn_readfirstlane(q - lane);
+                if (!(all_in && qw >= qa && qw + kWave <= qb)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (ok[e] && key[e] >= sprefix) {
-                    if (at < (uint32_t)RCAP) {
-                        s_key[wave * RCAP + at] = key[e];
-                        s_pos[wave * RCAP + at] = p0 + e - lo;
-                    }
-                    ++at;
+                    for (int e = 0; e < 4; ++e) c[e] = c[e] && q < wq1 && p0 + e >= lo && p0 + e < hi;
                 }
-            cnt += tot;
-        });
+                const uint32_t cc = (uint32_t)c[0] + (uint32_t)c[1] + (uint32_t)c[2] + (uint32_t)c[3];
+                uint32_t pre, tot;
+                wave_prefix4(cc, pre, tot);
+                uint32_t at = cnt + pre;
+                const bool room = cnt + tot <= (uint32_t)RCAP;  // wave-uniform: no slot of this step overflows
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool w = c[e] && (room || at < (uint32_t)RCAP);
+                    uint32_t *kd = w ? &s_key[wave * RCAP + at] : &s_hist[spare];
+                    int32_t *pd = w ? &s_pos[wave * RCAP + at] : (int32_t *)&s_hist[NT + spare];
+                    *kd = __float_as_uint(x[e]);
+                    *pd = p0 + e - lo;
+                    at += c[e];
+                }
+                cnt += tot;
+            });
+        } else {
+            wave_walk(rowbase, lo, hi, wq0, wq1, [&](int p0, const uint32_t *key, const bool *ok) {
+                uint32_t c = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c += (ok[e] && key[e] >= sprefix) ? 1u : 0u;
+                uint32_t pre, tot;
+                wave_prefix4(c, pre, tot);
+                uint32_t at = cnt + pre;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (ok[e] && key[e] >= sprefix) {
+                        if (at < (uint32_t)RCAP) {
+                            s_key[wave * RCAP + at] = key[e];
+                            s_pos[wave * RCAP + at] = p0 + e - lo;
+                        }
+                        ++at;
+                    }
+                cnt += tot;
+            });
+        }
         if (lane == 0) s_wcnt[wave] = cnt;
         __syncthreads();
         uint32_t base = 0, total = 0, over = 0;
@@ -292,6 +367,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                 const uint32_t i = lane + u * kWave;
                 if (i < cnt) {
                     kv[u] = s_key[wave * RCAP + i];
+                    if (raw) kv[u] = order_key(__uint_as_float(kv[u]));
                     pv[u] = s_pos[wave * RCAP + i];
                 }
             }

@@ -128,6 +128,36 @@ def test_sampled_path_rows():
     _shared_input_check(L, np.full(n, W), 2048, ks=ks)
 
 
+def test_sampled_path_float_threshold():
+    """The sampled append tests candidates with one float compare against the
+    float whose order key opens the picked bucket. Rows where that bucket lies
+    among negative values, exactly at +-0, among subnormals, or at or below
+    -inf (where the key compare is kept) must select exactly as the oracle."""
+    rng = np.random.default_rng(850)
+    W = 70000
+    rows = [-np.abs(rng.standard_normal(W)) - 1.0]          # all negative: bucket among negatives
+    r = rng.standard_normal(W)
+    r[r > 0] = 0.0
+    r[rng.random(W) < 0.5] *= -1.0                           # many +0 / -0 at the top
+    rows.append(r)
+    rows.append(rng.standard_normal(W) * 1e-39)              # subnormals
+    r = np.full(W, -np.inf)
+    r[::50] = rng.standard_normal(W // 50 + 1)[: len(r[::50])]  # 1400 finite values, the rest -inf
+    rows.append(r)
+    r = rng.standard_normal(W)
+    r[rng.random(W) < 0.7] = np.nan                          # NaN-heavy
+    rows.append(r)
+    r = -np.abs(rng.standard_normal(W)) * 1e30
+    r[::3] = -np.inf                                         # huge negatives and -inf
+    rows.append(r)
+    L = np.stack(rows)
+    n = L.shape[0]
+    G.banner("top-k sampled path, float threshold cases")
+    for k in (1, 64, 2048, 4096):
+        _shared_input_check(L, [W] * n, k)
+    _shared_input_check(L, [W, 69999, 65536, W, 66001, 68000], 1500)
+
+
 def _acceptance(gpu: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray, k: int, wsum: np.ndarray):
     for r in range(gpu.shape[0]):
         n = max(0, int(hi[r] - lo[r]))
