@@ -111,7 +111,7 @@ template <int NTH = kLThreads>
 __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int64_t r0, int g, uint8_t *s_q,
                                            float *s_w) {
     constexpr int kChunks = kQBytes / 16;               // 16-B chunks per row
-    constexpr int kPer = kGMax * kChunks / NTH;         // chunks per thread, at most
+    constexpr int kPer = (kGMax * kChunks + NTH - 1) / NTH;  // chunks per thread, at most
     constexpr int kWPer = (kGMax * PML_HEADS + NTH - 1) / NTH;
     const int tid = threadIdx.x;
     const int nchunk = g * kChunks;
