@@ -4,7 +4,8 @@
 // tensor whose size the prefill chunking bounds, sparse_attn_indexer page,
 // forward_cpu: per-row lengths ke - ks).
 //
-// Grid (x = chunk of kChunk key blocks, y = piece of kGMax consecutive rows).
+// Grid (x = chunk of key blocks, y = piece of kGMax consecutive rows; the chunk
+// is as wide as still gives about kTargetWGs workgroups: whole rows at prefill sizes).
 // A workgroup stages q and w of its rows in LDS; its 4 waves take the chunk's
 // blocks that intersect the union of the rows' key ranges in turn, loading 64
 // keys at a time into VGPRs (three buffers deep) and scoring them with the
@@ -19,7 +20,8 @@
 
 namespace pml {
 
-constexpr int kChunk = 32;  // key blocks per workgroup
+constexpr int kMinChunk = 32;      // key blocks per workgroup, at least
+constexpr int kTargetWGs = 4096;   // workgroups the grid aims for (about 8 per CU, in turn)
 
 struct RaggedArgs {
     const uint8_t *q;
@@ -32,6 +34,7 @@ struct RaggedArgs {
     int M;
     float *out;
     int64_t out_ld;
+    int chunk;  // key blocks per workgroup
 };
 
 // One step of a wave's block loop (see wave_step of the paged kernel); every
@@ -70,7 +73,9 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
     const int tid = threadIdx.x;
     const int wave = uni(tid / kWave);
     const int N = a.N;
-    const int row0 = blockIdx.y * kGMax;
+    // pieces go out last-rows-first: in a causal prefill those see the most
+    // keys, so the longest workgroups start first and the short ones fill the tail
+    const int row0 = (gridDim.y - 1 - blockIdx.y) * kGMax;
     const int g = uni(min(kGMax, a.M - row0));
 
     // the union of the piece's key ranges, as key blocks
@@ -84,8 +89,8 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
         }
     }
     const int nb = (N + BKV - 1) / BKV;
-    const int c0 = blockIdx.x * kChunk;
-    const int c1 = min(c0 + kChunk, nb);
+    const int c0 = blockIdx.x * a.chunk;
+    const int c1 = min(c0 + a.chunk, nb);
     int u_lo = c0, u_hi = c0;  // blocks of this chunk to score
     if (hi_max > lo_min) {
         u_lo = uni(max(lo_min / BKV, c0));
@@ -179,10 +184,20 @@ extern "C" int mqa_logits(const void *q, int M, int num_heads, int head_dim, con
     if (logits_ld < N || logits_ld % 4 != 0) return PML_ERR_STRIDE;
     if (!al16r(q) || !al16r(k) || !al16r(weights) || !al16r(logits)) return PML_ERR_ALIGN;
     if (((uintptr_t)k_scale & 3) != 0) return PML_ERR_ALIGN;
-    pml::RaggedArgs a{(const uint8_t *)q, weights, (const uint8_t *)k, k_scale, N, cu_seqlen_ks,
-                      cu_seqlen_ke, M, logits, logits_ld};
+    // Key chunks per row: as few as give about kTargetWGs workgroups, at least
+    // kMinChunk blocks wide. Few, long workgroups keep the CUs on scoring work;
+    // a grid of many chunks spends its time starting workgroups that only fill
+    // -inf (measured: a causal 32K x 32K prefill took 3.5 ms in 32-block chunks,
+    // 1.3 ms in whole rows).
     const int nb = (N + 63) / 64;
-    const dim3 grid((nb + pml::kChunk - 1) / pml::kChunk, (M + pml::kGMax - 1) / pml::kGMax);
+    const int pieces = (M + pml::kGMax - 1) / pml::kGMax;
+    const int max_chunks = (nb + pml::kMinChunk - 1) / pml::kMinChunk;
+    const int want = (pml::kTargetWGs + pieces - 1) / pieces;
+    const int nchunks = want < max_chunks ? want : max_chunks;
+    const int chunk = (nb + nchunks - 1) / nchunks;
+    pml::RaggedArgs a{(const uint8_t *)q, weights, (const uint8_t *)k, k_scale, N, cu_seqlen_ks,
+                      cu_seqlen_ke, M, logits, logits_ld, chunk};
+    const dim3 grid((nb + chunk - 1) / chunk, pieces);
     if (grid.y > 65535) return PML_ERR_SHAPE;
     hipLaunchKernelGGL(pml::ragged_logits_kernel, grid, dim3(pml::kLThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
