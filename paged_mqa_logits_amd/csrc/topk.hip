@@ -7,6 +7,9 @@
 // One workgroup per row, radix select on an order-preserving 32-bit key (NaN
 // lowest, -0 == +0) followed by an ordered compaction, so positions come out
 // ascending without a sort:
+//  * When every row fits the 8192-entry list (max_width <= 8192) a compact
+//    256-thread kernel reads the row once into LDS and selects there
+//    (topk_small_kernel: 37 KB of LDS, four rows per CU).
 //  * A row that fits the LDS candidate list is read once into it.
 //  * A row of 64K columns or more first takes a sampled pass: a histogram of the top 11 key
 //    bits over one 1-KB chunk in 8 picks a bucket b with a margin (about
@@ -96,25 +99,24 @@ __device__ __forceinline__ void wave_prefix4(uint32_t c, uint32_t &pre, uint32_t
     }
 }
 
-// Find the bin holding the kk-th largest key among s_hist[0, nbins): writes
-// (bin, count of keys in higher bins) to s_pick.
-template <int NT>
-__device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint32_t kk, uint32_t *s_wave,
-                                         uint32_t *s_pick) {
+// Find the bin holding the kk-th largest key among bins [0, nbins) whose
+// counts count(b) gives: writes (bin, count of keys in higher bins) to s_pick.
+template <int NT, typename C>
+__device__ __forceinline__ void pick_bin_by(C count, int nbins, uint32_t kk, uint32_t *s_wave, uint32_t *s_pick) {
     const int per = (nbins + NT - 1) / NT;
     const int t = threadIdx.x;
     // thread t owns bins top - t*per - j, j < per (descending)
     uint32_t own = 0;
     for (int j = 0; j < per; ++j) {
         const int b = nbins - 1 - (t * per + j);
-        if (b >= 0) own += s_hist[b];
+        if (b >= 0) own += count(b);
     }
     uint32_t tot;
     uint32_t above = block_scan<NT>(own, s_wave, &tot) - own;
     for (int j = 0; j < per; ++j) {
         const int b = nbins - 1 - (t * per + j);
         if (b < 0) break;
-        const uint32_t h = s_hist[b];
+        const uint32_t h = count(b);
         if (above < kk && kk <= above + h) {
             s_pick[0] = (uint32_t)b;
             s_pick[1] = above;
@@ -122,6 +124,12 @@ __device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint
         above += h;
     }
     __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint32_t kk, uint32_t *s_wave,
+                                         uint32_t *s_pick) {
+    pick_bin_by<NT>([&](int b) { return s_hist[b]; }, nbins, kk, s_wave, s_pick);
 }
 
 struct TopkArgs {
@@ -520,6 +528,98 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
 }
 
+// Rows of at most CAP columns (max_width <= 8192): the row is read once into
+// LDS as order keys, three radix passes select the k-th key, and one block
+// scan places the selected positions (the list index is the position). Bin
+// counts never pass 8192, so the histogram keeps two 16-bit counters per word;
+// with no position array the workgroup needs 37 KB of LDS and four fit on a CU.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
+    constexpr int NW = NT / kWave;
+    constexpr int CAP = TopkCfg<NT>::CAP;
+    static_assert(CAP < 65536, "16-bit bin counters");
+    __shared__ uint32_t s_hist[kBins / 2];
+    __shared__ uint32_t s_key[CAP];
+    __shared__ uint32_t s_wave[2 * NW];
+    __shared__ uint32_t s_pick[2];
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    int lo = a.ks ? a.ks[r] : 0;
+    int hi;
+    if (a.ks || a.next_n == 1)
+        hi = a.ke[r];
+    else
+        hi = a.ke[r / a.next_n] - a.next_n + (r % a.next_n) + 1;
+    const int64_t ldc = a.ld < 0x7fffffff ? a.ld : 0x7fffffff;
+    lo = (int)min<int64_t>(max(lo, 0), ldc);
+    hi = (int)min<int64_t>(max(hi, lo), ldc);
+    hi = (int)min<int64_t>(hi, (int64_t)lo + min(a.max_width, CAP));
+    const int n = hi - lo;
+    const int k = a.k;
+    int32_t *out = a.out + (int64_t)r * a.out_ld;
+    if (n <= k) {
+        for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
+        return;
+    }
+    const float *row = a.logits + (int64_t)r * a.ld + lo;
+    // 8 loads in flight per thread (addresses clamped into the row)
+    for (int i0 = 0; i0 < n; i0 += 8 * NT) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = row[min(i0 + j * NT + tid, n - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (i0 + j * NT + tid < n) s_key[i0 + j * NT + tid] = order_key(x[j]);
+    }
+    uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 2 ? 1024 : 2048;
+        for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
+        __syncthreads();  // (also publishes the keys before the first pass)
+        for (int i = tid; i < n; i += NT) {
+            const uint32_t key = s_key[i];
+            if ((key & mask) == prefix) {
+                const uint32_t bin = (key >> shift) & (nbins - 1);
+                atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
+            }
+        }
+        __syncthreads();
+        pick_bin_by<NT>([&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; }, nbins, kk, s_wave,
+                        s_pick);
+        prefix |= s_pick[0] << shift;
+        mask |= (uint32_t)(nbins - 1) << shift;
+        kk -= s_pick[1];
+        __syncthreads();
+    }
+    const uint32_t T = prefix;
+    const uint32_t need = kk;  // elements equal to T that are taken (>= 1)
+    // ordered compaction: slot = (# greater before) + min(# equal before, need)
+    const int per = (n + NT - 1) / NT;
+    const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+    uint32_t gt = 0, eq = 0;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t key = s_key[i];
+        gt += key > T;
+        eq += key == T;
+    }
+    uint32_t tot;
+    const uint32_t packed = gt | (eq << 16);
+    const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
+    uint32_t gb = excl & 0xffffu, eb = excl >> 16;
+    for (int i = i0; i < i1; ++i) {
+        const uint32_t key = s_key[i];
+        if (key > T) {
+            out[gb + min(eb, need)] = i;
+            ++gb;
+        } else if (key == T) {
+            if (eb < need) out[gb + eb] = i;
+            ++eb;
+        }
+    }
+}
+
 }  // namespace pml
 
 extern "C" size_t top_k_per_row_workspace_size(int num_rows, int max_width, int k) {
@@ -546,7 +646,7 @@ extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_l
     pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld};
     hipStream_t st = (hipStream_t)stream;
     if (max_width <= pml::TopkCfg<256>::CAP)
-        hipLaunchKernelGGL(pml::topk_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
+        hipLaunchKernelGGL(pml::topk_small_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL(pml::topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
