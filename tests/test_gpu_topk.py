@@ -79,10 +79,11 @@ def test_bounds_and_next_n():
 
 
 def test_wide_rows_streaming_list_and_fallback():
-    """Rows wider than the in-LDS list: the multi-workgroup segments, the
-    in-list path of the wide-row kernel for the narrower rows of the launch,
-    the streaming passes when one segment's candidates overflow its slot, and
-    the passes over the row when ties overflow the list."""
+    """Rows wider than the in-LDS list: the sampled path for rows of 16K+
+    columns, the exact streaming passes for the narrower rows of the launch
+    (10000 .. 12289 wide) and wherever the sample misjudges (ties, one wave's
+    region overflowing), and the passes over the row when ties overflow the
+    list."""
     rng = np.random.default_rng(830)
     W = 40000
     rows = [rng.standard_normal(W),                     # streaming, few candidates
@@ -92,7 +93,7 @@ def test_wide_rows_streaming_list_and_fallback():
             rng.standard_normal(W) * 1e3,
             np.arange(W, dtype=np.float64)]             # ascending: the top is at the end
     r = rng.standard_normal(W)
-    r[17000:19100] = 50.0                               # one segment's candidates overflow its slot
+    r[17000:19100] = 50.0                               # one wave's candidates overflow its region
     rows.append(r)
     L = np.stack(rows)
     G.banner("top-k wide rows")
@@ -104,7 +105,7 @@ def test_wide_rows_streaming_list_and_fallback():
 
 
 def test_sampled_path_rows():
-    """Rows of 64K columns or more: a sampled bucket, then one append pass into
+    """Rows of 16K columns or more: a sampled bucket, then one append pass into
     per-wave regions (fast path); a cluster of large values that overflows one
     wave's region, and heavy ties, fall back to the exact passes."""
     rng = np.random.default_rng(840)
