@@ -8,8 +8,13 @@ same counter reads for a device-to-device copy of known size
 (``bench.py --copy-calibration`` issues one).
 
   python -m paged_mqa_logits_amd.profsum stats  <kernel_stats.csv>
+  python -m paged_mqa_logits_amd.profsum trace  <kernel_trace.csv>
   python -m paged_mqa_logits_amd.profsum pmc    <counter_collection.csv> <counter> <copy_bytes>
   python -m paged_mqa_logits_amd.profsum digest
+
+``trace`` groups the dispatches of a kernel trace by kernel and launch
+shape (grid and workgroup size), so one run over several workloads that share
+kernels still gives each workload's durations.
 
 ``digest`` prints a hash of the decode-logits kernel sources; a traffic
 figure is only valid for the sources it was measured on.
@@ -47,6 +52,23 @@ def kernel_stats(path: str) -> list[dict]:
     return out
 
 
+def trace_by_shape(path: str) -> list[dict]:
+    """Dispatches of a *_kernel_trace.csv grouped by (kernel, grid, workgroup):
+    count and average / min / max duration in us."""
+    groups = defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            grid = tuple(int(r[f"Grid_Size_{a}"]) for a in "XYZ")
+            wg = tuple(int(r[f"Workgroup_Size_{a}"]) for a in "XYZ")
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(r["Kernel_Name"], grid, wg)].append(dur)
+    out = []
+    for (name, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        out.append({"name": name, "grid": grid, "wg": wg, "calls": len(d), "avg_us": sum(d) / len(d),
+                    "min_us": min(d), "max_us": max(d)})
+    return out
+
+
 def counter_means(path: str, counter: str) -> dict[str, tuple[int, float]]:
     """Kernel name -> (dispatches, mean counter value per dispatch) from a counter_collection.csv."""
     per = defaultdict(dict)  # name -> dispatch -> summed value
@@ -77,11 +99,18 @@ def calibrated(path: str, counter: str, copy_bytes: int) -> tuple[float, dict[st
 
 
 def _main(argv: list[str]) -> None:
-    if not argv or argv[0] not in ("stats", "pmc", "digest"):
+    if not argv or argv[0] not in ("stats", "trace", "pmc", "digest"):
         print(__doc__)
         raise SystemExit(2)
     if argv[0] == "digest":
         print(source_digest())
+    elif argv[0] == "trace":
+        print(f"{'kernel':70s} {'grid (threads)':>22s} {'wg':>5s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} "
+              f"{'max_us':>10s}")
+        for r in trace_by_shape(argv[1]):
+            g = "x".join(str(v) for v in r["grid"])
+            print(f"{r['name'][:70]:70s} {g:>22s} {r['wg'][0]:5d} {r['calls']:6d} {r['avg_us']:10.2f} "
+                  f"{r['min_us']:10.2f} {r['max_us']:10.2f}")
     elif argv[0] == "stats":
         print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'time%':>7s}")
         for r in kernel_stats(argv[1]):
