@@ -61,6 +61,14 @@ def _bind(path) -> ctypes.CDLL:
     L.pml_oracle_topk.restype = None
     L.pml_oracle_topk.argtypes = [u8p, ctypes.c_int, ctypes.c_int64, u8p, u8p, ctypes.c_int, u8p]
     L.pml_oracle_num_threads.restype = ctypes.c_int
+    L.pml_oracle_dcp_global_id.restype = ctypes.c_int64
+    L.pml_oracle_dcp_global_id.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.pml_oracle_dcp_pack.restype = None
+    L.pml_oracle_dcp_pack.argtypes = [
+        u8p, ctypes.c_int, ctypes.c_int64, u8p, u8p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, u8p]
+    L.pml_oracle_dcp_merge.restype = None
+    L.pml_oracle_dcp_merge.argtypes = [u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
     return L
 
 
@@ -153,6 +161,36 @@ def topk(scores: np.ndarray, ke, k: int, ks=None) -> np.ndarray:
     if rows:
         lib().pml_oracle_topk(_ptr(s), rows, s.shape[1], None if ks_a is None else _ptr(ks_a),
                               _ptr(ke_a), k, _ptr(out))
+    return out
+
+
+def dcp_global_id(p: int, rank: int, world: int, interleave: int) -> int:
+    """Global token id of local position p on ``rank`` (runs of ``interleave`` tokens dealt in turn)."""
+    return lib().pml_oracle_dcp_global_id(p, rank, world, interleave)
+
+
+def dcp_pack(logits: np.ndarray, topk_local: np.ndarray, rank: int, world: int, interleave: int,
+             ks=None) -> np.ndarray:
+    """One rank's (score, global id) float32 pairs [rows][k][2]; padding is (-inf, -1)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    tk = np.ascontiguousarray(topk_local, dtype=np.int32)
+    rows, k = tk.shape
+    ks_a = None if ks is None else np.ascontiguousarray(ks, dtype=np.int32)
+    out = np.empty((rows, k, 2), dtype=np.float32)
+    if rows and k:
+        lib().pml_oracle_dcp_pack(_ptr(lg), rows, lg.shape[1], None if ks_a is None else _ptr(ks_a),
+                                  _ptr(tk), tk.shape[1], k, rank, world, interleave, _ptr(out))
+    return out
+
+
+def dcp_merge(gathered: np.ndarray, k: int) -> np.ndarray:
+    """Global top-k ids [rows][k] (ascending, -1 padded) from [world][rows][k][2] candidates."""
+    g = np.ascontiguousarray(gathered, dtype=np.float32)
+    world, rows = g.shape[0], g.shape[1]
+    assert g.shape == (world, rows, k, 2)
+    out = np.empty((rows, k), dtype=np.int32)
+    if rows and k:
+        lib().pml_oracle_dcp_merge(_ptr(g), world, rows, k, _ptr(out))
     return out
 
 

@@ -103,3 +103,30 @@ def topk(scores: np.ndarray, ke, k: int, ks=None) -> np.ndarray:
         sel = np.sort(order[:k])
         out[r, : len(sel)] = sel
     return out
+
+
+def dcp_tokens(T: int, world: int, interleave: int) -> list:
+    """Global ids held by each rank, in local order, by dealing runs of ``interleave`` tokens in turn."""
+    held = [[] for _ in range(world)]
+    run, t = 0, 0
+    while t < T:
+        for _ in range(interleave):
+            if t < T:
+                held[run % world].append(t)
+                t += 1
+        run += 1
+    return held
+
+
+def dcp_merge(gathered: np.ndarray, k: int) -> np.ndarray:
+    """lexsort over every rank's valid pairs by (score desc, NaN last, id asc); ids ascending, -1 padded."""
+    world, rows = gathered.shape[0], gathered.shape[1]
+    out = np.full((rows, k), -1, dtype=np.int32)
+    for r in range(rows):
+        pairs = gathered[:, r].reshape(-1, 2).astype(np.float64)
+        ok = (pairs[:, 1] >= 0) & (pairs[:, 1] < 2 ** 24)
+        v, ids = pairs[ok, 0], np.trunc(pairs[ok, 1]).astype(np.int64)
+        order = np.lexsort((ids, -v))
+        sel = np.sort(ids[order[:k]])
+        out[r, : len(sel)] = sel
+    return out

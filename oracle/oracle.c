@@ -278,3 +278,87 @@ int pml_oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* ---- exact merge of per-shard top-k candidates ---------------------------
+ *
+ * Decode context parallelism shards each request's key tokens over `world`
+ * ranks. Every rank scores its shard, takes a local top-k, and ships
+ * (score, global token id) pairs as float32; a stable top-k over all ranks'
+ * candidates gives the global top-k ("vllm.model_executor.layers.
+ * sparse_attn_indexer", _merge_dcp_topk_global). Nothing is lost: a token of
+ * the global top-k has fewer than k tokens ahead of it overall, hence fewer
+ * than k on its own rank, so it is in that rank's local top-k.
+ *
+ * Token placement (a reading: the pages name only the interleave size): runs
+ * of `interleave` consecutive tokens go to ranks 0, 1, ..., world - 1 in turn,
+ * so local position p of rank r holds global token
+ *     (p / interleave) * world * interleave + r * interleave + p % interleave.
+ */
+int64_t pml_oracle_dcp_global_id(int64_t p, int rank, int world, int interleave)
+{
+    return (p / interleave) * (int64_t)world * interleave + (int64_t)rank * interleave + p % interleave;
+}
+
+/* Pack one rank's candidates (the page's pack step). For row r and slot j,
+ * idx = topk[r * topk_ld + j] is a local position relative to the row's
+ * start ks[r] (0 without ks); it is a candidate when 0 <= idx < ld - ks[r],
+ * and then packed[r][j] = (logits[r][ks[r] + idx], global id of idx as a
+ * float). Any other idx (the -1 padding) packs as (-inf, -1).
+ *   packed  float [rows][k][2] */
+void pml_oracle_dcp_pack(const float *logits, int rows, int64_t ld, const int32_t *ks,
+                         const int32_t *topk, int64_t topk_ld, int k, int rank, int world,
+                         int interleave, float *packed)
+{
+    for (int r = 0; r < rows; ++r) {
+        int64_t lo = ks ? ks[r] : 0;
+        for (int j = 0; j < k; ++j) {
+            int64_t idx = topk[(int64_t)r * topk_ld + j];
+            float *o = packed + ((int64_t)r * k + j) * 2;
+            if (idx >= 0 && lo + idx < ld) {
+                o[0] = logits[(int64_t)r * ld + lo + idx];
+                o[1] = (float)pml_oracle_dcp_global_id(idx, rank, world, interleave);
+            } else {
+                o[0] = -INFINITY;
+                o[1] = -1.0f;
+            }
+        }
+    }
+}
+
+/* Stable top-k over the gathered candidates (the page's merge step).
+ *   gathered  float [world][rows][k][2] (score, id), rank-major as the
+ *             all-gather along dim 0 leaves it
+ *   out       int32 [rows][k]
+ * A pair is a candidate when its id field f satisfies 0 <= f < 2^24 (every
+ * integer there is exact in float32); its id is f truncated to an integer.
+ * Candidates are ordered as in pml_oracle_topk (larger score first, NaN after
+ * every number, equal scores by lower id), the first k are kept, and row r
+ * of out holds their ids in ascending order, then -1. */
+void pml_oracle_dcp_merge(const float *gathered, int world, int rows, int k, int32_t *out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < rows; ++r) {
+        int64_t cap = (int64_t)world * k;
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (cap > 0 ? cap : 1));
+        int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (k > 0 ? k : 1));
+        int n = 0;
+        for (int w = 0; w < world; ++w)
+            for (int j = 0; j < k; ++j) {
+                const float *p = gathered + (((int64_t)w * rows + r) * k + j) * 2;
+                if (p[1] >= 0.0f && p[1] < 16777216.0f) {
+                    c[n].v = p[0];
+                    c[n].i = (int32_t)p[1];
+                    ++n;
+                }
+            }
+        qsort(c, n, sizeof(cand_t), cand_cmp);
+        int m = n < k ? n : k;
+        for (int j = 0; j < m; ++j)
+            sel[j] = c[j].i;
+        qsort(sel, m, sizeof(int32_t), idx_cmp);
+        for (int j = 0; j < k; ++j)
+            out[(int64_t)r * k + j] = j < m ? sel[j] : -1;
+        free(c);
+        free(sel);
+    }
+}
