@@ -136,6 +136,52 @@ class RaggedBench:
             ev[3].record()
 
 
+class DcpBench:
+    """One rank's share of a decode step split over `world` context-parallel ranks,
+    after its logits: local top_k_per_row on its 1/world of the columns, the pack
+    into (score, global id) pairs, and the merge of all ranks' gathered pairs
+    (the all-gather itself is not part of one GPU's work)."""
+
+    def __init__(self, case: syn.PagedCase, world: int = 8, interleave: int = 1):
+        d = torch.device("cuda:0")
+        self.world, self.interleave, self.k = world, interleave, case.topk
+        self.rows = case.rows
+        T = case.max_ctx
+        self.local_w = -(-T // world)
+        ld = (self.local_w + 3) // 4 * 4
+        vis = syn.vis_per_row(case)
+        g = torch.Generator(device=d)
+        g.manual_seed(77)
+        self.local = [torch.randn(self.rows, ld, device=d, generator=g) for _ in range(world)]
+        # rank r holds the tokens t < vis with (t // interleave) % world == r
+        ke = []
+        for r in range(world):
+            full_runs = vis // (world * interleave)
+            rem = vis - full_runs * world * interleave
+            n_r = full_runs * interleave + np.clip(rem - r * interleave, 0, interleave)
+            ke.append(torch.from_numpy(n_r.astype(np.int32)).to(d))
+        self.ke = ke
+        self.loc = [pml.top_k_per_row(self.local[r], ke[r], self.k, max_width=self.local_w) for r in range(world)]
+        self.gathered = torch.stack([pml.pack_dcp_topk_candidates(self.local[r], self.loc[r], r, world, interleave)
+                                     for r in range(world)])
+        self.out = torch.empty(self.rows, self.k, dtype=torch.int32, device=d)
+        torch.cuda.synchronize()
+
+    def step(self, i: int, ev=None):
+        if ev:
+            ev[0].record()
+        pml.top_k_per_row(self.local[0], self.ke[0], self.k, max_width=self.local_w, out=self.loc[0])
+        if ev:
+            ev[1].record()
+        pml.pack_dcp_topk_candidates(self.local[0], self.loc[0], 0, self.world, self.interleave,
+                                     out=self.gathered[0])
+        if ev:
+            ev[2].record()
+        pml.stable_topk_from_gathered_candidates(self.gathered, self.k, out=self.out)
+        if ev:
+            ev[3].record()
+
+
 def run_timed(b, steps: int, warmup: int):
     """Warm up, then time exactly `steps` steps; per-kernel times from events."""
     for i in range(warmup):
@@ -300,6 +346,18 @@ def main():
                 w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
             print(json.dumps(paged_summary(name, ob, w2, p2, args.steps)), file=sys.stderr, flush=True)
             del ob
+        print("[bench] dcp_merge_8ranks", file=sys.stderr, flush=True)
+        db = DcpBench(syn.config_varlen_fp8())
+        w2, p2 = run_timed(db, args.steps, args.warmup)
+        t_m = float(p2[:, 2].mean()) * 1e-3
+        mbytes = db.world * db.rows * db.k * 8 + db.rows * db.k * 4
+        print(json.dumps({"workload": "dcp_topk_merge_8ranks_varlen120k", "rows": db.rows, "k": db.k,
+                          "world": db.world, "local_width": db.local_w,
+                          "ms_local_topk": float(p2[:, 0].mean()), "ms_pack": float(p2[:, 1].mean()),
+                          "ms_merge": t_m * 1e3, "merge_bytes": mbytes,
+                          "merge_GBs": mbytes / t_m / 1e9, "merge_hbm_frac": mbytes / t_m / 1e9 / PEAK_HBM_GBS}),
+              file=sys.stderr, flush=True)
+        del db
         print("[bench] ragged_prefill_4x8192", file=sys.stderr, flush=True)
         rb = RaggedBench(syn.config_ragged_prefill())
         w2, p2 = run_timed(rb, max(3, args.steps // 4), 2)

@@ -216,6 +216,58 @@ int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const in
                   const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
                   int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Exact top-k over key tokens sharded across decode-context-parallel ranks
+ * ("vllm.model_executor.layers.sparse_attn_indexer", _merge_dcp_topk_global:
+ * each rank packs its local top-k as (score, global token id) float32 pairs,
+ * the ranks all-gather them along the leading dimension, and a stable top-k
+ * over the gathered pairs gives the global top-k). The merge loses nothing: a
+ * token of the global top-k has fewer than k tokens ahead of it overall, hence
+ * fewer than k on its own rank, so it is in that rank's local top-k.
+ *
+ * Token placement: runs of `interleave` consecutive tokens of a request go to
+ * ranks 0, 1, ..., world - 1 in turn, so local position p of rank r holds
+ * global token (p / interleave) * world * interleave + r * interleave
+ * + p % interleave. (The page names only the interleave size; this is the
+ * library's reading of it.)
+ *
+ * pack_dcp_topk_candidates - one rank's pairs from its local top-k.
+ *   logits      fp32 [num_rows][logits_ld]: this rank's logits.
+ *   row_starts  int32 [num_rows] column of each row's local position 0, or
+ *               NULL (= 0); clamped to [0, logits_ld] as in top_k_per_row.
+ *   topk        int32 [num_rows][topk_ld], topk_ld >= k: local positions as
+ *               top_k_per_row writes them (relative to row_starts, -1 padded).
+ *   rank, world 0 <= rank < world; interleave >= 1.
+ *   packed      fp32 [num_rows][k][2], 8-B aligned: for slot j with local
+ *               position p, 0 <= p < logits_ld - row_start, the pair
+ *               (logits[row][row_start + p], global id of p as a float);
+ *               any other entry packs as (-inf, -1).
+ *   Ids must stay exact in float32: PML_ERR_SHAPE when the global id of local
+ *   position logits_ld - 1 reaches 2^24. k in [1, 4096] (else PML_ERR_K).
+ *
+ * stable_topk_from_gathered_candidates - the merge.
+ *   gathered    fp32 [world][num_rows][k][2], 8-B aligned, rank-major as the
+ *               all-gather leaves it. A pair is a candidate when its id field
+ *               f has 0 <= f < 2^24; its id is f truncated. Candidate ids of a
+ *               row must be distinct (otherwise which duplicates are kept is
+ *               unspecified; at most k ids are still written).
+ *   k           [1, 4096] (else PML_ERR_K); world * k <= 32768 (else
+ *               PML_ERR_SHAPE).
+ *   out         int32 [num_rows][out_ld], out_ld >= k: per row the ids of the
+ *               k best candidates in ascending order, then -1 when the row has
+ *               fewer than k. Order of selection: larger score first (NaN after
+ *               every number, -0.0 equal to +0.0), equal scores by lower id --
+ *               the order of top_k_per_row, so with the placement above the
+ *               merge of every rank's packed top_k_per_row output equals
+ *               top_k_per_row over the unsharded row.
+ */
+int pack_dcp_topk_candidates(const float *logits, int num_rows, int64_t logits_ld,
+                             const int32_t *row_starts, const int32_t *topk, int64_t topk_ld,
+                             int k, int rank, int world, int interleave, float *packed,
+                             void *stream);
+int stable_topk_from_gathered_candidates(const float *gathered, int world, int num_rows, int k,
+                                         int32_t *out, int64_t out_ld, void *stream);
+
 /* Text of a status code (static storage). */
 const char *pml_status_string(int status);
 

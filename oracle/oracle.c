@@ -301,7 +301,8 @@ int64_t pml_oracle_dcp_global_id(int64_t p, int rank, int world, int interleave)
 
 /* Pack one rank's candidates (the page's pack step). For row r and slot j,
  * idx = topk[r * topk_ld + j] is a local position relative to the row's
- * start ks[r] (0 without ks); it is a candidate when 0 <= idx < ld - ks[r],
+ * start ks[r] (0 without ks; clamped to [0, ld]); it is a candidate when
+ * 0 <= idx < ld - ks[r],
  * and then packed[r][j] = (logits[r][ks[r] + idx], global id of idx as a
  * float). Any other idx (the -1 padding) packs as (-inf, -1).
  *   packed  float [rows][k][2] */
@@ -311,6 +312,7 @@ void pml_oracle_dcp_pack(const float *logits, int rows, int64_t ld, const int32_
 {
     for (int r = 0; r < rows; ++r) {
         int64_t lo = ks ? ks[r] : 0;
+        lo = lo < 0 ? 0 : (lo > ld ? ld : lo); /* row starts clamped to [0, ld], as for the top-k */
         for (int j = 0; j < k; ++j) {
             int64_t idx = topk[(int64_t)r * topk_ld + j];
             float *o = packed + ((int64_t)r * k + j) * 2;

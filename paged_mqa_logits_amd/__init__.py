@@ -69,7 +69,11 @@ def lib() -> ctypes.CDLL:
             L.top_k_per_row_workspace_size.argtypes = [I, I, I]
             L.top_k_per_row_workspace_size.restype = SZ
             L.top_k_per_row.argtypes = [P, I, I64, P, P, I, I, I, P, I64, P, SZ, P]
-        for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row"):
+        if hasattr(L, "stable_topk_from_gathered_candidates"):
+            L.pack_dcp_topk_candidates.argtypes = [P, I, I64, P, P, I64, I, I, I, I, P, P]
+            L.stable_topk_from_gathered_candidates.argtypes = [P, I, I, I, P, I64, P]
+        for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
+                     "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates"):
             if hasattr(L, name):
                 getattr(L, name).restype = I
         L.pml_status_string.argtypes = [I]
@@ -266,4 +270,45 @@ def top_k_per_row(logits: torch.Tensor, ke: torch.Tensor, k: int, ks: torch.Tens
     _check(lib().top_k_per_row(_p(logits), rows, logits.stride(0), _p(ks), _p(ke.contiguous()), next_n, k,
                                max_width, _p(out), out.stride(0), _p(workspace), wbytes, _stream()),
            "top_k_per_row")
+    return out
+
+
+def pack_dcp_topk_candidates(logits: torch.Tensor, topk: torch.Tensor, rank: int, world: int, interleave: int,
+                             row_starts: torch.Tensor | None = None, k: int | None = None,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 [rows, k, 2]: this rank's (score, global token id) pairs from its local
+    top-k positions; padding entries become (-inf, -1)."""
+    _dev(logits, "logits", _F32)
+    _dev(topk, "topk", _I32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or topk.dim() != 2 or topk.stride(1) != 1:
+        raise ValueError("logits and topk must be 2-D with unit inner stride")
+    rows = topk.shape[0]
+    if logits.shape[0] != rows:
+        raise ValueError("logits and topk must have the same rows")
+    k = topk.shape[1] if k is None else k
+    if row_starts is not None:
+        row_starts = _dev(row_starts, "row_starts", _I32).contiguous()
+    if out is None:
+        out = torch.empty(rows, max(k, 1), 2, dtype=torch.float32, device=logits.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (rows, k, 2) or out.dtype != torch.float32:
+        raise ValueError("out must be a contiguous fp32 [rows, k, 2] tensor")
+    _check(lib().pack_dcp_topk_candidates(_p(logits), rows, logits.stride(0), _p(row_starts), _p(topk),
+                                          topk.stride(0), k, rank, world, interleave, _p(out), _stream()),
+           "pack_dcp_topk_candidates")
+    return out
+
+
+def stable_topk_from_gathered_candidates(gathered: torch.Tensor, k: int,
+                                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """int32 [rows, k]: ids of the k best (score, id) pairs of each row over all
+    ranks of gathered [world, rows, k, 2], ascending, then -1."""
+    _dev(gathered, "gathered", _F32)
+    if gathered.dim() != 4 or gathered.shape[2] != k or gathered.shape[3] != 2 or not gathered.is_contiguous():
+        raise ValueError("gathered must be a contiguous fp32 [world, rows, k, 2] tensor")
+    world, rows = gathered.shape[0], gathered.shape[1]
+    if out is None:
+        out = torch.empty(rows, max(k, 1), dtype=torch.int32, device=gathered.device)
+    _check(lib().stable_topk_from_gathered_candidates(_p(gathered), world, rows, k, _p(out), out.stride(0),
+                                                      _stream()),
+           "stable_topk_from_gathered_candidates")
     return out

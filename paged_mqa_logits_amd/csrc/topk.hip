@@ -32,19 +32,12 @@
 //    block scan over it places every selected element.
 //  * If the candidates overflow the list (heavy ties), the selection finishes
 //    with passes over the row itself.
-#include "pml_device.h"
+#include "select.h"
 
 namespace pml {
 
 constexpr int kBins = 2048;
 constexpr int kUnroll = 4;  // float4 loads in flight per lane in the streaming passes
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN sorts below every number
-    if (u == 0x80000000u) u = 0u;                    // -0 counts as +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 template <int NT>
 struct TopkCfg {
@@ -55,82 +48,6 @@ struct TopkCfg {
 constexpr int kSampleDiv = 8;       // the sampled pass reads one 1-KB chunk in 8
 constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled path (measured:
                                     // 32K-64K rows 47 -> 35 us; narrower rows gain nothing)
-
-// Inclusive scan of one uint32 per thread over the workgroup; *total gets the sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t *s_wave, uint32_t *total) {
-    constexpr int NW = NT / kWave;
-    const int lane = lane_id();
-    const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
-    if (lane == kWave - 1) s_wave[wave] = x;
-    __syncthreads();
-    if (wave == 0) {
-        uint32_t v = lane < NW ? s_wave[lane] : 0u;
-#pragma unroll
-        for (int o = 1; o < NW; o <<= 1) {
-            const uint32_t y = __shfl_up(v, o, kWave);
-            if (lane >= o) v += y;
-        }
-        if (lane < NW) s_wave[NW + lane] = v;
-    }
-    __syncthreads();
-    const uint32_t before = wave > 0 ? s_wave[NW + wave - 1] : 0u;
-    *total = s_wave[2 * NW - 1];
-    const uint32_t r = x + before;
-    __syncthreads();
-    return r;
-}
-
-// Exclusive prefix over the wave's lanes of c (0 <= c <= 4), and the wave total.
-__device__ __forceinline__ void wave_prefix4(uint32_t c, uint32_t &pre, uint32_t &tot) {
-    pre = 0;
-    tot = 0;
-#pragma unroll
-    for (int b = 0; b < 3; ++b) {
-        const uint64_t m = __ballot((c >> b) & 1u);
-        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        pre += below << b;
-        tot += (uint32_t)__popcll(m) << b;
-    }
-}
-
-// Find the bin holding the kk-th largest key among bins [0, nbins) whose
-// counts count(b) gives: writes (bin, count of keys in higher bins) to s_pick.
-template <int NT, typename C>
-__device__ __forceinline__ void pick_bin_by(C count, int nbins, uint32_t kk, uint32_t *s_wave, uint32_t *s_pick) {
-    const int per = (nbins + NT - 1) / NT;
-    const int t = threadIdx.x;
-    // thread t owns bins top - t*per - j, j < per (descending)
-    uint32_t own = 0;
-    for (int j = 0; j < per; ++j) {
-        const int b = nbins - 1 - (t * per + j);
-        if (b >= 0) own += count(b);
-    }
-    uint32_t tot;
-    uint32_t above = block_scan<NT>(own, s_wave, &tot) - own;
-    for (int j = 0; j < per; ++j) {
-        const int b = nbins - 1 - (t * per + j);
-        if (b < 0) break;
-        const uint32_t h = count(b);
-        if (above < kk && kk <= above + h) {
-            s_pick[0] = (uint32_t)b;
-            s_pick[1] = above;
-        }
-        above += h;
-    }
-    __syncthreads();
-}
-
-template <int NT>
-__device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint32_t kk, uint32_t *s_wave,
-                                         uint32_t *s_pick) {
-    pick_bin_by<NT>([&](int b) { return s_hist[b]; }, nbins, kk, s_wave, s_pick);
-}
 
 struct TopkArgs {
     const float *logits;
@@ -214,7 +131,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t s_hist[kBins];
     __shared__ uint32_t s_key[CAP];
     __shared__ int32_t s_pos[CAP];
-    __shared__ uint32_t s_wave[2 * NW];
+    __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
 
@@ -540,7 +457,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     static_assert(CAP < 65536, "16-bit bin counters");
     __shared__ uint32_t s_hist[kBins / 2];
     __shared__ uint32_t s_key[CAP];
-    __shared__ uint32_t s_wave[2 * NW];
+    __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
     const int r = blockIdx.x;

@@ -20,7 +20,8 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
-              "top_k_per_row_workspace_size", "pml_status_string", "pml_version"):
+              "top_k_per_row_workspace_size", "pml_status_string", "pml_version",
+              "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates"):
         assert n in names
 
 
@@ -90,3 +91,49 @@ def test_metadata_validation():
     assert f(FAKE, 4, 1, 0, None, 64, (1 << 20) + 1, FAKE, None) == 2
     assert f(None, 4, 1, 0, None, 64, 4, FAKE, None) == 1
     assert f(FAKE, 4, 1, 0, None, 64, 4, P(0x1008), None) == 6
+
+
+def _pack(**kw):
+    a = dict(logits=FAKE, rows=4, ld=1024, rs=None, topk=FAKE, topk_ld=64, k=64, rank=1, world=4, il=1,
+             packed=FAKE, stream=None)
+    a.update(kw)
+    return pml.lib().pack_dcp_topk_candidates(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 2), (dict(ld=-4), 2), (dict(k=0), 7), (dict(k=4097, topk_ld=5000), 7),
+    (dict(world=0, rank=0), 2), (dict(rank=4), 2), (dict(rank=-1), 2), (dict(il=0), 2),
+    (dict(logits=None), 1), (dict(topk=None), 1), (dict(packed=None), 1), (dict(topk_ld=63), 5),
+    (dict(packed=P(0x1004)), 6),
+    # ids must stay exact in float32: local position 2^21 of rank 0 of 8, interleave 1, is id 2^24
+    (dict(ld=(1 << 21) + 1, world=8, rank=0), 2),
+])
+def test_pack_validation(kw, code):
+    assert _pack(**kw) == code
+
+
+def test_pack_id_limit_edge_and_zero_rows():
+    # local position 2^21 - 1 on rank 7 of 8, interleave 1: global id 2^24 - 1, the largest allowed
+    assert _pack(rows=0, ld=(1 << 21), world=8, rank=7) == 0
+    assert _pack(rows=0, ld=(1 << 21) + 1, world=8, rank=7) == 2
+    assert _pack(rows=0) == 0
+
+
+def _merge(**kw):
+    a = dict(g=FAKE, world=8, rows=4, k=2048, out=FAKE, out_ld=2048, stream=None)
+    a.update(kw)
+    return pml.lib().stable_topk_from_gathered_candidates(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 2), (dict(world=0), 2), (dict(k=0), 7), (dict(k=4097, out_ld=5000), 7),
+    (dict(world=9, k=4096, out_ld=4096), 2), (dict(g=None), 1), (dict(out=None), 1),
+    (dict(out_ld=2047), 5), (dict(g=P(0x1004)), 6),
+])
+def test_merge_validation(kw, code):
+    assert _merge(**kw) == code
+
+
+def test_merge_zero_rows_and_largest_pairs():
+    assert _merge(rows=0) == 0
+    assert _merge(rows=0, world=8, k=4096, out_ld=4096) == 0
