@@ -76,9 +76,11 @@ def parse():
 
 
 class PagedBench:
-    """Device copies of one paged case and the three calls of one step."""
+    """Device copies of one paged case and the three calls of one step. With bf16,
+    the logits are written as bf16 and upcast over each row's span for the top-k
+    (four calls)."""
 
-    def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None):
+    def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None, bf16: bool = False):
         d = torch.device("cuda:0")
         self.case = case
         self.q = case.q.to(d)
@@ -90,6 +92,13 @@ class PagedBench:
         self.num_cus = num_cus or pml.default_num_workers()
         self.sched = torch.empty(pml.schedule_rows(self.num_cus), 2, dtype=torch.int32, device=d)
         self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
+        self.bf16 = bf16
+        self.nev = 5 if bf16 else 4
+        if bf16:
+            assert case.next_n == 1
+            ld = (case.max_ctx + 7) // 8 * 8
+            self.logits_bf16 = torch.empty(case.rows, ld, dtype=torch.bfloat16, device=d)
+            self.logits = torch.empty(case.rows, ld, dtype=torch.float32, device=d)
         self.topk = torch.empty(case.rows, case.topk, dtype=torch.int32, device=d)
         self.req_tokens = int(sum(case.req_ctx))
         self.pairs = syn.scored_pairs(case)
@@ -104,12 +113,16 @@ class PagedBench:
             ev[1].record()
         pml.fp8_fp4_paged_mqa_logits(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt, self.sched,
                                      c.max_ctx, self.indices, kv_format=c.kv_format, block_kv=c.block_kv,
-                                     next_n=c.next_n, logits=self.logits)
+                                     next_n=c.next_n, logits=self.logits_bf16 if self.bf16 else self.logits)
         if ev is not None:
             ev[2].record()
+        if self.bf16:
+            pml.as_fp32_logits(self.logits_bf16, self.lens, out=self.logits, cols=c.max_ctx)
+            if ev is not None:
+                ev[3].record()
         pml.top_k_per_row(self.logits, self.lens, c.topk, next_n=c.next_n, max_width=c.max_ctx, out=self.topk)
         if ev is not None:
-            ev[3].record()
+            ev[self.nev - 1].record()
 
 
 class RaggedBench:
@@ -187,15 +200,16 @@ def run_timed(b, steps: int, warmup: int):
     for i in range(warmup):
         b.step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    nev = getattr(b, "nev", 4)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         b.step(warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
-    return wall, per  # per: [steps, 3] ms of (schedule, logits, top-k)
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(nev - 1)] for e in evs])
+    return wall, per  # per: [steps, nev - 1] ms of (schedule, logits, [upcast,] top-k)
 
 
 def capture_steps(b) -> list:
@@ -346,6 +360,21 @@ def main():
                 w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
             print(json.dumps(paged_summary(name, ob, w2, p2, args.steps)), file=sys.stderr, flush=True)
             del ob
+        print("[bench] varlen_spec_decode_fp8_120k_bf16", file=sys.stderr, flush=True)
+        ob = PagedBench(syn.config_varlen_fp8(), args.copies, bf16=True)
+        w2, p2 = run_timed(ob, args.steps, args.warmup)
+        if not args.no_graph:
+            w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
+        c = ob.case
+        t_log = float(p2[:, 1].mean()) * 1e-3
+        kbytes = ob.req_tokens * BYTES_PER_TOKEN[c.kv_format]
+        print(json.dumps({"workload": "varlen_spec_decode_fp8_120k_bf16_logits", "ms_per_step": w2 / args.steps * 1e3,
+                          "ms_schedule": float(p2[:, 0].mean()), "ms_logits": t_log * 1e3,
+                          "ms_upcast": float(p2[:, 2].mean()), "ms_topk": float(p2[:, 3].mean()),
+                          "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
+                          "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
+                          "logits_out_bytes": c.rows * c.max_ctx * 2}), file=sys.stderr, flush=True)
+        del ob
         print("[bench] dcp_merge_8ranks", file=sys.stderr, flush=True)
         db = DcpBench(syn.config_varlen_fp8())
         w2, p2 = run_timed(db, args.steps, args.warmup)

@@ -217,6 +217,45 @@ int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const in
                   int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fp8_fp4_paged_mqa_logits_bf16 - the same call as fp8_fp4_paged_mqa_logits,
+ * writing bf16 logits (the SM100 kernel's output type; sparse_attn_indexer
+ * page, as_fp32_logits and _varlen_decode_rows). Every argument means what it
+ * means there, except:
+ *   logits     bf16 bits [num_rows][logits_ld] (uint16_t), 16-B aligned;
+ *              logits_ld >= max_ctx and a multiple of 8 (else
+ *              PML_ERR_STRIDE). Each value is the fp32 logit rounded to the
+ *              nearest bf16, ties to even; -inf stays -inf (0xff80), NaN stays
+ *              a NaN.
+ * The scores are computed exactly as in the fp32 call; only the store differs,
+ * so the bf16 output equals the fp32 output rounded to bf16, bit for bit.
+ */
+int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int next_n, int num_heads,
+                                  int head_dim, const void *kv_cache, int kv_format,
+                                  int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                  const float *weights, const int32_t *context_lens,
+                                  int context_lens_2d, const int32_t *block_table,
+                                  int64_t block_table_ld, int block_table_cols,
+                                  int32_t *schedule, int num_CUs,
+                                  const int32_t *indices, int max_ctx, uint16_t *logits,
+                                  int64_t logits_ld, void *stream);
+
+/*
+ * as_fp32_logits - fp32 copy of bf16 logits over each row's valid span, for
+ * the fp32 top-k (sparse_attn_indexer page, as_fp32_logits: only columns below
+ * the row's end are converted, and the row stride is kept).
+ *   logits     bf16 bits [num_rows][logits_ld], 16-B aligned, logits_ld a
+ *              multiple of 8 and >= cols.
+ *   cols       the logits width (max_ctx); row ends are clamped to [0, cols].
+ *   row_ends   int32 [num_rows].
+ *   out        fp32 [num_rows][out_ld], 16-B aligned, out_ld a multiple of 4
+ *              and >= cols. Columns [0, row_end) receive the exact fp32 value
+ *              of each bf16 (the bits shifted up by 16); the other columns are
+ *              not written.
+ */
+int as_fp32_logits(const uint16_t *logits, int num_rows, int64_t logits_ld, int cols,
+                   const int32_t *row_ends, float *out, int64_t out_ld, void *stream);
+
+/*
  * Exact top-k over key tokens sharded across decode-context-parallel ranks
  * ("vllm.model_executor.layers.sparse_attn_indexer", _merge_dcp_topk_global:
  * each rank packs its local top-k as (score, global token id) float32 pairs,

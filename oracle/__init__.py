@@ -194,5 +194,24 @@ def dcp_merge(gathered: np.ndarray, k: int) -> np.ndarray:
     return out
 
 
+def bf16_round(x) -> np.ndarray:
+    """bf16 bits (uint16) of float32 values, rounded to nearest, ties to even.
+
+    bf16 is the upper half of an IEEE binary32 (1 sign, 8 exponent, 7 mantissa
+    bits). Rounding the binary32 magnitude to a multiple of 2^16 units in the
+    last place, ties to the even result, is rounding to the nearest bf16; a
+    carry out of the mantissa moves to the next binade or to infinity, as it
+    should. NaN maps to the quiet NaN 0x7fc0 with the input's sign."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    return np.where(nan, ((u >> 16) & 0x8000).astype(np.uint16) | np.uint16(0x7FC0), r).astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """float32 value of bf16 bits: the 16 bits as the upper half of a binary32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def num_threads() -> int:
     return lib().pml_oracle_num_threads()

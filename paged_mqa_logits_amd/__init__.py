@@ -63,6 +63,9 @@ def lib() -> ctypes.CDLL:
         L.paged_mqa_logits_schedule_rows.restype = I
         L.fp8_fp4_paged_mqa_logits.argtypes = [P, I, I, I, I, P, I, I, I64, I64, P, P, I, P, I64, I, P,
                                                I, P, I, P, I64, P]
+        if hasattr(L, "fp8_fp4_paged_mqa_logits_bf16"):
+            L.fp8_fp4_paged_mqa_logits_bf16.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes
+            L.as_fp32_logits.argtypes = [P, I, I64, I, P, P, I64, P]
         if hasattr(L, "mqa_logits"):
             L.mqa_logits.argtypes = [P, I, I, I, P, P, I, P, P, P, P, I64, P]
         if hasattr(L, "top_k_per_row"):
@@ -73,7 +76,8 @@ def lib() -> ctypes.CDLL:
             L.pack_dcp_topk_candidates.argtypes = [P, I, I64, P, P, I64, I, I, I, I, P, P]
             L.stable_topk_from_gathered_candidates.argtypes = [P, I, I, I, P, I64, P]
         for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
-                     "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates"):
+                     "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
+                     "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits"):
             if hasattr(L, name):
                 getattr(L, name).restype = I
         L.pml_status_string.argtypes = [I]
@@ -183,10 +187,12 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
                              schedule: torch.Tensor, max_model_len: int,
                              indices: torch.Tensor | None = None, *, kv_format: int = KV_FP8,
                              block_kv: int = 64, next_n: int = 1,
-                             logits: torch.Tensor | None = None) -> torch.Tensor:
-    """Paged logits fp32 [rows, ld >= max_model_len]; columns past each row's
-    visible length are -inf. ``kv_cache`` is [num_pages, page_stride_bytes] uint8
-    (a row stride larger than the page is allowed)."""
+                             logits: torch.Tensor | None = None,
+                             out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Paged logits [rows, ld >= max_model_len], fp32 or bf16 (``out_dtype``, or
+    the dtype of a given ``logits``); columns past each row's visible length are
+    -inf. ``kv_cache`` is [num_pages, page_stride_bytes] uint8 (a row stride
+    larger than the page is allowed)."""
     _dev(q, "q", _FP8_TYPES)
     _dev(kv_cache, "kv_cache", (torch.uint8,))
     _dev(weights, "weights", _F32)
@@ -207,18 +213,41 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     if rows != q.shape[0]:
         raise ValueError(f"q has {q.shape[0]} rows but the lengths describe {rows}")
     if logits is None:
-        logits = torch.empty(rows, logits_ld(max_model_len), dtype=torch.float32, device=q.device)
-    if logits.dim() != 2 or logits.stride(1) != 1:
-        raise ValueError("logits must be 2-D with unit inner stride")
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("out_dtype must be float32 or bfloat16")
+        ld = logits_ld(max_model_len) if out_dtype == torch.float32 else (max_model_len + 7) // 8 * 8
+        logits = torch.empty(rows, max(ld, 8), dtype=out_dtype, device=q.device)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be a 2-D float32 or bfloat16 tensor with unit inner stride")
     num_cus = schedule_workers(schedule)
     if not schedule.is_contiguous():
         raise ValueError("schedule must be contiguous")
-    _check(lib().fp8_fp4_paged_mqa_logits(
+    call = lib().fp8_fp4_paged_mqa_logits if logits.dtype == torch.float32 else lib().fp8_fp4_paged_mqa_logits_bf16
+    _check(call(
         _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
         kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
         block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
         max_model_len, _p(logits), logits.stride(0), _stream()), "fp8_fp4_paged_mqa_logits")
     return logits
+
+
+def as_fp32_logits(logits: torch.Tensor, row_ends: torch.Tensor, out: torch.Tensor | None = None,
+                   cols: int | None = None) -> torch.Tensor:
+    """fp32 copy of bf16 logits over each row's columns [0, row_end), with the
+    same row stride; other columns of ``out`` are left as they are."""
+    _dev(logits, "logits", (torch.bfloat16,))
+    _dev(row_ends, "row_ends", _I32)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit inner stride")
+    rows = logits.shape[0]
+    cols = logits.shape[1] if cols is None else cols
+    if row_ends.numel() != rows:
+        raise ValueError("row_ends needs one entry per row")
+    if out is None:
+        out = torch.empty_strided(logits.shape, (logits.stride(0), 1), dtype=torch.float32, device=logits.device)
+    _check(lib().as_fp32_logits(_p(logits), rows, logits.stride(0), cols, _p(row_ends.contiguous()), _p(out),
+                                out.stride(0), _stream()), "as_fp32_logits")
+    return out
 
 
 def mqa_logits(q: torch.Tensor, k: torch.Tensor, k_scale: torch.Tensor, weights: torch.Tensor,

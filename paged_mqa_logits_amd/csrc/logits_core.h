@@ -274,6 +274,21 @@ __device__ __forceinline__ void store_f32_async(float *p, float v) {
 __device__ __forceinline__ void store_v4f_async(float *p, v4f v) {
     asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_v2u_async(uint16_t *p, v2u v) {
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_u16_async(uint16_t *p, uint32_t v) {
+    asm volatile("global_store_short %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+// Two floats rounded to bf16 (nearest even, NaN kept), lo in bits 0-15.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const v2f_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2bf_t));
+}
 
 // One block's logits for up to kGMax rows, parked in the wave's own LDS slot
 // until the next step stores them ahead of the key loads it issues.
@@ -284,11 +299,12 @@ struct WaveSlot {
 
 // Store rows (bit i of mask) of the parked block at columns [col0, col0 + BKV),
 // never at or past ncols. Each lane moves 4 consecutive columns of one row, so
-// one 16-byte store instruction covers 64 * 4 / BKV rows; a 4-column group
-// that crosses ncols is stored column by column.
-template <int BKV>
+// one store instruction (16 bytes of fp32, or 8 of bf16) covers 64 * 4 / BKV
+// rows; a 4-column group that crosses ncols is stored column by column. OT is
+// float, or uint16_t for bf16 logits (rounded to nearest even).
+template <int BKV, typename OT = float>
 __device__ __forceinline__ void flush_slot(const WaveSlot<BKV> &sl, int mask, int64_t row0, int col0, int ncols,
-                                           float *out, int64_t out_ld) {
+                                           OT *out, int64_t out_ld) {
     constexpr int kLanesPerRow = BKV / 4;
     constexpr int kRowsPer = kWave / kLanesPerRow;  // rows per instruction: 4 (BKV 64) or 8 (BKV 32)
     const int lane = lane_id();
@@ -300,29 +316,49 @@ __device__ __forceinline__ void flush_slot(const WaveSlot<BKV> &sl, int mask, in
         const int i = m + lane / kLanesPerRow;
         if (i < kGMax && ((mask >> i) & 1)) {
             const v4f v = lds_ld<v4f>(&sl.v[i][c4]);
-            float *p = out + (row0 + i) * out_ld + s;
-            if (s + 4 <= ncols) {
-                store_v4f_async(p, v);
-            } else {
+            OT *p = out + (row0 + i) * out_ld + s;
+            if constexpr (sizeof(OT) == 4) {
+                if (s + 4 <= ncols) {
+                    store_v4f_async(p, v);
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (s + j < ncols) store_f32_async(p + j, v[j]);
+                    for (int j = 0; j < 4; ++j)
+                        if (s + j < ncols) store_f32_async(p + j, v[j]);
+                }
+            } else {
+                const v2u h = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+                if (s + 4 <= ncols) {
+                    store_v2u_async(p, h);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (s + j < ncols) store_u16_async(p + j, h[j / 2] >> (16 * (j % 2)));
+                }
             }
         }
     }
 }
 
-// Fill columns [c0, c1) of one row with -inf (the whole workgroup of NTH threads).
-template <int NTH = kLThreads>
-__device__ __forceinline__ void fill_neg_inf(float *row, int c0, int c1) {
+// Fill columns [c0, c1) of one row with -inf (the whole workgroup of NTH
+// threads), fp32 or bf16 (OT = uint16_t); rows are 16-B aligned.
+template <int NTH = kLThreads, typename OT = float>
+__device__ __forceinline__ void fill_neg_inf(OT *row, int c0, int c1) {
     if (c0 >= c1) return;
+    constexpr int V = 16 / sizeof(OT);  // columns per 16-B store
+    constexpr uint32_t kBits = sizeof(OT) == 4 ? 0xff800000u : 0xff80ff80u;  // -inf (fp32 / two bf16)
+    OT ninf;
+    if constexpr (sizeof(OT) == 4)
+        ninf = -__builtin_inff();
+    else
+        ninf = (OT)0xff80u;
     const int tid = threadIdx.x;
-    const v4f ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-    const int a4 = min((c0 + 3) & ~3, c1);  // first 16-B aligned column (rows are 16-B aligned)
-    const int b4 = max(a4, c1 & ~3);
-    if (c0 + tid < a4) row[c0 + tid] = -__builtin_inff();
-    for (int col = a4 + 4 * tid; col < b4; col += 4 * NTH) *(v4f *)(row + col) = ninf;
-    if (b4 + tid < c1) row[b4 + tid] = -__builtin_inff();
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u pat = {kBits, kBits, kBits, kBits};
+    const int a = min((c0 + V - 1) & ~(V - 1), c1);  // first 16-B aligned column
+    const int b = max(a, c1 & ~(V - 1));
+    if (c0 + tid < a) row[c0 + tid] = ninf;
+    for (int col = a + V * tid; col < b; col += V * NTH) *(v4u *)(row + col) = pat;
+    if (b + tid < c1) row[b + tid] = ninf;
 }
 
 }  // namespace pml

@@ -40,7 +40,7 @@ struct PagedArgs {
     const int32_t *sched;  // chunk entries (read through the scalar cache)
     int32_t *ctr;          // 64-bit work counters, kPoolStride int32 apart
     int max_ctx;
-    float *out;
+    void *out;  // float, or uint16_t bf16 bits
     int64_t out_ld;
 };
 
@@ -61,13 +61,13 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 // into the wave's LDS slot. Rows whose visible length ends before the block are
 // skipped (their tail is filled separately). Lane i of vis_lane holds the
 // visible length of row i.
-template <bool FP4, int BKV, bool PF>
+template <bool FP4, int BKV, typename OT, bool PF>
 __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int b,
                                           const KeyRegs<FP4, BKV> &kc, bool okc, int bp, KeyRegs<FP4, BKV> &kp,
                                           bool &okp, const uint8_t *s_q, const float *s_w, int vis_lane,
                                           WaveSlot<BKV> &sl, int &mask, int &col0p) {
     touch<FP4, BKV>(kc);
-    flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
+    flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
     if constexpr (PF) okp = fetch_block<FP4, BKV>(a, bt_row, bp, kp);
     const int lane = lane_id();
     const int col0 = b * BKV;
@@ -114,7 +114,7 @@ struct Draw {
 // loads behind its wait). The first blocks are requested before q is staged,
 // so the two memory round trips overlap. With draw_here, the wave issues the
 // draw DrawAhead steps before its blocks end.
-template <bool FP4, int BKV>
+template <bool FP4, int BKV, typename OT>
 __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int64_t bt_row, int b0, int nmy,
                                           uint8_t *s_q, float *s_w, int *s_vis, WaveSlot<BKV> &sl, Draw &dr,
                                           bool draw_here) {
@@ -138,19 +138,19 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
             for (int u = 0; u < NB; ++u) {
                 if (j + u >= nmy) break;
                 if (draw_here && j + u == max(nmy - kDrawAhead, 0)) dr.issue();
-                wave_step<FP4, BKV, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
+                wave_step<FP4, BKV, OT, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
                                           kb[(u + kDepth) % NB], okb[(u + kDepth) % NB], s_q, s_w, vis_lane, sl, mask,
                                           col0p);
             }
         }
-        flush_slot<BKV>(sl, mask, r0, col0p, a.max_ctx, a.out, a.out_ld);
+        flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
     }
 }
 
 // The units from chunk e0's start to chunk e1's start (the whole workgroup).
 // Wave 0 issues the draw kDrawAhead steps before its share of the last piece
 // ends; a range too short for that leaves it to the caller.
-template <bool FP4, int BKV>
+template <bool FP4, int BKV, typename OT>
 __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, uint8_t *s_q, float *s_w, int *s_vis,
                                            WaveSlot<BKV> &sl, Draw &dr) {
     const int tid = threadIdx.x;
@@ -175,14 +175,14 @@ __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, u
             const int b0 = blk_lo + wave * per + min(wave, rem);
             const int nmy = per + (wave < rem ? 1 : 0);
             const bool draw_here = last_piece && wave == 0 && !dr.done;
-            run_piece<FP4, BKV>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
+            run_piece<FP4, BKV, OT>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
         }
         r0 = rn;
         blk_lo = 0;
     }
 }
 
-template <bool FP4, int BKV>
+template <bool FP4, int BKV, typename OT>
 __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     int e0 = kStaticChunks * c, e1 = kStaticChunks * (c + 1);
     for (int par = 0;; par ^= 1) {
         dr.done = false;
-        run_chunks<FP4, BKV>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
+        run_chunks<FP4, BKV, OT>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
         if (!dr.done) dr.issue();
         if (tid == 0) lds_st<unsigned>(&s_take[par], (unsigned)(dr.v % (Dx + Wx)));
         barrier_lds();  // (also: every wave is done reading s_take[par ^ 1])
@@ -230,13 +230,13 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     for (int r = c; r < n; r += W) {
         const int vis = a.rows.visible_s(r);
         const int start = min((vis + BKV - 1) / BKV * BKV, a.max_ctx);
-        fill_neg_inf<kPThreads>(a.out + (int64_t)r * a.out_ld, start, a.max_ctx);
+        fill_neg_inf<kPThreads, OT>((OT *)a.out + (int64_t)r * a.out_ld, start, a.max_ctx);
     }
 }
 
-template <bool FP4, int BKV>
+template <bool FP4, int BKV, typename OT>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV>), dim3(W), dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT>), dim3(W), dim3(kPThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
@@ -244,15 +244,14 @@ static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
 
 static inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n, int num_heads,
-                                        int head_dim, const void *kv_cache, int kv_format,
-                                        int block_kv, int64_t page_stride_bytes, int64_t num_pages,
-                                        const float *weights, const int32_t *context_lens,
-                                        int context_lens_2d, const int32_t *block_table,
-                                        int64_t block_table_ld, int block_table_cols,
-                                        int32_t *schedule, int num_CUs,
-                                        const int32_t *indices, int max_ctx, float *logits,
-                                        int64_t logits_ld, void *stream) {
+// Shared by the fp32 and bf16 entry points (bf16: logits are uint16_t bits and
+// rows must be 16-B aligned, logits_ld a multiple of 8).
+static int paged_logits(const void *q, int num_rows, int next_n, int num_heads, int head_dim,
+                        const void *kv_cache, int kv_format, int block_kv, int64_t page_stride_bytes,
+                        int64_t num_pages, const float *weights, const int32_t *context_lens,
+                        int context_lens_2d, const int32_t *block_table, int64_t block_table_ld,
+                        int block_table_cols, int32_t *schedule, int num_CUs, const int32_t *indices,
+                        int max_ctx, void *logits, int64_t logits_ld, bool bf16, void *stream) {
     if (num_rows < 0 || next_n < 1 || num_CUs < 1 || max_ctx < 0) return PML_ERR_SHAPE;
     if (num_heads != PML_HEADS || head_dim != PML_HEAD_DIM) return PML_ERR_SHAPE;
     if (kv_format != PML_KV_FP8 && kv_format != PML_KV_MXFP4) return PML_ERR_FORMAT;
@@ -268,7 +267,7 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
     const int64_t pb = kv_format == PML_KV_FP8 ? (int64_t)block_kv * (head_dim + 4)
                                                : (int64_t)block_kv * (head_dim / 2 + head_dim / 32);
     if (page_stride_bytes < pb || page_stride_bytes % 16 != 0) return PML_ERR_STRIDE;
-    if (logits_ld < max_ctx || logits_ld % 4 != 0) return PML_ERR_STRIDE;
+    if (logits_ld < max_ctx || logits_ld % (bf16 ? 8 : 4) != 0) return PML_ERR_STRIDE;
     if (!al16(q) || !al16(kv_cache) || !al16(weights) || !al16(logits) || !al16(schedule)) return PML_ERR_ALIGN;
     pml::PagedArgs a;
     a.q = (const uint8_t *)q;
@@ -286,9 +285,46 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
     a.out = logits;
     a.out_ld = logits_ld;
     hipStream_t st = (hipStream_t)stream;
+    if (bf16) {
+        if (kv_format == PML_KV_FP8)
+            return block_kv == 64 ? pml::launch_paged<false, 64, uint16_t>(a, num_CUs, st)
+                                  : pml::launch_paged<false, 32, uint16_t>(a, num_CUs, st);
+        return block_kv == 64 ? pml::launch_paged<true, 64, uint16_t>(a, num_CUs, st)
+                              : pml::launch_paged<true, 32, uint16_t>(a, num_CUs, st);
+    }
     if (kv_format == PML_KV_FP8)
-        return block_kv == 64 ? pml::launch_paged<false, 64>(a, num_CUs, st)
-                              : pml::launch_paged<false, 32>(a, num_CUs, st);
-    return block_kv == 64 ? pml::launch_paged<true, 64>(a, num_CUs, st)
-                          : pml::launch_paged<true, 32>(a, num_CUs, st);
+        return block_kv == 64 ? pml::launch_paged<false, 64, float>(a, num_CUs, st)
+                              : pml::launch_paged<false, 32, float>(a, num_CUs, st);
+    return block_kv == 64 ? pml::launch_paged<true, 64, float>(a, num_CUs, st)
+                          : pml::launch_paged<true, 32, float>(a, num_CUs, st);
+}
+
+extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n, int num_heads,
+                                        int head_dim, const void *kv_cache, int kv_format,
+                                        int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                        const float *weights, const int32_t *context_lens,
+                                        int context_lens_2d, const int32_t *block_table,
+                                        int64_t block_table_ld, int block_table_cols,
+                                        int32_t *schedule, int num_CUs,
+                                        const int32_t *indices, int max_ctx, float *logits,
+                                        int64_t logits_ld, void *stream) {
+    return paged_logits(q, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
+                        page_stride_bytes, num_pages, weights, context_lens, context_lens_2d, block_table,
+                        block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx, logits,
+                        logits_ld, false, stream);
+}
+
+extern "C" int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int next_n, int num_heads,
+                                             int head_dim, const void *kv_cache, int kv_format,
+                                             int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                             const float *weights, const int32_t *context_lens,
+                                             int context_lens_2d, const int32_t *block_table,
+                                             int64_t block_table_ld, int block_table_cols,
+                                             int32_t *schedule, int num_CUs,
+                                             const int32_t *indices, int max_ctx, uint16_t *logits,
+                                             int64_t logits_ld, void *stream) {
+    return paged_logits(q, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
+                        page_stride_bytes, num_pages, weights, context_lens, context_lens_2d, block_table,
+                        block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx, logits,
+                        logits_ld, true, stream);
 }

@@ -15,6 +15,15 @@ SENTINEL = 12345.0  # prefilled into output buffers: any cell left unwritten sho
 REL = 2e-3
 ABS = 1e-3
 
+# bf16 logits: the fp32 logit x = oracle + e, |e| <= REL |oracle| + ABS S, is
+# rounded to nearest bf16, which adds at most u |x| with u = 2^-8 (half a unit in
+# the 8th significant bit). So |bf16(x) - oracle| <= u (|oracle| + |e|) + |e|
+# <= (u + REL (1 + u)) |oracle| + ABS (1 + u) S.
+U_BF16 = 2.0 ** -8
+REL_BF16 = U_BF16 + REL * (1 + U_BF16)
+ABS_BF16 = ABS * (1 + U_BF16)
+SENTINEL_BF16 = 0x1234  # bf16 bits prefilled into output buffers
+
 
 def dev():
     return torch.device("cuda:0")
@@ -49,11 +58,28 @@ def run_paged(case: syn.PagedCase, t: dict | None = None, *, num_cus=None, indic
     return o[:, : case.max_ctx]
 
 
-def abs_tol(weights: torch.Tensor) -> np.ndarray:
-    return ABS * np.abs(weights.double().numpy()).sum(axis=1)
+def run_paged_bf16(case: syn.PagedCase, t: dict | None = None, *, ld=None, sched=None) -> np.ndarray:
+    """GPU bf16 logits [rows, max_ctx] as uint16 bits (checks the sentinel columns past max_ctx)."""
+    t = t or upload(case)
+    if sched is None:
+        sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, None, indices=t["indices"],
+                                              next_n=case.next_n)
+    ld = ld or (case.max_ctx + 7) // 8 * 8 + 8
+    out = torch.full((case.rows, ld), SENTINEL_BF16, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+    pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx, t["indices"],
+                                 kv_format=case.kv_format, block_kv=case.block_kv, next_n=case.next_n, logits=out)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.all(o[:, case.max_ctx:] == SENTINEL_BF16), "columns past max_ctx were written"
+    return o[:, : case.max_ctx]
 
 
-def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Tensor, what: str = "") -> None:
+def abs_tol(weights: torch.Tensor, a: float = ABS) -> np.ndarray:
+    return a * np.abs(weights.double().numpy()).sum(axis=1)
+
+
+def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Tensor, what: str = "",
+                        rel: float = REL, abs_: float = ABS) -> None:
     """The acceptance bar: masked cells exactly -inf, the rest within tolerance."""
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
     assert not np.any(gpu == SENTINEL), f"{what}: unwritten cells"
@@ -62,7 +88,7 @@ def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Te
     assert not bad_mask.any(), f"{what}: -inf pattern differs at {np.argwhere(bad_mask)[:5]}"
     assert not np.isnan(ref).any(), f"{what}: oracle produced NaN"
     fin = ~masked
-    tol = REL * np.abs(ref) + abs_tol(weights_rows)[:, None]
+    tol = rel * np.abs(ref) + abs_tol(weights_rows, abs_)[:, None]
     err = np.abs(gpu.astype(np.float64) - ref)
     bad = fin & ~(err <= tol)
     if fin.any():

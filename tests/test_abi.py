@@ -21,7 +21,8 @@ def test_header_declares_the_four_calls():
     names = _declared()
     for n in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
               "top_k_per_row_workspace_size", "pml_status_string", "pml_version",
-              "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates"):
+              "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
+              "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits"):
         assert n in names
 
 
@@ -137,3 +138,43 @@ def test_merge_validation(kw, code):
 def test_merge_zero_rows_and_largest_pairs():
     assert _merge(rows=0) == 0
     assert _merge(rows=0, world=8, k=4096, out_ld=4096) == 0
+
+
+def _paged_bf16(**kw):
+    a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
+             w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
+             max_ctx=512, out=FAKE, ld=512, stream=None)
+    a.update(kw)
+    return pml.lib().fp8_fp4_paged_mqa_logits_bf16(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=32), 2), (dict(fmt=2), 9), (dict(bkv=16), 3), (dict(q=None), 1), (dict(out=None), 1),
+    (dict(ld=508), 5), (dict(ld=516, max_ctx=512), 5), (dict(ld=500), 5), (dict(out=P(0x1008)), 6),
+])
+def test_paged_bf16_validation(kw, code):
+    assert _paged_bf16(**kw) == code
+
+
+def test_paged_bf16_zero_rows():
+    assert _paged_bf16(rows=0) == 0
+
+
+def _upcast(**kw):
+    a = dict(src=FAKE, rows=4, ld=1024, cols=1000, ends=FAKE, out=FAKE, out_ld=1024, stream=None)
+    a.update(kw)
+    return pml.lib().as_fp32_logits(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 2), (dict(cols=-1), 2), (dict(src=None), 1), (dict(ends=None), 1), (dict(out=None), 1),
+    (dict(ld=1020), 5), (dict(ld=996), 5), (dict(out_ld=998), 5), (dict(out_ld=996), 5),
+    (dict(src=P(0x1008)), 6), (dict(out=P(0x1004)), 6),
+])
+def test_upcast_validation(kw, code):
+    assert _upcast(**kw) == code
+
+
+def test_upcast_empty_is_ok():
+    assert _upcast(rows=0) == 0
+    assert _upcast(cols=0) == 0

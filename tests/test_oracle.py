@@ -329,3 +329,28 @@ def test_topk_matches_numpy_and_torch():
     t = oracle.topk(s[[0]], ke[[0]], 50)
     tt = torch.topk(torch.from_numpy(s[0]), 50).indices.sort().values.numpy()
     assert np.array_equal(t[0], tt)
+
+
+# --------------------------------------------------------------------------
+# bf16 (logits output format)
+
+def test_bf16_helpers_match_torch():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0) ** rng.integers(-40, 40, 20000),
+        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 3.3895e38, 3.4e38, -3.4e38, 1e-40, -1e-45,
+                  1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20], dtype=np.float32)])
+    # exact ties: halfway between two bf16 values, both parities
+    u = (rng.integers(0x00800000, 0x7f000000, 5000, dtype=np.uint32) & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    x = np.concatenate([x, u.view(np.float32), -u.view(np.float32)])
+    got = oracle.bf16_round(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    finite = ~np.isnan(x)
+    assert np.array_equal(got[finite], want[finite])
+    assert np.isnan(oracle.bf16_to_f32(got[~finite])).all()
+    back = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.bf16_to_f32(got)[finite], back[finite])
+    # the rounding error bound used for the bf16 logits tolerance: half a unit in the 8th bit
+    xf = x[finite & np.isfinite(x) & (np.abs(x) > 1e-37) & (np.abs(x) < 3e38)].astype(np.float64)
+    err = np.abs(oracle.bf16_to_f32(oracle.bf16_round(xf.astype(np.float32))).astype(np.float64) - xf)
+    assert (err <= 2.0 ** -8 * np.abs(xf)).all()
