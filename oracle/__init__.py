@@ -51,7 +51,7 @@ def _bind(path) -> ctypes.CDLL:
     L.pml_oracle_e8m0.argtypes = [ctypes.c_uint8]
     L.pml_oracle_paged_logits.restype = None
     L.pml_oracle_paged_logits.argtypes = [
-        u8p, ctypes.c_int, ctypes.c_int, u8p, u8p, ctypes.c_int, ctypes.c_int,
+        u8p, u8p, ctypes.c_int, ctypes.c_int, u8p, u8p, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, ctypes.c_int64, u8p, ctypes.c_int, ctypes.c_int, u8p,
         ctypes.c_int64, u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
     L.pml_oracle_ragged_logits.restype = None
@@ -121,9 +121,10 @@ def paged_logits(case, rows=None, col_begin: int = 0, col_end: int | None = None
     if col_end is None:
         col_end = case.max_ctx
     out = np.empty((len(rows), col_end - col_begin), dtype=np.float64)
+    qs = None if getattr(case, "q_scale", None) is None else _np(case.q_scale, np.uint8)
     if out.size:
         lib().pml_oracle_paged_logits(
-            _ptr(q), case.H, case.D, _ptr(w), _ptr(kv), case.kv_format, case.block_kv,
+            _ptr(q), None if qs is None else _ptr(qs), case.H, case.D, _ptr(w), _ptr(kv), case.kv_format, case.block_kv,
             kv.shape[1], kv.shape[0], _ptr(lens), int(case.lens_2d), case.next_n,
             _ptr(bt), bt.shape[1] if bt.ndim == 2 else 0, _ptr(rows), len(rows),
             col_begin, col_end, _ptr(out))

@@ -52,9 +52,21 @@ def dequant_page_tokens(case, page: int) -> np.ndarray:
     return e2m1_np(nib) * np.repeat(e8m0_np(sc), 32, axis=1)
 
 
+def q_dequant(case) -> np.ndarray:
+    """q as float64 [rows, H, D]: fp8 codes, or packed e2m1 times per-32 e8m0 scales."""
+    if getattr(case, "q_scale", None) is None:
+        return fp8_e4m3_np(case.q.numpy())
+    packed = case.q.numpy()                          # [rows, H, D/2]
+    rows, H, half = packed.shape
+    nib = np.empty((rows, H, 2 * half), dtype=np.uint8)
+    nib[..., 0::2] = packed & 15
+    nib[..., 1::2] = packed >> 4
+    return e2m1_np(nib) * np.repeat(e8m0_np(case.q_scale.numpy()), 32, axis=2)
+
+
 def paged_logits(case) -> np.ndarray:
     """Dense [rows, max_ctx] float64 logits by gather + einsum."""
-    q = fp8_e4m3_np(case.q.numpy())                  # [rows, H, D]
+    q = q_dequant(case)                              # [rows, H, D]
     w = case.weights.numpy().astype(np.float64)      # [rows, H]
     lens = case.context_lens.numpy().astype(np.int64)
     bt = case.block_table.numpy()

@@ -114,15 +114,30 @@ static int64_t visible(const int32_t *lens, int lens_2d, int next_n, int r)
     return v < 0 ? 0 : v;
 }
 
+/* Element d of head h of one query row. fp8 q (qsrow NULL): the e4m3 code.
+ * fp4 q (the indexer's FP4 path passes q as a (values, scales) pair,
+ * sparse_attn_indexer page, forward_cuda; the layout read here is the
+ * library's: the MXFP4 key layout applied to q): values [H][D/2] packed e2m1,
+ * element 2i in the low nibble of byte i, and scales [H][D/32] e8m0, one per
+ * 32 consecutive elements. */
+static double q_elem(const uint8_t *qrow, const uint8_t *qsrow, int D, int h, int d)
+{
+    if (!qsrow)
+        return FP8[qrow[(size_t)h * D + d]];
+    uint8_t byte = qrow[(size_t)h * (D / 2) + d / 2];
+    uint8_t nib = (d % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return E2M1[nib] * E8M0[qsrow[(size_t)h * (D / 32) + d / 32]];
+}
+
 /* One score: sum_h w[h] * max(0, sum_d q^[h,d] * k^[s,d]). */
-static double score_paged(const uint8_t *qrow, const float *wrow, int H, int D,
+static double score_paged(const uint8_t *qrow, const uint8_t *qsrow, const float *wrow, int H, int D,
                           const uint8_t *page, int kv_format, int block_kv, int slot)
 {
     double total = 0.0;
     for (int h = 0; h < H; ++h) {
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-            dot += FP8[qrow[(size_t)h * D + d]] *
+            dot += q_elem(qrow, qsrow, D, h, d) *
                    key_elem(page, kv_format, block_kv, D, slot, d);
         total += (double)wrow[h] * (dot > 0.0 ? dot : 0.0);
     }
@@ -132,7 +147,8 @@ static double score_paged(const uint8_t *qrow, const float *wrow, int H, int D,
 /* Paged logits (fp8_fp4_paged_mqa_logits as called from _varlen_decode_rows,
  * and fp8_paged_mqa_logits_cpu in forward_cpu, which reads the cache through
  * the page table with an explicit page stride).
- *   q          fp8 e4m3 codes [rows][H][D]
+ *   q          fp8 e4m3 codes [rows][H][D]; with q_scale, packed e2m1
+ *              [rows][H][D/2] and q_scale e8m0 [rows][H][D/32] (q_elem)
  *   w          float [rows][H]
  *   kv_cache   num_pages pages, page p at kv_cache + p * page_stride
  *   lens       int32 [rows] (next_n == 1), [rows/next_n] (1-D, next_n > 1)
@@ -141,7 +157,7 @@ static double score_paged(const uint8_t *qrow, const float *wrow, int H, int D,
  * Writes out[i][c - col_begin] for rows row_list[i] and columns
  * [col_begin, col_end): the score for c < visible(r), else -inf. Blocks that
  * are visible but whose table entry is outside [0, num_pages) give NaN. */
-void pml_oracle_paged_logits(const uint8_t *q, int H, int D, const float *w,
+void pml_oracle_paged_logits(const uint8_t *q, const uint8_t *q_scale, int H, int D, const float *w,
                              const uint8_t *kv_cache, int kv_format, int block_kv,
                              int64_t page_stride, int64_t num_pages,
                              const int32_t *lens, int lens_2d, int next_n,
@@ -165,7 +181,8 @@ void pml_oracle_paged_logits(const uint8_t *q, int H, int D, const float *w,
             if (page < 0 || page >= num_pages)
                 val = NAN;
             else
-                val = score_paged(q + (size_t)r * H * D, w + (size_t)r * H, H, D,
+                val = score_paged(q_scale ? q + (size_t)r * H * (D / 2) : q + (size_t)r * H * D,
+                                  q_scale ? q_scale + (size_t)r * H * (D / 32) : NULL, w + (size_t)r * H, H, D,
                                   kv_cache + (size_t)page * page_stride, kv_format,
                                   block_kv, c % block_kv);
         }

@@ -14,6 +14,8 @@ batch 40, speculative steps) with H = 64 heads and D = 128.
 Recipes (all random draws come from one seeded ``torch.Generator`` on the CPU):
 
 * q  = fp8_e4m3fn(clamp(N(0,1), +-448))            [rows, H, D]
+  or, with q_fp4, the same N(0,1) draw MX-quantised like the fp4 keys:
+  packed e2m1 [rows, H, D/2] plus e8m0 scales [rows, H, D/32]
 * w  = N(0,1) / 8, float32                          [rows, H]
 * fp8 K, per token: x ~ N(0,1)^D, codes = fp8(clamp(448 x / max|x|)),
   scale ~ U(0.5, 2) / 448 (float32)
@@ -97,7 +99,7 @@ def mx_fp4_quantize(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 @dataclass
 class PagedCase:
     """Inputs of one paged-logits call (CPU tensors)."""
-    q: torch.Tensor            # uint8 fp8 codes [rows, H, D]
+    q: torch.Tensor            # uint8 fp8 codes [rows, H, D], or packed e2m1 [rows, H, D/2]
     weights: torch.Tensor      # float32 [rows, H]
     kv_cache: torch.Tensor     # uint8 [num_pages, page_stride]
     kv_format: int
@@ -111,6 +113,7 @@ class PagedCase:
     H: int = H_DEFAULT
     D: int = D_DEFAULT
     req_ctx: list = field(default_factory=list)  # per request (or batch entry) full length
+    q_scale: torch.Tensor | None = None  # uint8 e8m0 [rows, H, D/32] when q is e2m1
 
     @property
     def rows(self) -> int:
@@ -199,6 +202,7 @@ def make_paged_case(
     spare_frac: float = 0.05,
     fp4_spread: int = 0,
     row_ctx: list[int] | None = None,
+    q_fp4: bool = False,
 ) -> PagedCase:
     """Build a paged case.
 
@@ -212,6 +216,7 @@ def make_paged_case(
       the block table has one row per request and ``context_lens`` is 1-D (the
       full length) or, with ``lens_2d``, [B, next_n] per-row lengths.
     ``row_ctx`` overrides the per-row visible lengths (varlen only).
+    ``q_fp4`` MX-quantises q (packed e2m1 + e8m0 per 32 elements) instead of fp8.
     """
     g = _gen(seed)
     B = len(req_ctx)
@@ -238,7 +243,14 @@ def make_paged_case(
         _write_request_tokens(kv, pages, req_ctx[i], kv_format, block_kv, D, g, fp4_spread)
 
     rows = sum(req_rows)
-    q = fp8_codes(torch.randn(rows, H, D, generator=g, dtype=torch.float32))
+    qf = torch.randn(rows, H, D, generator=g, dtype=torch.float32)
+    q_scale = None
+    if q_fp4:
+        packed, sc = mx_fp4_quantize(qf.reshape(rows * H, D).numpy().astype(np.float64))
+        q = torch.from_numpy(packed.reshape(rows, H, D // 2).copy())
+        q_scale = torch.from_numpy(sc.reshape(rows, H, D // MX_BLOCK).copy())
+    else:
+        q = fp8_codes(qf)
     w = torch.randn(rows, H, generator=g, dtype=torch.float32) / 8
     req_of_row = np.repeat(np.arange(B, dtype=np.int32), req_rows)
     if varlen:
@@ -265,7 +277,7 @@ def make_paged_case(
     return PagedCase(q=q, weights=w, kv_cache=torch.from_numpy(kv), kv_format=kv_format,
                      block_kv=block_kv, block_table=block_table, context_lens=context_lens,
                      indices=indices, next_n=(1 if varlen else next_n), max_ctx=max_ctx,
-                     topk=topk, H=H, D=D, req_ctx=list(req_ctx))
+                     topk=topk, H=H, D=D, req_ctx=list(req_ctx), q_scale=q_scale)
 
 
 @dataclass

@@ -354,3 +354,34 @@ def test_bf16_helpers_match_torch():
     xf = x[finite & np.isfinite(x) & (np.abs(x) > 1e-37) & (np.abs(x) < 3e38)].astype(np.float64)
     err = np.abs(oracle.bf16_to_f32(oracle.bf16_round(xf.astype(np.float32))).astype(np.float64) - xf)
     assert (err <= 2.0 ** -8 * np.abs(xf)).all()
+
+
+# --------------------------------------------------------------------------
+# fp4 q (values + per-32 e8m0 scales)
+
+@pytest.mark.parametrize("fmt,bkv", [(1, 32), (1, 64), (0, 64)])
+def test_fp4q_oracle_matches_numpy(fmt, bkv):
+    case = syn.make_paged_case([300, 64, 130], [3, 1, 2], seed=960 + fmt + bkv, kv_format=fmt, block_kv=bkv,
+                               max_ctx=320, q_fp4=True, H=8)
+    assert case.q.shape == (6, 8, 64) and case.q_scale.shape == (6, 8, 4)
+    a = oracle.paged_logits(case)
+    b = brute.paged_logits(case)
+    fin = np.isfinite(b)
+    assert np.array_equal(np.isneginf(a), np.isneginf(b))
+    np.testing.assert_allclose(a[fin], b[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_fp4q_equals_fp8q_when_exact_in_fp8():
+    """e2m1 values times 2^e stay exact in e4m3 for the generator's scales, so the same
+    real q given as fp8 codes (through torch's fp8 conversion) scores identically."""
+    case = syn.make_paged_case([500, 90], [2, 3], seed=970, kv_format=1, block_kv=32, max_ctx=512, q_fp4=True)
+    qv = brute.q_dequant(case)
+    codes = syn.fp8_codes(torch.from_numpy(qv.astype(np.float32)))
+    assert np.array_equal(codes.view(torch.float8_e4m3fn).double().numpy(), qv)
+    c8 = syn.PagedCase(**{**case.__dict__, "q": codes, "q_scale": None})
+    a, b = oracle.paged_logits(case), oracle.paged_logits(c8)
+    assert np.array_equal(a, b)
+    # the scales matter: one changed scale byte changes that head's scores
+    c2 = syn.PagedCase(**{**case.__dict__, "q_scale": case.q_scale.clone()})
+    c2.q_scale[0, 5, 1] += 1
+    assert not np.array_equal(oracle.paged_logits(c2)[0], a[0])
