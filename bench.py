@@ -37,6 +37,7 @@ import pml_synth as syn  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense fp4 MFMA (both operands e2m1)
 BYTES_PER_TOKEN = {syn.KV_FP8: 132, syn.KV_FP4: 68}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "paged_logits_fp8_varlen120k_traffic.md")
 
@@ -84,6 +85,7 @@ class PagedBench:
         d = torch.device("cuda:0")
         self.case = case
         self.q = case.q.to(d)
+        self.q_scale = None if case.q_scale is None else case.q_scale.to(d)
         self.w = case.weights.to(d)
         self.lens = case.context_lens.to(d)
         self.bt = case.block_table.to(d)
@@ -113,7 +115,8 @@ class PagedBench:
             ev[1].record()
         pml.fp8_fp4_paged_mqa_logits(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt, self.sched,
                                      c.max_ctx, self.indices, kv_format=c.kv_format, block_kv=c.block_kv,
-                                     next_n=c.next_n, logits=self.logits_bf16 if self.bf16 else self.logits)
+                                     next_n=c.next_n, logits=self.logits_bf16 if self.bf16 else self.logits,
+                                     q_scale=self.q_scale)
         if ev is not None:
             ev[2].record()
         if self.bf16:
@@ -278,7 +281,8 @@ def paged_summary(name: str, b: PagedBench, wall: float, per: np.ndarray, steps:
             "ms_schedule": float(per[:, 0].mean()), "ms_logits": t_log * 1e3, "ms_topk": float(per[:, 2].mean()),
             "scored_Ktok_s": b.pairs / (wall / steps) / 1e3,
             "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
-            "logits_mfma_frac": b.pairs * 2 * c.H * c.D / t_log / 1e12 / PEAK_FP8_TFLOPS,
+            "logits_mfma_frac": b.pairs * 2 * c.H * c.D / t_log / 1e12 /
+                                (PEAK_FP4_TFLOPS if c.q_scale is not None else PEAK_FP8_TFLOPS),
             "logits_out_bytes": c.rows * c.max_ctx * 4, **describe(c)}
 
 
@@ -351,6 +355,8 @@ def main():
     if args.all:
         others = [("uniform_decode_fp8_32k", lambda: PagedBench(syn.config_uniform_decode(), args.copies * 2)),
                   ("varlen_spec_decode_mxfp4_64k", lambda: PagedBench(syn.config_varlen_fp4(), args.copies * 2)),
+                  ("varlen_spec_decode_mxfp4_64k_fp4q",
+                   lambda: PagedBench(syn.config_varlen_fp4(q_fp4=True), args.copies * 2)),
                   ("tiny_decode_fp8", lambda: PagedBench(syn.config_tiny_decode(), 1))]
         for name, mk in others:
             print(f"[bench] {name}", file=sys.stderr, flush=True)

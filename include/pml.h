@@ -240,6 +240,32 @@ int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int next_n, int n
                                   int64_t logits_ld, void *stream);
 
 /*
+ * fp8_fp4_paged_mqa_logits_fp4q - the paged logits with fp4 q: the indexer's
+ * FP4 path passes q as a (values, scales) pair (sparse_attn_indexer page,
+ * forward_cuda; the pair is forwarded to fp8_fp4_paged_mqa_logits in
+ * _varlen_decode_rows). The layout is this library's reading: the MXFP4 key
+ * layout applied to q.
+ *   q_values   packed e2m1 [num_rows][num_heads][head_dim / 2], element 2i in
+ *              the low nibble of byte i; 16-B aligned.
+ *   q_scales   e8m0 [num_rows][num_heads][head_dim / 32], one per 32
+ *              consecutive elements; 16-B aligned (else PML_ERR_ALIGN; NULL
+ *              with rows is PML_ERR_NULL).
+ *   kv_format  must be PML_KV_MXFP4 (else PML_ERR_UNSUPPORTED).
+ * Every other argument means what it means for fp8_fp4_paged_mqa_logits, and
+ * the logits are fp32. Both operands of the scaled MFMA are e2m1, which gfx950
+ * runs at twice the fp8 rate.
+ */
+int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scales, int num_rows,
+                                  int next_n, int num_heads, int head_dim, const void *kv_cache,
+                                  int kv_format, int block_kv, int64_t page_stride_bytes,
+                                  int64_t num_pages, const float *weights,
+                                  const int32_t *context_lens, int context_lens_2d,
+                                  const int32_t *block_table, int64_t block_table_ld,
+                                  int block_table_cols, int32_t *schedule, int num_CUs,
+                                  const int32_t *indices, int max_ctx, float *logits,
+                                  int64_t logits_ld, void *stream);
+
+/*
  * as_fp32_logits - fp32 copy of bf16 logits over each row's valid span, for
  * the fp32 top-k (sparse_attn_indexer page, as_fp32_logits: only columns below
  * the row's end are converted, and the row stride is kept).

@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         if hasattr(L, "fp8_fp4_paged_mqa_logits_bf16"):
             L.fp8_fp4_paged_mqa_logits_bf16.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes
             L.as_fp32_logits.argtypes = [P, I, I64, I, P, P, I64, P]
+        if hasattr(L, "fp8_fp4_paged_mqa_logits_fp4q"):
+            L.fp8_fp4_paged_mqa_logits_fp4q.argtypes = [P, P] + L.fp8_fp4_paged_mqa_logits.argtypes[1:]
         if hasattr(L, "mqa_logits"):
             L.mqa_logits.argtypes = [P, I, I, I, P, P, I, P, P, P, P, I64, P]
         if hasattr(L, "top_k_per_row"):
@@ -77,7 +79,7 @@ def lib() -> ctypes.CDLL:
             L.stable_topk_from_gathered_candidates.argtypes = [P, I, I, I, P, I64, P]
         for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
                      "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
-                     "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits"):
+                     "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q"):
             if hasattr(L, name):
                 getattr(L, name).restype = I
         L.pml_status_string.argtypes = [I]
@@ -188,11 +190,14 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
                              indices: torch.Tensor | None = None, *, kv_format: int = KV_FP8,
                              block_kv: int = 64, next_n: int = 1,
                              logits: torch.Tensor | None = None,
-                             out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+                             out_dtype: torch.dtype = torch.float32,
+                             q_scale: torch.Tensor | None = None) -> torch.Tensor:
     """Paged logits [rows, ld >= max_model_len], fp32 or bf16 (``out_dtype``, or
     the dtype of a given ``logits``); columns past each row's visible length are
     -inf. ``kv_cache`` is [num_pages, page_stride_bytes] uint8 (a row stride
-    larger than the page is allowed)."""
+    larger than the page is allowed). With ``q_scale`` (uint8 e8m0 [rows, heads,
+    head_dim / 32]) q is packed e2m1 [rows, heads, head_dim / 2] (MXFP4 keys,
+    fp32 logits)."""
     _dev(q, "q", _FP8_TYPES)
     _dev(kv_cache, "kv_cache", (torch.uint8,))
     _dev(weights, "weights", _F32)
@@ -201,6 +206,14 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     _dev(schedule, "schedule", _I32)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [rows, heads, head_dim] tensor")
+    head_dim = q.shape[2]
+    if q_scale is not None:
+        _dev(q_scale, "q_scale", (torch.uint8,))
+        head_dim = 2 * q.shape[2]
+        if tuple(q_scale.shape) != (q.shape[0], q.shape[1], head_dim // 32) or not q_scale.is_contiguous():
+            raise ValueError("q_scale must be a contiguous uint8 [rows, heads, head_dim / 32] tensor")
+        if out_dtype != torch.float32 or (logits is not None and logits.dtype != torch.float32):
+            raise ValueError("fp4 q writes fp32 logits")
     if kv_cache.dim() != 2 or kv_cache.stride(1) != 1:
         raise ValueError("kv_cache must be [num_pages, page_stride] with unit inner stride")
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -222,9 +235,14 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     num_cus = schedule_workers(schedule)
     if not schedule.is_contiguous():
         raise ValueError("schedule must be contiguous")
-    call = lib().fp8_fp4_paged_mqa_logits if logits.dtype == torch.float32 else lib().fp8_fp4_paged_mqa_logits_bf16
+    if q_scale is not None:
+        call, lead = lib().fp8_fp4_paged_mqa_logits_fp4q, (_p(q), _p(q_scale))
+    elif logits.dtype == torch.float32:
+        call, lead = lib().fp8_fp4_paged_mqa_logits, (_p(q),)
+    else:
+        call, lead = lib().fp8_fp4_paged_mqa_logits_bf16, (_p(q),)
     _check(call(
-        _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
+        *lead, rows, next_n, q.shape[1], head_dim, _p(kv_cache), kv_format, block_kv,
         kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
         block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
         max_model_len, _p(logits), logits.stride(0), _stream()), "fp8_fp4_paged_mqa_logits")

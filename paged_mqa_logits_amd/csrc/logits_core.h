@@ -137,6 +137,64 @@ __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int
         if (tid + k * NTH < g * PML_HEADS) s_w[tid + k * NTH] = wv[k];
 }
 
+// fp4 q (packed e2m1 values [H][D/2] and e8m0 scales [H][D/32] per row, the
+// MXFP4 key layout) in the same 8-KB LDS row: head h's 64 value bytes at
+// h * 64, its 16-B chunk c (k-block c) at chunk position c ^ ((h >> 2) & 3) so
+// that the 16 heads of an A-operand read land in distinct banks, then the
+// scales, 4 bytes per head, from byte 4096.
+constexpr int kQ4Values = PML_HEADS * PML_HEAD_DIM / 2;  // 4096
+constexpr int kQ4Scales = PML_HEADS * PML_HEAD_DIM / 32;  // 256
+__device__ __forceinline__ int q4_lds_off(int h, int c) { return h * (PML_HEAD_DIM / 2) + ((c ^ ((h >> 2) & 3)) << 4); }
+
+// Stage fp4 q (values and scales) and w of rows r0 .. r0 + g - 1 into LDS,
+// every load issued before the first store.
+template <int NTH = kLThreads>
+__device__ __forceinline__ void stage_rows_q4(const uint8_t *qv, const uint8_t *qs, const float *w, int64_t r0,
+                                              int g, uint8_t *s_q, float *s_w) {
+    constexpr int kVC = kQ4Values / 16, kSC = kQ4Scales / 16, kRow = kVC + kSC;  // 16-B chunks
+    constexpr int kPer = (kGMax * kRow + NTH - 1) / NTH;
+    constexpr int kWPer = (kGMax * PML_HEADS + NTH - 1) / NTH;
+    const int tid = threadIdx.x;
+    const int nchunk = g * kRow;
+    v4i x[kPer];
+    float wv[kWPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * NTH;
+        if (i < nchunk) {
+            const int row = i / kRow, rem = i % kRow;
+            const uint8_t *src = rem < kVC ? qv + (r0 + row) * kQ4Values + rem * 16
+                                           : qs + (r0 + row) * kQ4Scales + (rem - kVC) * 16;
+            x[k] = *(const v4i *)src;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kWPer; ++k)
+        if (tid + k * NTH < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * NTH];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * NTH;
+        if (i < nchunk) {
+            const int row = i / kRow, rem = i % kRow;
+            const int off = rem < kVC ? q4_lds_off(rem / 4, rem % 4) : kQ4Values + (rem - kVC) * 16;
+            *(v4i *)(s_q + row * kQBytes + off) = x[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kWPer; ++k)
+        if (tid + k * NTH < g * PML_HEADS) s_w[tid + k * NTH] = wv[k];
+}
+
+// A operand of fp4 q (heads 16 ht + lane % 16, k-block lane / 16: one 16-B
+// chunk, the upper half of the operand unused) and its e8m0 scale in bits 0-7.
+__device__ __forceinline__ v8i load_a_q4(const uint8_t *s_qrow, int ht, int &scale) {
+    const int lane = lane_id();
+    const int h = 16 * ht + (lane & 15), grp = lane >> 4;
+    const v4i v = lds_ld<v4i>(s_qrow + q4_lds_off(h, grp));
+    scale = (int)((lds_ld<uint32_t>(s_qrow + kQ4Values + 4 * h) >> (8 * grp)) & 0xffu);
+    return v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+}
+
 // A operand (q of heads 16 ht + lane % 16) of one staged row, in the
 // hardware's k order for v_mfma_scale_f32_16x16x128_f8f6f4 as measured on
 // gfx950: an fp8 operand holds k = 16g .. 16g+15 in bytes 0-15 and
@@ -185,12 +243,16 @@ constexpr int kPipe = 2;  // MFMAs issued ahead of the epilogue that reads them
 // MFMA of one 16-token slice t. fp8 x fp8 takes the unscaled opcode: the
 // scaled form costs an extra VALU instruction per MFMA (it loads the scales),
 // measured as about a fifth more SIMD time for MFMA plus epilogue. MXFP4 keys
-// need their e8m0 block scales, with A at unit scale (`unit` = 127).
-template <bool FP4, int BKV>
-__device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i &a, int t, int unit) {
+// need their e8m0 block scales, with fp8 A at unit scale (`a_scale` = 127) or
+// fp4 A (Q4) at its own e8m0 scale: e2m1 x e2m1 runs at twice the fp8 rate.
+template <bool FP4, int BKV, bool Q4 = false>
+__device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i &a, int t, int a_scale) {
     if constexpr (FP4) {
         const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3], 0, 0, 0, 0};
-        return mfma_scaled<4>(a, b, unit, (int)(k_.sc[t] & 0xffu));
+        if constexpr (Q4)
+            return mfma_scaled_ab<4, 4>(a, b, a_scale, (int)(k_.sc[t] & 0xffu));
+        else
+            return mfma_scaled<4>(a, b, a_scale, (int)(k_.sc[t] & 0xffu));
     } else {
         const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3],
                           k_.v[t][1][0], k_.v[t][1][1], k_.v[t][1][2], k_.v[t][1][3]};
@@ -198,9 +260,10 @@ __device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i
     }
 }
 
-template <bool FP4, int BKV>
+template <bool FP4, int BKV, bool Q4 = false>
 __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const uint8_t *s_qrow,
                                            const float *s_wrow) {
+    static_assert(!Q4 || FP4, "fp4 q pairs with MXFP4 keys");
     using C = BlockCfg<FP4, BKV>;
     const int lane = lane_id();
     const int grp = lane >> 4;
@@ -210,9 +273,13 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
     // all LDS operands of the row first: one wait instead of one per head tile
     v8i av[4];
     v4f wv[4];
+    [[maybe_unused]] int asc[4];  // fp4 q: A scale per head tile
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) {
-        av[ht] = load_a<FP4>(s_qrow, ht);
+        if constexpr (Q4)
+            av[ht] = load_a_q4(s_qrow, ht, asc[ht]);
+        else
+            av[ht] = load_a<FP4>(s_qrow, ht);
         wv[ht] = lds_ld<v4f>(s_wrow + 16 * ht + 4 * grp);
     }
     // MFMA k = (head tile k / NT, slice k % NT) is issued kPipe steps before
@@ -222,18 +289,23 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
     // statements pin the order: each MFMA takes an operand (its A tile, or
     // for MXFP4 the unit A scale) that the asm before it claims to rewrite,
     // and each epilogue reads its result only after the asm that follows the
-    // next MFMAs.
+    // next MFMAs. (fp4 q: the operand is the head tile's A scale.)
     constexpr int NK = 4 * C::NT;
     v4f d[NK];
     int unit = 127;  // e8m0 1.0
 #pragma unroll
     for (int k = 0; k < NK + kPipe; ++k) {
         if (k < NK) {
-            if constexpr (FP4)
-                asm volatile("" : "+v"(unit));
-            else
-                asm volatile("" : "+v"(av[k / C::NT]));
-            d[k] = mfma_slice<FP4, BKV>(k_, av[k / C::NT], k % C::NT, unit);
+            if constexpr (Q4) {
+                asm volatile("" : "+v"(asc[k / C::NT]));
+                d[k] = mfma_slice<FP4, BKV, true>(k_, av[k / C::NT], k % C::NT, asc[k / C::NT]);
+            } else {
+                if constexpr (FP4)
+                    asm volatile("" : "+v"(unit));
+                else
+                    asm volatile("" : "+v"(av[k / C::NT]));
+                d[k] = mfma_slice<FP4, BKV>(k_, av[k / C::NT], k % C::NT, unit);
+            }
         }
         if (k >= kPipe) {
             const int e = k - kPipe, ht = e / C::NT, t = e % C::NT;

@@ -28,7 +28,7 @@
 namespace pml {
 
 struct PagedArgs {
-    const uint8_t *q;
+    const uint8_t *q;  // fp8 codes, or packed e2m1 values (fp4 q)
     const float *w;
     const uint8_t *kv;
     int64_t page_stride;
@@ -42,6 +42,7 @@ struct PagedArgs {
     int max_ctx;
     void *out;  // float, or uint16_t bf16 bits
     int64_t out_ld;
+    const uint8_t *qs;  // fp4 q: e8m0 scales [rows][H][D/32]
 };
 
 // Load block b of the piece whose table row is bt_row; false (and page 0 is
@@ -61,7 +62,7 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 // into the wave's LDS slot. Rows whose visible length ends before the block are
 // skipped (their tail is filled separately). Lane i of vis_lane holds the
 // visible length of row i.
-template <bool FP4, int BKV, typename OT, bool PF>
+template <bool FP4, int BKV, typename OT, bool Q4, bool PF>
 __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int b,
                                           const KeyRegs<FP4, BKV> &kc, bool okc, int bp, KeyRegs<FP4, BKV> &kp,
                                           bool &okp, const uint8_t *s_q, const float *s_w, int vis_lane,
@@ -78,7 +79,7 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
     for (int i = 0; i < g; ++i) {
         const int vis = __builtin_amdgcn_readlane(vis_lane, i);
         if (col0 >= vis) continue;
-        float v = score_row<FP4, BKV>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
+        float v = score_row<FP4, BKV, Q4>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
         if (!okc) v = __builtin_nanf("");
         if (s >= vis) v = -__builtin_inff();
         if (out_lane<BKV>(lane)) lds_st<float>(&sl.v[i][tok], v);
@@ -114,7 +115,7 @@ struct Draw {
 // loads behind its wait). The first blocks are requested before q is staged,
 // so the two memory round trips overlap. With draw_here, the wave issues the
 // draw DrawAhead steps before its blocks end.
-template <bool FP4, int BKV, typename OT>
+template <bool FP4, int BKV, typename OT, bool Q4>
 __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int64_t bt_row, int b0, int nmy,
                                           uint8_t *s_q, float *s_w, int *s_vis, WaveSlot<BKV> &sl, Draw &dr,
                                           bool draw_here) {
@@ -127,7 +128,10 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 #pragma unroll
         for (int u = 0; u < kDepth; ++u) okb[u] = fetch_block<FP4, BKV>(a, bt_row, b0 + min(u, last), kb[u]);
     }
-    stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w);
+    if constexpr (Q4)
+        stage_rows_q4<kPThreads>(a.q, a.qs, a.w, r0, g, s_q, s_w);
+    else
+        stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w);
     if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
     barrier_lds();
     const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
@@ -138,7 +142,7 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
             for (int u = 0; u < NB; ++u) {
                 if (j + u >= nmy) break;
                 if (draw_here && j + u == max(nmy - kDrawAhead, 0)) dr.issue();
-                wave_step<FP4, BKV, OT, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
+                wave_step<FP4, BKV, OT, Q4, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
                                           kb[(u + kDepth) % NB], okb[(u + kDepth) % NB], s_q, s_w, vis_lane, sl, mask,
                                           col0p);
             }
@@ -150,7 +154,7 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 // The units from chunk e0's start to chunk e1's start (the whole workgroup).
 // Wave 0 issues the draw kDrawAhead steps before its share of the last piece
 // ends; a range too short for that leaves it to the caller.
-template <bool FP4, int BKV, typename OT>
+template <bool FP4, int BKV, typename OT, bool Q4>
 __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, uint8_t *s_q, float *s_w, int *s_vis,
                                            WaveSlot<BKV> &sl, Draw &dr) {
     const int tid = threadIdx.x;
@@ -175,14 +179,14 @@ __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, u
             const int b0 = blk_lo + wave * per + min(wave, rem);
             const int nmy = per + (wave < rem ? 1 : 0);
             const bool draw_here = last_piece && wave == 0 && !dr.done;
-            run_piece<FP4, BKV, OT>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
+            run_piece<FP4, BKV, OT, Q4>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
         }
         r0 = rn;
         blk_lo = 0;
     }
 }
 
-template <bool FP4, int BKV, typename OT>
+template <bool FP4, int BKV, typename OT, bool Q4>
 __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
@@ -216,7 +220,7 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     int e0 = kStaticChunks * c, e1 = kStaticChunks * (c + 1);
     for (int par = 0;; par ^= 1) {
         dr.done = false;
-        run_chunks<FP4, BKV, OT>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
+        run_chunks<FP4, BKV, OT, Q4>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
         if (!dr.done) dr.issue();
         if (tid == 0) lds_st<unsigned>(&s_take[par], (unsigned)(dr.v % (Dx + Wx)));
         barrier_lds();  // (also: every wave is done reading s_take[par ^ 1])
@@ -234,9 +238,9 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     }
 }
 
-template <bool FP4, int BKV, typename OT>
+template <bool FP4, int BKV, typename OT, bool Q4 = false>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT>), dim3(W), dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT, Q4>), dim3(W), dim3(kPThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
@@ -244,9 +248,10 @@ static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
 
 static inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-// Shared by the fp32 and bf16 entry points (bf16: logits are uint16_t bits and
-// rows must be 16-B aligned, logits_ld a multiple of 8).
-static int paged_logits(const void *q, int num_rows, int next_n, int num_heads, int head_dim,
+// Shared by the fp32, bf16 and fp4-q entry points (bf16: logits are uint16_t
+// bits and rows must be 16-B aligned, logits_ld a multiple of 8; fp4 q:
+// q_scale given, MXFP4 keys only).
+static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_rows, int next_n, int num_heads, int head_dim,
                         const void *kv_cache, int kv_format, int block_kv, int64_t page_stride_bytes,
                         int64_t num_pages, const float *weights, const int32_t *context_lens,
                         int context_lens_2d, const int32_t *block_table, int64_t block_table_ld,
@@ -258,7 +263,10 @@ static int paged_logits(const void *q, int num_rows, int next_n, int num_heads, 
     if (block_kv != 32 && block_kv != 64) return PML_ERR_BLOCK_KV;
     if (indices && next_n != 1) return PML_ERR_VARLEN_NEXT_N;
     if (num_rows % next_n != 0) return PML_ERR_SHAPE;
+    if (q4 && kv_format != PML_KV_MXFP4) return PML_ERR_UNSUPPORTED;
     if (num_rows == 0) return PML_OK;
+    if (q4 && !q_scale) return PML_ERR_NULL;
+    if (q4 && !al16(q_scale)) return PML_ERR_ALIGN;
     if (!q || !kv_cache || !weights || !context_lens || !block_table || !schedule || !logits)
         return PML_ERR_NULL;
     if (paged_mqa_logits_schedule_rows(num_CUs) < 0) return PML_ERR_SHAPE;
@@ -271,6 +279,7 @@ static int paged_logits(const void *q, int num_rows, int next_n, int num_heads, 
     if (!al16(q) || !al16(kv_cache) || !al16(weights) || !al16(logits) || !al16(schedule)) return PML_ERR_ALIGN;
     pml::PagedArgs a;
     a.q = (const uint8_t *)q;
+    a.qs = q_scale;
     a.w = weights;
     a.kv = (const uint8_t *)kv_cache;
     a.page_stride = page_stride_bytes;
@@ -285,6 +294,9 @@ static int paged_logits(const void *q, int num_rows, int next_n, int num_heads, 
     a.out = logits;
     a.out_ld = logits_ld;
     hipStream_t st = (hipStream_t)stream;
+    if (q4)
+        return block_kv == 64 ? pml::launch_paged<true, 64, float, true>(a, num_CUs, st)
+                              : pml::launch_paged<true, 32, float, true>(a, num_CUs, st);
     if (bf16) {
         if (kv_format == PML_KV_FP8)
             return block_kv == 64 ? pml::launch_paged<false, 64, uint16_t>(a, num_CUs, st)
@@ -308,7 +320,7 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n,
                                         int32_t *schedule, int num_CUs,
                                         const int32_t *indices, int max_ctx, float *logits,
                                         int64_t logits_ld, void *stream) {
-    return paged_logits(q, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
+    return paged_logits(q, false, nullptr, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
                         page_stride_bytes, num_pages, weights, context_lens, context_lens_2d, block_table,
                         block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx, logits,
                         logits_ld, false, stream);
@@ -323,8 +335,23 @@ extern "C" int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int ne
                                              int32_t *schedule, int num_CUs,
                                              const int32_t *indices, int max_ctx, uint16_t *logits,
                                              int64_t logits_ld, void *stream) {
-    return paged_logits(q, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
+    return paged_logits(q, false, nullptr, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
                         page_stride_bytes, num_pages, weights, context_lens, context_lens_2d, block_table,
                         block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx, logits,
                         logits_ld, true, stream);
+}
+
+extern "C" int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scales, int num_rows,
+                                             int next_n, int num_heads, int head_dim, const void *kv_cache,
+                                             int kv_format, int block_kv, int64_t page_stride_bytes,
+                                             int64_t num_pages, const float *weights,
+                                             const int32_t *context_lens, int context_lens_2d,
+                                             const int32_t *block_table, int64_t block_table_ld,
+                                             int block_table_cols, int32_t *schedule, int num_CUs,
+                                             const int32_t *indices, int max_ctx, float *logits,
+                                             int64_t logits_ld, void *stream) {
+    return paged_logits(q_values, true, q_scales, num_rows, next_n, num_heads,
+                        head_dim, kv_cache, kv_format, block_kv, page_stride_bytes, num_pages, weights,
+                        context_lens, context_lens_2d, block_table, block_table_ld, block_table_cols, schedule,
+                        num_CUs, indices, max_ctx, logits, logits_ld, false, stream);
 }

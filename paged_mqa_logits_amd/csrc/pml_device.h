@@ -115,6 +115,14 @@ __device__ __forceinline__ v4f mfma_scaled(const v8i &a, const v8i &b, int a_sca
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, FMT_B, 0, a_scale, 0, b_scale);
 }
 
+// D = A(16x128) * B(128x16) with both operand formats given (0 fp8, 4 e2m1)
+// and an e8m0 scale per row / column and 32-block of k for each.
+template <int FMT_A, int FMT_B>
+__device__ __forceinline__ v4f mfma_scaled_ab(const v8i &a, const v8i &b, int a_scale, int b_scale) {
+    v4f z = {0.f, 0.f, 0.f, 0.f};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, FMT_A, FMT_B, 0, a_scale, 0, b_scale);
+}
+
 // Exchange halves between two registers (gfx950 v_permlane32_swap / 16_swap).
 // swap32(x, y): x <- (x.lanes[0,32), y.lanes[0,32)), y <- (x.lanes[32,64), y.lanes[32,64)).
 __device__ __forceinline__ void swap32(float &x, float &y) {

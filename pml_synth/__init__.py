@@ -360,13 +360,14 @@ def config_varlen_fp8(seed: int = 1003, R: int = 40, lo: int = 102400, hi: int =
 
 
 def config_varlen_fp4(seed: int = 1004, R: int = 64, lo: int = 32768, hi: int = 65536,
-                      max_ctx: int = 65536) -> PagedCase:
-    """64 requests, ctx U[32K,64K], lengths U{1..4}, MXFP4 K, block_kv 32."""
+                      max_ctx: int = 65536, q_fp4: bool = False) -> PagedCase:
+    """64 requests, ctx U[32K,64K], lengths U{1..4}, MXFP4 K, block_kv 32
+    (with q_fp4, q MX-quantised from the same draw)."""
     g = _gen(seed)
     ctx = _randint(g, lo, hi, R)
     nrows = _randint(g, 1, 4, R)
     return make_paged_case(ctx, nrows, seed=seed + 100, kv_format=KV_FP4, block_kv=32,
-                           max_ctx=max_ctx, varlen=True, topk=2048)
+                           max_ctx=max_ctx, varlen=True, topk=2048, q_fp4=q_fp4)
 
 
 def config_ragged_prefill(seed: int = 1005, nseq: int = 4, L: int = 8192) -> RaggedCase:

@@ -37,7 +37,8 @@ def upload(case: syn.PagedCase) -> dict:
     d = dev()
     return dict(
         q=case.q.to(d), kv=case.kv_cache.to(d), w=case.weights.to(d), lens=case.context_lens.to(d),
-        bt=case.block_table.to(d), indices=None if case.indices is None else case.indices.to(d))
+        bt=case.block_table.to(d), indices=None if case.indices is None else case.indices.to(d),
+        qs=None if case.q_scale is None else case.q_scale.to(d))
 
 
 def run_paged(case: syn.PagedCase, t: dict | None = None, *, num_cus=None, indices="case",
@@ -51,7 +52,7 @@ def run_paged(case: syn.PagedCase, t: dict | None = None, *, num_cus=None, indic
     out = torch.full((case.rows, ld), SENTINEL, dtype=torch.float32, device=dev())
     pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx, idx,
                                  kv_format=case.kv_format, block_kv=case.block_kv, next_n=case.next_n,
-                                 logits=out)
+                                 logits=out, q_scale=t["qs"])
     torch.cuda.synchronize()
     o = out.cpu().numpy()
     assert np.all(o[:, case.max_ctx:] == SENTINEL), "columns past max_ctx were written"

@@ -22,7 +22,7 @@ def test_header_declares_the_four_calls():
     for n in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
               "top_k_per_row_workspace_size", "pml_status_string", "pml_version",
               "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
-              "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits"):
+              "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q"):
         assert n in names
 
 
@@ -178,3 +178,24 @@ def test_upcast_validation(kw, code):
 def test_upcast_empty_is_ok():
     assert _upcast(rows=0) == 0
     assert _upcast(cols=0) == 0
+
+
+def _paged_fp4q(**kw):
+    a = dict(q=FAKE, qs=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=1, bkv=32, stride=32 * 68, pages=10,
+             w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
+             max_ctx=256, out=FAKE, ld=256, stream=None)
+    a.update(kw)
+    return pml.lib().fp8_fp4_paged_mqa_logits_fp4q(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=0, bkv=64, stride=64 * 132), 10), (dict(fmt=0, bkv=64, stride=64 * 132, rows=0), 10),
+    (dict(qs=None), 1), (dict(q=None), 1), (dict(qs=P(0x1008)), 6), (dict(H=32), 2), (dict(bkv=16), 3),
+    (dict(ld=252), 5),
+])
+def test_paged_fp4q_validation(kw, code):
+    assert _paged_fp4q(**kw) == code
+
+
+def test_paged_fp4q_zero_rows():
+    assert _paged_fp4q(rows=0, qs=None) == 0
