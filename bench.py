@@ -81,7 +81,8 @@ class PagedBench:
     the logits are written as bf16 and upcast over each row's span for the top-k
     (four calls)."""
 
-    def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None, bf16: bool = False):
+    def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None, bf16: bool = False,
+                 fused: bool = False):
         d = torch.device("cuda:0")
         self.case = case
         self.q = case.q.to(d)
@@ -95,7 +96,11 @@ class PagedBench:
         self.sched = torch.empty(pml.schedule_rows(self.num_cus), 2, dtype=torch.int32, device=d)
         self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
         self.bf16 = bf16
-        self.nev = 5 if bf16 else 4
+        self.fused = fused
+        self.nev = 5 if bf16 else (3 if fused else 4)
+        if fused:
+            need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, case.topk)
+            self.ws = torch.empty(need, dtype=torch.uint8, device=d)
         if bf16:
             assert case.next_n == 1
             ld = (case.max_ctx + 7) // 8 * 8
@@ -113,6 +118,14 @@ class PagedBench:
                                       next_n=c.next_n, out=self.sched)
         if ev is not None:
             ev[1].record()
+        if self.fused:
+            pml.fp8_fp4_paged_mqa_logits_topk(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt,
+                                              self.sched, c.max_ctx, c.topk, self.indices, kv_format=c.kv_format,
+                                              block_kv=c.block_kv, next_n=c.next_n, logits=self.logits,
+                                              out=self.topk, workspace=self.ws)
+            if ev is not None:
+                ev[2].record()
+            return
         pml.fp8_fp4_paged_mqa_logits(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt, self.sched,
                                      c.max_ctx, self.indices, kv_format=c.kv_format, block_kv=c.block_kv,
                                      next_n=c.next_n, logits=self.logits_bf16 if self.bf16 else self.logits,
@@ -380,6 +393,16 @@ def main():
                           "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
                           "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
                           "logits_out_bytes": c.rows * c.max_ctx * 2}), file=sys.stderr, flush=True)
+        del ob
+        print("[bench] varlen_spec_decode_fp8_120k_fused", file=sys.stderr, flush=True)
+        ob = PagedBench(syn.config_varlen_fp8(), args.copies, fused=True)
+        w2, p2 = run_timed(ob, args.steps, args.warmup)
+        if not args.no_graph:
+            w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
+        print(json.dumps({"workload": "varlen_spec_decode_fp8_120k_fused_logits_topk",
+                          "ms_per_step": w2 / args.steps * 1e3, "ms_schedule": float(p2[:, 0].mean()),
+                          "ms_fused_logits_topk": float(p2[:, 1].mean()),
+                          "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3}), file=sys.stderr, flush=True)
         del ob
         print("[bench] dcp_merge_8ranks", file=sys.stderr, flush=True)
         db = DcpBench(syn.config_varlen_fp8())

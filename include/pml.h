@@ -266,6 +266,49 @@ int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scal
                                   int64_t logits_ld, void *stream);
 
 /*
+ * fp8_fp4_paged_mqa_logits_topk - the paged logits and their per-row top-k in
+ * one call, the top-k taken from candidates the logits kernel keeps instead of
+ * a second full pass over the rows (the indexer page names a fused prefill
+ * top-k and bounds the logits it materialises: sparse_attn_indexer page,
+ * _decode_chunk_ranges; the fused form here is this library's). The first
+ * arguments through logits_ld mean what they mean for
+ * fp8_fp4_paged_mqa_logits (fp8 q), and the fp32 logits are written as that
+ * call writes them. Then:
+ *   k          1..4096 (else PML_ERR_K).
+ *   topk       int32 [num_rows][topk_ld], topk_ld >= k: what top_k_per_row
+ *              writes for these logits with ke = the rows' visible lengths
+ *              (context_lens read as for the logits) and max_width = max_ctx,
+ *              bit for bit.
+ *   workspace  device scratch of at least
+ *              fp8_fp4_paged_mqa_logits_topk_workspace_size(num_rows, max_ctx,
+ *              block_kv, k) bytes, 256-B aligned (else PML_ERR_WORKSPACE /
+ *              PML_ERR_ALIGN). Its contents need no initialisation and are
+ *              garbage afterwards. Layout, each region 256-B aligned:
+ *              thresholds fp32 [num_rows], widths int32 [num_rows], done flags
+ *              int32 [num_rows], candidate counts int32 [num_rows][nb], then
+ *              candidate lists fp32 [num_rows][nb * block_kv][2], with
+ *              nb = ceil(max_ctx / block_kv).
+ * How: a first kernel scores an evenly spaced sample of each wide row's blocks
+ * and sets a threshold that about 2k of the row's columns are expected to
+ * reach (rows of at most 4k columns take every finite logit). The logits
+ * kernel also writes, per row and key block, the columns at or above the
+ * threshold. A selection kernel takes the k best of a row's candidates when
+ * there are k to 4k of them; every other row goes through the full top-k over
+ * the written logits, so the result is exact for any data.
+ */
+size_t fp8_fp4_paged_mqa_logits_topk_workspace_size(int num_rows, int max_ctx, int block_kv, int k);
+int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int next_n, int num_heads,
+                                  int head_dim, const void *kv_cache, int kv_format,
+                                  int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                  const float *weights, const int32_t *context_lens,
+                                  int context_lens_2d, const int32_t *block_table,
+                                  int64_t block_table_ld, int block_table_cols,
+                                  int32_t *schedule, int num_CUs,
+                                  const int32_t *indices, int max_ctx, float *logits,
+                                  int64_t logits_ld, int k, int32_t *topk, int64_t topk_ld,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * as_fp32_logits - fp32 copy of bf16 logits over each row's valid span, for
  * the fp32 top-k (sparse_attn_indexer page, as_fp32_logits: only columns below
  * the row's end are converted, and the row stride is kept).

@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
         if hasattr(L, "fp8_fp4_paged_mqa_logits_bf16"):
             L.fp8_fp4_paged_mqa_logits_bf16.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes
             L.as_fp32_logits.argtypes = [P, I, I64, I, P, P, I64, P]
+        if hasattr(L, "fp8_fp4_paged_mqa_logits_topk"):
+            L.fp8_fp4_paged_mqa_logits_topk.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes[:-1] + [I, P, I64, P, SZ, P]
+            L.fp8_fp4_paged_mqa_logits_topk_workspace_size.argtypes = [I, I, I, I]
+            L.fp8_fp4_paged_mqa_logits_topk_workspace_size.restype = SZ
         if hasattr(L, "fp8_fp4_paged_mqa_logits_fp4q"):
             L.fp8_fp4_paged_mqa_logits_fp4q.argtypes = [P, P] + L.fp8_fp4_paged_mqa_logits.argtypes[1:]
         if hasattr(L, "mqa_logits"):
@@ -79,7 +83,8 @@ def lib() -> ctypes.CDLL:
             L.stable_topk_from_gathered_candidates.argtypes = [P, I, I, I, P, I64, P]
         for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
                      "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
-                     "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q"):
+                     "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q",
+                     "fp8_fp4_paged_mqa_logits_topk"):
             if hasattr(L, name):
                 getattr(L, name).restype = I
         L.pml_status_string.argtypes = [I]
@@ -359,3 +364,49 @@ def stable_topk_from_gathered_candidates(gathered: torch.Tensor, k: int,
                                                       _stream()),
            "stable_topk_from_gathered_candidates")
     return out
+
+
+def fused_topk_workspace_size(rows: int, max_model_len: int, block_kv: int, k: int) -> int:
+    return int(lib().fp8_fp4_paged_mqa_logits_topk_workspace_size(rows, max_model_len, block_kv, k))
+
+
+def fp8_fp4_paged_mqa_logits_topk(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
+                                  context_lens: torch.Tensor, block_table: torch.Tensor,
+                                  schedule: torch.Tensor, max_model_len: int, k: int,
+                                  indices: torch.Tensor | None = None, *, kv_format: int = KV_FP8,
+                                  block_kv: int = 64, next_n: int = 1, logits: torch.Tensor | None = None,
+                                  out: torch.Tensor | None = None,
+                                  workspace: torch.Tensor | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Paged logits (fp32, as fp8_fp4_paged_mqa_logits writes them) and their per-row
+    top-k (as top_k_per_row over them, max_width = max_model_len) in one call, the
+    top-k taken from candidates the logits kernel keeps. Returns (logits, topk)."""
+    _dev(q, "q", _FP8_TYPES)
+    _dev(kv_cache, "kv_cache", (torch.uint8,))
+    _dev(weights, "weights", _F32)
+    _dev(context_lens, "context_lens", _I32)
+    _dev(block_table, "block_table", _I32)
+    _dev(schedule, "schedule", _I32)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [rows, heads, head_dim] tensor")
+    weights = weights.contiguous()
+    context_lens = context_lens.contiguous()
+    if indices is not None:
+        indices = _dev(indices, "indices", _I32).contiguous()
+    rows, l2d = _rows_of(context_lens, next_n, indices)
+    if rows != q.shape[0]:
+        raise ValueError(f"q has {q.shape[0]} rows but the lengths describe {rows}")
+    if logits is None:
+        logits = torch.empty(rows, logits_ld(max_model_len), dtype=torch.float32, device=q.device)
+    if out is None:
+        out = torch.empty(rows, max(k, 1), dtype=torch.int32, device=q.device)
+    need = fused_topk_workspace_size(rows, max_model_len, block_kv, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    num_cus = schedule_workers(schedule)
+    _check(lib().fp8_fp4_paged_mqa_logits_topk(
+        _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
+        kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
+        block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
+        max_model_len, _p(logits), logits.stride(0), k, _p(out), out.stride(0), _p(workspace),
+        workspace.numel() * workspace.element_size(), _stream()), "fp8_fp4_paged_mqa_logits_topk")
+    return logits, out

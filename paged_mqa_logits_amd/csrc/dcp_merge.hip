@@ -25,6 +25,7 @@
 //    per lane: strides below E inside a lane's registers, strides inside a
 //    wave by DPP / swizzle lane exchanges, the last few through LDS.
 #include "select.h"
+#include "fused.h"
 
 namespace pml {
 
@@ -66,98 +67,11 @@ struct MergeArgs {
     int64_t out_ld;
 };
 
-// One radix pass: histogram of bits [shift, shift + log2(nbins)) of key(i)
-// over the pairs live(i) whose key matches prefix under mask, then the bin of
-// the kk-th largest. Returns that bin's count; s_pick holds (bin, count above).
-template <int P, typename K, typename L>
-__device__ __forceinline__ uint32_t radix_pass(K key, L live, uint32_t prefix, uint32_t mask, int shift, int nbins,
-                                               uint32_t kk, uint32_t *s_hist, uint32_t *s_wave, uint32_t *s_pick) {
-    for (int b = threadIdx.x; b < nbins; b += kMergeThreads) s_hist[b] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const uint32_t x = key(i);
-        if (live(i) && (x & mask) == prefix) atomicAdd(&s_hist[(x >> shift) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    pick_bin<kMergeThreads>(s_hist, nbins, kk, s_wave, s_pick);
-    const uint32_t cnt = s_hist[s_pick[0]];
-    __syncthreads();
-    return cnt;
-}
-
-// Value of lane (lane ^ m) of the wave, m a power of two below 64 (a
-// constant once the caller's loops are unrolled).
-__device__ __forceinline__ int32_t lane_xor(int32_t v, int m) {
-    switch (m) {
-        case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
-        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
-        case 4: return __builtin_amdgcn_ds_swizzle(v, 0x101F);                       // xor 4 in 32 lanes
-        case 8: return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);  // row_ror:8 = xor 8
-        case 16: return __builtin_amdgcn_ds_swizzle(v, 0x401F);                      // xor 16 in 32 lanes
-        default: return __shfl_xor(v, 32, kWave);
-    }
-}
-
-constexpr int kSortThreads = 256;  // the four waves that run the sort
-
-// Ascending bitonic sort of s[0, kSortThreads * E): every thread of the
-// workgroup calls it (it holds the barriers); threads below kSortThreads load
-// entries t * E .. t * E + E - 1 from s, sort, and leave them in x.
-template <int E>
-__device__ __forceinline__ void bitonic_sort(int32_t (&x)[E], int32_t *s) {
-    constexpr int NS = kSortThreads * E;
-    const int t = threadIdx.x;
-    const bool active = t < kSortThreads;
-    if (active) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = s[t * E + e];
-    }
-#pragma unroll
-    for (int sz = 2; sz <= NS; sz <<= 1) {
-#pragma unroll
-        for (int j = sz >> 1; j > 0; j >>= 1) {
-            if (j < E) {
-                if (active) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e)
-                        if ((e & j) == 0) {
-                            const bool asc = ((t * E + e) & sz) == 0;
-                            const int32_t lo = min(x[e], x[e | j]), hi = max(x[e], x[e | j]);
-                            x[e] = asc ? lo : hi;
-                            x[e | j] = asc ? hi : lo;
-                        }
-                }
-                continue;
-            }
-            int32_t y[E];
-            if (j < kWave * E) {
-                if (!active) continue;
-#pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = lane_xor(x[e], j / E);
-            } else {
-                __syncthreads();  // earlier reads of s are done
-                if (active) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) s[t * E + e] = x[e];
-                }
-                __syncthreads();
-                if (!active) continue;
-#pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = s[(t * E + e) ^ j];
-            }
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int i = t * E + e;
-                const bool keep_low = ((i & j) == 0) == ((i & sz) == 0);
-                x[e] = keep_low ? min(x[e], y[e]) : max(x[e], y[e]);
-            }
-        }
-    }
-}
-
+// The k best of the pairs (key[i], id[i]) the workgroup holds (id < 0: no
+// pair), P per thread: their ids in ascending order, then -1, into out_row[0, k).
 template <int P, int E>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void select_k_ids(const uint32_t (&key)[P], const int32_t (&id)[P], uint32_t nmine,
+                                             int k, int32_t *out_row) {
     constexpr int NT = kMergeThreads;
     constexpr int NS = kSortThreads * E;  // sorted entries (>= k)
     __shared__ uint32_t s_hist[2048];
@@ -167,29 +81,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     __shared__ uint32_t s_nsel;
     const int tid = threadIdx.x;
     if (tid == 0) s_nsel = 0;  // (published by the barriers of the first scan)
-    const int r = blockIdx.x;
-    const int k = a.k;
-    const int M = a.world * k;
-
-    // pairs c = i * NT + tid: rank c / k, slot c % k
-    float2 v[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int c = min(i * NT + tid, M - 1);
-        const int w = c / k;
-        const int j = c - w * k;
-        v[i] = *reinterpret_cast<const float2 *>(a.gathered + (((int64_t)w * a.rows + r) * k + j) * 2);
-    }
-    uint32_t key[P];
-    int32_t id[P];
-    uint32_t nmine = 0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const bool ok = i * NT + tid < M && v[i].y >= 0.0f && v[i].y < (float)kIdLimit;
-        key[i] = order_key(v[i].x);
-        id[i] = ok ? (int32_t)v[i].y : -1;
-        nmine += ok;
-    }
     uint32_t nvalid;
     block_scan<NT>(nmine, s_wave, &nvalid);
 
@@ -204,7 +95,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
         for (int pass = 0; pass < 3; ++pass) {
             const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
             const int nbins = pass == 2 ? 1024 : 2048;
-            cnt = radix_pass<P>(kf, live, prefix, mask, shift, nbins, kk, s_hist, s_wave, s_pick);
+            cnt = radix_pass<kMergeThreads, P>(kf, live, prefix, mask, shift, nbins, kk, s_hist, s_wave, s_pick);
             prefix |= s_pick[0] << shift;
             mask |= (uint32_t)(nbins - 1) << shift;
             kk -= s_pick[1];
@@ -222,7 +113,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
             for (int pass = 0; pass < 3; ++pass) {
                 const int shift = pass == 0 ? 13 : (pass == 1 ? 2 : 0);
                 const int nbins = pass == 2 ? 4 : 2048;
-                radix_pass<P>(inv, tied, p2, m2, shift, nbins, k2, s_hist, s_wave, s_pick);
+                radix_pass<kMergeThreads, P>(inv, tied, p2, m2, shift, nbins, k2, s_hist, s_wave, s_pick);
                 p2 |= s_pick[0] << shift;
                 m2 |= (uint32_t)(nbins - 1) << shift;
                 k2 -= s_pick[1];
@@ -262,13 +153,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     int32_t x[E];
     bitonic_sort<E>(x, s_ids);
     if (tid < kSortThreads) {
-        int32_t *out = a.out + (int64_t)r * a.out_ld;
+        int32_t *out = out_row;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int j = tid * E + e;
             if (j < k) out[j] = j < m ? x[e] : -1;
         }
     }
+}
+
+
+template <int P, int E>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+    constexpr int NT = kMergeThreads;
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const int k = a.k;
+    const int M = a.world * k;
+
+    // pairs c = i * NT + tid: rank c / k, slot c % k
+    float2 v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int c = min(i * NT + tid, M - 1);
+        const int w = c / k;
+        const int j = c - w * k;
+        v[i] = *reinterpret_cast<const float2 *>(a.gathered + (((int64_t)w * a.rows + r) * k + j) * 2);
+    }
+    uint32_t key[P];
+    int32_t id[P];
+    uint32_t nmine = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const bool ok = i * NT + tid < M && v[i].y >= 0.0f && v[i].y < (float)kIdLimit;
+        key[i] = order_key(v[i].x);
+        id[i] = ok ? (int32_t)v[i].y : -1;
+        nmine += ok;
+    }
+    select_k_ids<P, E>(key, id, nmine, k, a.out + (int64_t)r * a.out_ld);
 }
 
 template <int E>
@@ -281,6 +203,110 @@ static void launch_merge(int P, const MergeArgs &a, hipStream_t st) {
         case 16: hipLaunchKernelGGL((merge_kernel<16, E>), g, b, 0, st, a); break;
         default: hipLaunchKernelGGL((merge_kernel<32, E>), g, b, 0, st, a); break;
     }
+}
+
+// Top-k from a row's candidates (the fused logits + top-k call): rows no
+// wider than k take their columns in order; rows with k to cap candidates
+// select among them (the candidates hold every column scoring at or above the
+// row's threshold, so the k best of the row are among them); other rows are
+// left to the full top-k (done[r] = 0). A scan of the block counts gives each
+// block's first candidate index; candidate c finds its block by a binary
+// search over those in LDS.
+template <int P, int E>
+__global__ __launch_bounds__(kMergeThreads) void cand_select_kernel(CandSelectArgs a) {
+    constexpr int NT = kMergeThreads;
+    constexpr int PB = kSelectMaxBlocks / NT;  // blocks per thread in the scan
+    __shared__ int32_t s_off[kSelectMaxBlocks + 1];
+    __shared__ uint32_t s_tot[kMergeWaves];
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const int k = a.k;
+    const int n = a.width[r];
+    int32_t *out = a.out + (int64_t)r * a.out_ld;
+    if (n <= k) {
+        for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
+        if (tid == 0) a.done[r] = 1;
+        return;
+    }
+    const int nb = (n + a.bkv - 1) / a.bkv;
+    if (nb > kSelectMaxBlocks) {
+        if (tid == 0) a.done[r] = 0;
+        return;
+    }
+    const int32_t *cnt = a.count + (int64_t)r * a.count_ld;
+    int c[PB];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+        const int b = tid * PB + j;
+        c[j] = b < nb ? cnt[b] : 0;
+        mine += (uint32_t)c[j];
+    }
+    uint32_t total;
+    uint32_t off = block_scan<NT>(mine, s_tot, &total) - mine;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+        const int b = tid * PB + j;
+        if (b < nb) s_off[b] = (int)off;
+        off += (uint32_t)c[j];
+    }
+    if (tid == 0) s_off[nb] = (int)total;
+    if (total < (uint32_t)k || total > (uint32_t)a.cap) {
+        if (tid == 0) a.done[r] = 0;
+        return;
+    }
+    __syncthreads();
+    const float *row = a.cand + (int64_t)r * a.cand_ld * 2;
+    float2 v[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int ci = min(i * NT + tid, (int)total - 1);
+        int lo = 0, hi = nb - 1;  // the last block whose first index is <= ci
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= ci)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        v[i] = *reinterpret_cast<const float2 *>(row + 2 * ((int64_t)lo * a.bkv + ci - s_off[lo]));
+    }
+    uint32_t key[P];
+    int32_t id[P];
+    uint32_t nmine = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const bool ok = i * NT + tid < (int)total;
+        key[i] = order_key(v[i].x);
+        id[i] = ok ? (int32_t)v[i].y : -1;
+        nmine += ok;
+    }
+    select_k_ids<P, E>(key, id, nmine, k, out);
+    if (tid == 0) a.done[r] = 1;
+}
+
+template <int E>
+static void launch_cand(int P, const CandSelectArgs &a, int rows, hipStream_t st) {
+    const dim3 g(rows), b(kMergeThreads);
+    switch (P) {
+        case 2: hipLaunchKernelGGL((cand_select_kernel<2, E>), g, b, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((cand_select_kernel<4, E>), g, b, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((cand_select_kernel<8, E>), g, b, 0, st, a); break;
+        default: hipLaunchKernelGGL((cand_select_kernel<16, E>), g, b, 0, st, a); break;
+    }
+}
+
+int launch_cand_select(const CandSelectArgs &a, int num_rows, hipStream_t st) {
+    if (a.cap > 16 * kMergeThreads || a.k > 4 * kSortThreads * 4) return PML_ERR_SHAPE;
+    int P = 2;
+    while (P * kMergeThreads < a.cap) P <<= 1;
+    if (a.k <= 4 * kSortThreads)
+        launch_cand<4>(P, a, num_rows, st);
+    else if (a.k <= 8 * kSortThreads)
+        launch_cand<8>(P, a, num_rows, st);
+    else
+        launch_cand<16>(P, a, num_rows, st);
+    return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
 }  // namespace pml

@@ -24,6 +24,8 @@
 //    workgroups after their units (row-strided).
 #include "logits_core.h"
 #include "rows.h"
+#include "select.h"
+#include "fused.h"
 
 namespace pml {
 
@@ -43,7 +45,23 @@ struct PagedArgs {
     void *out;  // float, or uint16_t bf16 bits
     int64_t out_ld;
     const uint8_t *qs;  // fp4 q: e8m0 scales [rows][H][D/32]
+    // fused top-k: per-row threshold; per (row, block) a candidate count and
+    // a list of up to block_kv (logit, column) pairs, compacted at its start
+    const float *theta;
+    int32_t *ccount;  // [rows][count_ld]
+    float *cand;      // [rows][cand_ld][2], block b's pairs from b * block_kv
+    int64_t count_ld, cand_ld;
 };
+
+__device__ __forceinline__ void store_i32_async(int32_t *p, int v) {
+    asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
+__device__ __forceinline__ void store_v2f_async(float *p, float x, float y) {
+    typedef float v2f_s __attribute__((ext_vector_type(2)));
+    const v2f_s v = {x, y};
+    asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
 
 // Load block b of the piece whose table row is bt_row; false (and page 0 is
 // read) when the table entry is unusable, then the block scores NaN.
@@ -62,11 +80,11 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 // into the wave's LDS slot. Rows whose visible length ends before the block are
 // skipped (their tail is filled separately). Lane i of vis_lane holds the
 // visible length of row i.
-template <bool FP4, int BKV, typename OT, bool Q4, bool PF>
+template <bool FP4, int BKV, typename OT, bool Q4, bool CAND, bool PF>
 __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int b,
                                           const KeyRegs<FP4, BKV> &kc, bool okc, int bp, KeyRegs<FP4, BKV> &kp,
                                           bool &okp, const uint8_t *s_q, const float *s_w, int vis_lane,
-                                          WaveSlot<BKV> &sl, int &mask, int &col0p) {
+                                          WaveSlot<BKV> &sl, int &mask, int &col0p, const float *s_th) {
     touch<FP4, BKV>(kc);
     flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
     if constexpr (PF) okp = fetch_block<FP4, BKV>(a, bt_row, bp, kp);
@@ -83,6 +101,16 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
         if (!okc) v = __builtin_nanf("");
         if (s >= vis) v = -__builtin_inff();
         if (out_lane<BKV>(lane)) lds_st<float>(&sl.v[i][tok], v);
+        if constexpr (CAND) {
+            // candidates (logit at or above the row's threshold) to the block's
+            // region of the row's list, in lane order, and their count
+            const bool pred = out_lane<BKV>(lane) && v >= lds_ld<float>(&s_th[i]);
+            const uint64_t cm = __ballot(pred);
+            const int64_t row = r0 + i;
+            if (lane == 0) store_i32_async(a.ccount + row * a.count_ld + b, (int)__popcll(cm));
+            const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(cm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)cm, 0u));
+            if (pred) store_v2f_async(a.cand + (row * a.cand_ld + col0 + pos) * 2, v, (float)s);
+        }
         m |= 1 << i;
     }
     mask = m;
@@ -115,10 +143,10 @@ struct Draw {
 // loads behind its wait). The first blocks are requested before q is staged,
 // so the two memory round trips overlap. With draw_here, the wave issues the
 // draw DrawAhead steps before its blocks end.
-template <bool FP4, int BKV, typename OT, bool Q4>
+template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
 __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int64_t bt_row, int b0, int nmy,
-                                          uint8_t *s_q, float *s_w, int *s_vis, WaveSlot<BKV> &sl, Draw &dr,
-                                          bool draw_here) {
+                                          uint8_t *s_q, float *s_w, int *s_vis, float *s_th, WaveSlot<BKV> &sl,
+                                          Draw &dr, bool draw_here) {
     constexpr int NB = kBufs;
     const int tid = threadIdx.x;
     const int last = nmy - 1;
@@ -133,6 +161,8 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
     else
         stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w);
     if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
+    if constexpr (CAND)
+        if (tid < g) s_th[tid] = a.theta[r0 + tid];
     barrier_lds();
     const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
     if (nmy > 0) {
@@ -142,9 +172,10 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
             for (int u = 0; u < NB; ++u) {
                 if (j + u >= nmy) break;
                 if (draw_here && j + u == max(nmy - kDrawAhead, 0)) dr.issue();
-                wave_step<FP4, BKV, OT, Q4, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u], b0 + min(j + u + kDepth, last),
-                                          kb[(u + kDepth) % NB], okb[(u + kDepth) % NB], s_q, s_w, vis_lane, sl, mask,
-                                          col0p);
+                wave_step<FP4, BKV, OT, Q4, CAND, true>(a, r0, g, bt_row, b0 + j + u, kb[u], okb[u],
+                                                        b0 + min(j + u + kDepth, last), kb[(u + kDepth) % NB],
+                                                        okb[(u + kDepth) % NB], s_q, s_w, vis_lane, sl, mask, col0p,
+                                                        s_th);
             }
         }
         flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
@@ -154,9 +185,9 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 // The units from chunk e0's start to chunk e1's start (the whole workgroup).
 // Wave 0 issues the draw kDrawAhead steps before its share of the last piece
 // ends; a range too short for that leaves it to the caller.
-template <bool FP4, int BKV, typename OT, bool Q4>
+template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
 __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, uint8_t *s_q, float *s_w, int *s_vis,
-                                           WaveSlot<BKV> &sl, Draw &dr) {
+                                           float *s_th, WaveSlot<BKV> &sl, Draw &dr) {
     const int tid = threadIdx.x;
     const int wave = uni(tid / kWave);
     const int n = a.rows.num_rows;
@@ -179,18 +210,19 @@ __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, u
             const int b0 = blk_lo + wave * per + min(wave, rem);
             const int nmy = per + (wave < rem ? 1 : 0);
             const bool draw_here = last_piece && wave == 0 && !dr.done;
-            run_piece<FP4, BKV, OT, Q4>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, sl, dr, draw_here);
+            run_piece<FP4, BKV, OT, Q4, CAND>(a, r0, g, bt_row, b0, nmy, s_q, s_w, s_vis, s_th, sl, dr, draw_here);
         }
         r0 = rn;
         blk_lo = 0;
     }
 }
 
-template <bool FP4, int BKV, typename OT, bool Q4>
+template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
 __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
     __shared__ int s_vis[kGMax];
+    __shared__ float s_th[CAND ? kGMax : 1];
     __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kPW];
     __shared__ unsigned s_take[2];
 
@@ -220,7 +252,7 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     int e0 = kStaticChunks * c, e1 = kStaticChunks * (c + 1);
     for (int par = 0;; par ^= 1) {
         dr.done = false;
-        run_chunks<FP4, BKV, OT, Q4>(a, e0, e1, s_q, s_w, s_vis, sl, dr);
+        run_chunks<FP4, BKV, OT, Q4, CAND>(a, e0, e1, s_q, s_w, s_vis, s_th, sl, dr);
         if (!dr.done) dr.issue();
         if (tid == 0) lds_st<unsigned>(&s_take[par], (unsigned)(dr.v % (Dx + Wx)));
         barrier_lds();  // (also: every wave is done reading s_take[par ^ 1])
@@ -238,25 +270,106 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     }
 }
 
-template <bool FP4, int BKV, typename OT, bool Q4 = false>
+template <bool FP4, int BKV, typename OT, bool Q4 = false, bool CAND = false>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT, Q4>), dim3(W), dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT, Q4, CAND>), dim3(W), dim3(kPThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
+}
+
+// Threshold of the fused top-k, one workgroup per row. A row with at most cap
+// visible columns takes every finite logit as a candidate (threshold
+// -FLT_MAX). A wider row scores an evenly spaced sample of its blocks
+// (kSampleTokens tokens) and takes the jr-th largest sampled value (the lower
+// bound of its radix bin) as the threshold, jr chosen so that about 2k of the
+// row's columns are expected at or above it. Any threshold gives the exact
+// result: the selection falls back to the full top-k when the candidates
+// number fewer than k or more than cap. Also writes the row's width.
+constexpr int kThThreads = 512;
+constexpr int kSampleTokens = 2048;
+
+template <bool FP4, int BKV>
+__global__ __launch_bounds__(kThThreads) void threshold_kernel(PagedArgs a, int k, int cap, float *theta,
+                                                               int32_t *width) {
+    constexpr int S = kSampleTokens / BKV;  // sampled blocks
+    constexpr int NW = kThThreads / kWave;
+    constexpr int PER = S / NW;             // blocks per wave
+    constexpr int NPT = kSampleTokens / kThThreads;
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kQBytes];
+    __shared__ __attribute__((aligned(16))) float s_w[PML_HEADS];
+    __shared__ uint32_t s_key[kSampleTokens];
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_pick[2];
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = uni(tid / kWave);
+    const int vis = min(a.rows.visible_s(r), a.max_ctx);
+    if (tid == 0) width[r] = vis;
+    if (vis <= cap) {
+        if (tid == 0) theta[r] = -__FLT_MAX__;
+        return;
+    }
+    const int nblk = (vis + BKV - 1) / BKV;  // (narrow rows may sample a block twice)
+    const int64_t bt_row = r / a.rows.next_n;
+    auto blk = [&](int t) { return (int)((int64_t)(2 * (wave + NW * t) + 1) * nblk / (2 * S)); };
+    KeyRegs<FP4, BKV> kb[2];
+    bool okb[2];
+    okb[0] = fetch_block<FP4, BKV>(a, bt_row, blk(0), kb[0]);
+    stage_rows<kThThreads>(a.q, a.w, r, 1, s_q, s_w);
+    barrier_lds();
+    const int tok = out_token<BKV>(lane);
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+        if (t + 1 < PER) okb[(t + 1) & 1] = fetch_block<FP4, BKV>(a, bt_row, blk(t + 1), kb[(t + 1) & 1]);
+        const KeyRegs<FP4, BKV> &kc = kb[t & 1];
+        const float scale = FP4 ? 0.5f : 0.5f * __uint_as_float(kc.sc[0]);
+        float v = score_row<FP4, BKV>(kc, s_q, s_w) * scale;
+        if (!okb[t & 1]) v = __builtin_nanf("");
+        if (blk(t) * BKV + tok >= vis) v = -__builtin_inff();
+        if (out_lane<BKV>(lane)) s_key[(wave + NW * t) * BKV + tok] = order_key(v);
+    }
+    barrier_lds();
+    uint32_t key[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) key[i] = s_key[i * kThThreads + tid];
+    const uint32_t jr = (uint32_t)max(1, (int)(((int64_t)2 * k * kSampleTokens + vis - 1) / vis));
+    uint32_t prefix = 0, mask = 0, kk = jr;
+    auto kf = [&](int i) { return key[i]; };
+    auto live = [&](int) { return true; };
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nbins = pass == 2 ? 1024 : 2048;
+        const uint32_t cnt = radix_pass<kThThreads, NPT>(kf, live, prefix, mask, shift, nbins, kk, s_hist, s_wave, s_pick);
+        prefix |= s_pick[0] << shift;
+        mask |= (uint32_t)(nbins - 1) << shift;
+        kk -= s_pick[1];
+        if (cnt == kk) break;
+    }
+    if (tid == 0) {
+        // the float whose order key is prefix (key 0, NaN, gives NaN: no candidates, the row falls back)
+        const uint32_t bits = (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix;
+        theta[r] = __uint_as_float(bits);
+    }
 }
 
 }  // namespace pml
 
 static inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
-// Shared by the fp32, bf16 and fp4-q entry points (bf16: logits are uint16_t
-// bits and rows must be 16-B aligned, logits_ld a multiple of 8; fp4 q:
-// q_scale given, MXFP4 keys only).
-static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_rows, int next_n, int num_heads, int head_dim,
-                        const void *kv_cache, int kv_format, int block_kv, int64_t page_stride_bytes,
-                        int64_t num_pages, const float *weights, const int32_t *context_lens,
-                        int context_lens_2d, const int32_t *block_table, int64_t block_table_ld,
-                        int block_table_cols, int32_t *schedule, int num_CUs, const int32_t *indices,
-                        int max_ctx, void *logits, int64_t logits_ld, bool bf16, void *stream) {
+// Validate the arguments shared by the paged-logits entry points and fill a
+// (bf16: logits are uint16_t bits and rows must be 16-B aligned, logits_ld a
+// multiple of 8; q4: fp4 q with its scales, MXFP4 keys only). PML_OK with
+// *empty set when there is nothing to launch.
+static int prepare_paged(pml::PagedArgs &a, bool &empty, const void *q, bool q4, const uint8_t *q_scale,
+                         int num_rows, int next_n, int num_heads, int head_dim, const void *kv_cache,
+                         int kv_format, int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                         const float *weights, const int32_t *context_lens, int context_lens_2d,
+                         const int32_t *block_table, int64_t block_table_ld, int block_table_cols,
+                         int32_t *schedule, int num_CUs, const int32_t *indices, int max_ctx, void *logits,
+                         int64_t logits_ld, bool bf16) {
+    empty = false;
     if (num_rows < 0 || next_n < 1 || num_CUs < 1 || max_ctx < 0) return PML_ERR_SHAPE;
     if (num_heads != PML_HEADS || head_dim != PML_HEAD_DIM) return PML_ERR_SHAPE;
     if (kv_format != PML_KV_FP8 && kv_format != PML_KV_MXFP4) return PML_ERR_FORMAT;
@@ -264,7 +377,10 @@ static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_
     if (indices && next_n != 1) return PML_ERR_VARLEN_NEXT_N;
     if (num_rows % next_n != 0) return PML_ERR_SHAPE;
     if (q4 && kv_format != PML_KV_MXFP4) return PML_ERR_UNSUPPORTED;
-    if (num_rows == 0) return PML_OK;
+    if (num_rows == 0) {
+        empty = true;
+        return PML_OK;
+    }
     if (q4 && !q_scale) return PML_ERR_NULL;
     if (q4 && !al16(q_scale)) return PML_ERR_ALIGN;
     if (!q || !kv_cache || !weights || !context_lens || !block_table || !schedule || !logits)
@@ -277,7 +393,7 @@ static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_
     if (page_stride_bytes < pb || page_stride_bytes % 16 != 0) return PML_ERR_STRIDE;
     if (logits_ld < max_ctx || logits_ld % (bf16 ? 8 : 4) != 0) return PML_ERR_STRIDE;
     if (!al16(q) || !al16(kv_cache) || !al16(weights) || !al16(logits) || !al16(schedule)) return PML_ERR_ALIGN;
-    pml::PagedArgs a;
+    a = pml::PagedArgs{};
     a.q = (const uint8_t *)q;
     a.qs = q_scale;
     a.w = weights;
@@ -293,6 +409,23 @@ static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_
     a.max_ctx = max_ctx;
     a.out = logits;
     a.out_ld = logits_ld;
+    return PML_OK;
+}
+
+// The fp32, bf16 and fp4-q logits calls.
+static int paged_logits(const void *q, bool q4, const uint8_t *q_scale, int num_rows, int next_n, int num_heads,
+                        int head_dim, const void *kv_cache, int kv_format, int block_kv, int64_t page_stride_bytes,
+                        int64_t num_pages, const float *weights, const int32_t *context_lens,
+                        int context_lens_2d, const int32_t *block_table, int64_t block_table_ld,
+                        int block_table_cols, int32_t *schedule, int num_CUs, const int32_t *indices,
+                        int max_ctx, void *logits, int64_t logits_ld, bool bf16, void *stream) {
+    pml::PagedArgs a;
+    bool empty;
+    const int st0 = prepare_paged(a, empty, q, q4, q_scale, num_rows, next_n, num_heads, head_dim, kv_cache,
+                                  kv_format, block_kv, page_stride_bytes, num_pages, weights, context_lens,
+                                  context_lens_2d, block_table, block_table_ld, block_table_cols, schedule, num_CUs,
+                                  indices, max_ctx, logits, logits_ld, bf16);
+    if (st0 != PML_OK || empty) return st0;
     hipStream_t st = (hipStream_t)stream;
     if (q4)
         return block_kv == 64 ? pml::launch_paged<true, 64, float, true>(a, num_CUs, st)
@@ -354,4 +487,85 @@ extern "C" int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint
                         head_dim, kv_cache, kv_format, block_kv, page_stride_bytes, num_pages, weights,
                         context_lens, context_lens_2d, block_table, block_table_ld, block_table_cols, schedule,
                         num_CUs, indices, max_ctx, logits, logits_ld, false, stream);
+}
+
+// Workspace of the fused call: thresholds, row widths and done flags
+// (fp32 / int32 [num_rows] each), the candidate counts (int32 [num_rows]
+// [ceil(max_ctx / block_kv)]) and the candidate lists (fp32 [num_rows]
+// [ceil(max_ctx / block_kv) * block_kv][2]); every region 256-B aligned.
+static size_t fused_region(size_t bytes) { return (bytes + 255) / 256 * 256; }
+
+extern "C" size_t fp8_fp4_paged_mqa_logits_topk_workspace_size(int num_rows, int max_ctx, int block_kv, int k) {
+    if (num_rows < 0 || max_ctx < 0 || (block_kv != 32 && block_kv != 64) || k < 1 || k > PML_MAX_TOPK) return 0;
+    const size_t rows = (size_t)num_rows;
+    const size_t nb = ((size_t)max_ctx + block_kv - 1) / block_kv;
+    return 3 * fused_region(4 * rows) + fused_region(rows * nb * 4) + fused_region(rows * nb * block_kv * 8);
+}
+
+extern "C" int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int next_n, int num_heads,
+                                             int head_dim, const void *kv_cache, int kv_format,
+                                             int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                             const float *weights, const int32_t *context_lens,
+                                             int context_lens_2d, const int32_t *block_table,
+                                             int64_t block_table_ld, int block_table_cols,
+                                             int32_t *schedule, int num_CUs,
+                                             const int32_t *indices, int max_ctx, float *logits,
+                                             int64_t logits_ld, int k, int32_t *topk, int64_t topk_ld,
+                                             void *workspace, size_t workspace_bytes, void *stream) {
+    if (k < 1 || k > PML_MAX_TOPK) return PML_ERR_K;
+    pml::PagedArgs a;
+    bool empty;
+    const int st0 = prepare_paged(a, empty, q, false, nullptr, num_rows, next_n, num_heads, head_dim, kv_cache,
+                                  kv_format, block_kv, page_stride_bytes, num_pages, weights, context_lens,
+                                  context_lens_2d, block_table, block_table_ld, block_table_cols, schedule, num_CUs,
+                                  indices, max_ctx, logits, logits_ld, false);
+    if (st0 != PML_OK || empty) return st0;
+    if (!topk) return PML_ERR_NULL;
+    if (topk_ld < k) return PML_ERR_STRIDE;
+    const size_t need = fp8_fp4_paged_mqa_logits_topk_workspace_size(num_rows, max_ctx, block_kv, k);
+    if (!workspace || workspace_bytes < need) return PML_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % 256) return PML_ERR_ALIGN;
+    const size_t rows = (size_t)num_rows;
+    const int64_t nb = ((int64_t)max_ctx + block_kv - 1) / block_kv;
+    uint8_t *ws = (uint8_t *)workspace;
+    const size_t reg = fused_region(4 * rows);
+    float *theta = (float *)ws;
+    int32_t *width = (int32_t *)(ws + reg);
+    int32_t *done = (int32_t *)(ws + 2 * reg);
+    int32_t *count = (int32_t *)(ws + 3 * reg);
+    float *cand = (float *)(ws + 3 * reg + fused_region(rows * nb * 4));
+    a.theta = theta;
+    a.ccount = count;
+    a.cand = cand;
+    a.count_ld = nb;
+    a.cand_ld = nb * block_kv;
+    const int cap = pml::kCandPerK * k;
+    hipStream_t st = (hipStream_t)stream;
+    const dim3 tg(num_rows), tb(pml::kThThreads);
+    int rc;
+    if (kv_format == PML_KV_FP8) {
+        if (block_kv == 64) {
+            hipLaunchKernelGGL((pml::threshold_kernel<false, 64>), tg, tb, 0, st, a, k, cap, theta, width);
+            rc = pml::launch_paged<false, 64, float, false, true>(a, num_CUs, st);
+        } else {
+            hipLaunchKernelGGL((pml::threshold_kernel<false, 32>), tg, tb, 0, st, a, k, cap, theta, width);
+            rc = pml::launch_paged<false, 32, float, false, true>(a, num_CUs, st);
+        }
+    } else {
+        if (block_kv == 64) {
+            hipLaunchKernelGGL((pml::threshold_kernel<true, 64>), tg, tb, 0, st, a, k, cap, theta, width);
+            rc = pml::launch_paged<true, 64, float, false, true>(a, num_CUs, st);
+        } else {
+            hipLaunchKernelGGL((pml::threshold_kernel<true, 32>), tg, tb, 0, st, a, k, cap, theta, width);
+            rc = pml::launch_paged<true, 32, float, false, true>(a, num_CUs, st);
+        }
+    }
+    if (rc != PML_OK) return rc;
+    pml::CandSelectArgs cs{cand, count, width, nb, nb * block_kv, block_kv, cap, k, topk, topk_ld, done};
+    rc = pml::launch_cand_select(cs, num_rows, st);
+    if (rc != PML_OK) return rc;
+    // rows the candidates could not settle: the full top-k over the written logits
+    pml::TopkArgs ta{logits, logits_ld, nullptr, context_lens, context_lens_2d ? 1 : next_n, k, max_ctx,
+                     topk, topk_ld, done};
+    return pml::launch_topk(ta, num_rows, st);
 }

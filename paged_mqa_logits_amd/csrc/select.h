@@ -98,4 +98,94 @@ __device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint
     pick_bin_by<NT>([&](int b) { return s_hist[b]; }, nbins, kk, s_wave, s_pick);
 }
 
+// One radix pass: histogram of bits [shift, shift + log2(nbins)) of key(i)
+// over the pairs live(i) whose key matches prefix under mask, then the bin of
+// the kk-th largest. Returns that bin's count; s_pick holds (bin, count above).
+template <int NT, int P, typename K, typename L>
+__device__ __forceinline__ uint32_t radix_pass(K key, L live, uint32_t prefix, uint32_t mask, int shift, int nbins,
+                                               uint32_t kk, uint32_t *s_hist, uint32_t *s_wave, uint32_t *s_pick) {
+    for (int b = threadIdx.x; b < nbins; b += NT) s_hist[b] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const uint32_t x = key(i);
+        if (live(i) && (x & mask) == prefix) atomicAdd(&s_hist[(x >> shift) & (nbins - 1)], 1u);
+    }
+    __syncthreads();
+    pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+    const uint32_t cnt = s_hist[s_pick[0]];
+    __syncthreads();
+    return cnt;
+}
+
+// Value of lane (lane ^ m) of the wave, m a power of two below 64 (a
+// constant once the caller's loops are unrolled).
+__device__ __forceinline__ int32_t lane_xor(int32_t v, int m) {
+    switch (m) {
+        case 1: return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false);   // quad_perm [1,0,3,2]
+        case 2: return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false);   // quad_perm [2,3,0,1]
+        case 4: return __builtin_amdgcn_ds_swizzle(v, 0x101F);                       // xor 4 in 32 lanes
+        case 8: return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);  // row_ror:8 = xor 8
+        case 16: return __builtin_amdgcn_ds_swizzle(v, 0x401F);                      // xor 16 in 32 lanes
+        default: return __shfl_xor(v, 32, kWave);
+    }
+}
+
+constexpr int kSortThreads = 256;  // the four waves that run the sort
+
+// Ascending bitonic sort of s[0, kSortThreads * E): every thread of the
+// workgroup calls it (it holds the barriers); threads below kSortThreads load
+// entries t * E .. t * E + E - 1 from s, sort, and leave them in x.
+template <int E>
+__device__ __forceinline__ void bitonic_sort(int32_t (&x)[E], int32_t *s) {
+    constexpr int NS = kSortThreads * E;
+    const int t = threadIdx.x;
+    const bool active = t < kSortThreads;
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = s[t * E + e];
+    }
+#pragma unroll
+    for (int sz = 2; sz <= NS; sz <<= 1) {
+#pragma unroll
+        for (int j = sz >> 1; j > 0; j >>= 1) {
+            if (j < E) {
+                if (active) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e)
+                        if ((e & j) == 0) {
+                            const bool asc = ((t * E + e) & sz) == 0;
+                            const int32_t lo = min(x[e], x[e | j]), hi = max(x[e], x[e | j]);
+                            x[e] = asc ? lo : hi;
+                            x[e | j] = asc ? hi : lo;
+                        }
+                }
+                continue;
+            }
+            int32_t y[E];
+            if (j < kWave * E) {
+                if (!active) continue;
+#pragma unroll
+                for (int e = 0; e < E; ++e) y[e] = lane_xor(x[e], j / E);
+            } else {
+                __syncthreads();  // earlier reads of s are done
+                if (active) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) s[t * E + e] = x[e];
+                }
+                __syncthreads();
+                if (!active) continue;
+#pragma unroll
+                for (int e = 0; e < E; ++e) y[e] = s[(t * E + e) ^ j];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int i = t * E + e;
+                const bool keep_low = ((i & j) == 0) == ((i & sz) == 0);
+                x[e] = keep_low ? min(x[e], y[e]) : max(x[e], y[e]);
+            }
+        }
+    }
+}
+
 }  // namespace pml

@@ -33,6 +33,7 @@
 //  * If the candidates overflow the list (heavy ties), the selection finishes
 //    with passes over the row itself.
 #include "select.h"
+#include "fused.h"
 
 namespace pml {
 
@@ -49,17 +50,6 @@ constexpr int kSampleDiv = 8;       // the sampled pass reads one 1-KB chunk in 
 constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled path (measured:
                                     // 32K-64K rows 47 -> 35 us; narrower rows gain nothing)
 
-struct TopkArgs {
-    const float *logits;
-    int64_t ld;
-    const int32_t *ks;
-    const int32_t *ke;
-    int next_n;
-    int k;
-    int max_width;
-    int32_t *out;
-    int64_t out_ld;
-};
 
 // Float4 walk of one wave's share [q0, q1) of the row's 16-B groups:
 // f(q, x, all_in) gets every group index q (lanes at or past q1 included: they
@@ -139,6 +129,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     const int lane = lane_id();
     const int wave = tid / kWave;
     const int r = blockIdx.x;
+    if (a.skip && a.skip[r]) return;
     int lo = a.ks ? a.ks[r] : 0;
     int hi;
     if (a.ks || a.next_n == 1)
@@ -461,6 +452,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
     const int r = blockIdx.x;
+    if (a.skip && a.skip[r]) return;
     int lo = a.ks ? a.ks[r] : 0;
     int hi;
     if (a.ks || a.next_n == 1)
@@ -537,6 +529,15 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     }
 }
 
+// Launch the top-k over num_rows rows (arguments validated by the caller).
+int launch_topk(const TopkArgs &a, int num_rows, hipStream_t st) {
+    if (a.max_width <= TopkCfg<256>::CAP)
+        hipLaunchKernelGGL(topk_small_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
+    return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
+}
+
 }  // namespace pml
 
 extern "C" size_t top_k_per_row_workspace_size(int num_rows, int max_width, int k) {
@@ -560,11 +561,6 @@ extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_l
     if (out_ld < k) return PML_ERR_STRIDE;
     if (((uintptr_t)logits & 15) != 0) return PML_ERR_ALIGN;
     if (logits_ld % 4 != 0) return PML_ERR_STRIDE;
-    pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld};
-    hipStream_t st = (hipStream_t)stream;
-    if (max_width <= pml::TopkCfg<256>::CAP)
-        hipLaunchKernelGGL(pml::topk_small_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL(pml::topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
-    return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
+    pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld, nullptr};
+    return pml::launch_topk(a, num_rows, (hipStream_t)stream);
 }

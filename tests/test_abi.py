@@ -199,3 +199,32 @@ def test_paged_fp4q_validation(kw, code):
 
 def test_paged_fp4q_zero_rows():
     assert _paged_fp4q(rows=0, qs=None) == 0
+
+
+def _fused(**kw):
+    a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
+             w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
+             max_ctx=512, out=FAKE, ld=512, k=64, topk=FAKE, topk_ld=64, ws=P(0x10000),
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return pml.lib().fp8_fp4_paged_mqa_logits_topk(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=0), 7), (dict(k=4097), 7), (dict(H=32), 2), (dict(bkv=16), 3), (dict(topk=None), 1),
+    (dict(topk_ld=63), 5), (dict(ws=None), 8), (dict(ws_bytes=100), 8), (dict(ws=P(0x10010)), 6),
+    (dict(q=None), 1), (dict(ld=500), 5),
+])
+def test_fused_validation(kw, code):
+    assert _fused(**kw) == code
+
+
+def test_fused_workspace_size():
+    f = pml.lib().fp8_fp4_paged_mqa_logits_topk_workspace_size
+    # 3 x [rows] int32 regions + counts [rows][nb] + pairs [rows][nb * bkv][2], each 256-B aligned
+    rows, mc, bkv, k = 135, 131072, 64, 2048
+    nb = mc // bkv
+    r = lambda b: (b + 255) // 256 * 256
+    assert f(rows, mc, bkv, k) == 3 * r(4 * rows) + r(4 * rows * nb) + r(8 * rows * nb * bkv)
+    assert f(rows, mc, 48, k) == 0 and f(rows, mc, bkv, 0) == 0 and f(-1, mc, bkv, k) == 0
+    assert _fused(rows=0, topk=None, ws=None) == 0
