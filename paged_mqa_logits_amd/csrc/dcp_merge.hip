@@ -209,15 +209,27 @@ static void launch_merge(int P, const MergeArgs &a, hipStream_t st) {
 // wider than k take their columns in order; rows with k to cap candidates
 // select among them (the candidates hold every column scoring at or above the
 // row's threshold, so the k best of the row are among them); other rows are
-// left to the full top-k (done[r] = 0). A scan of the block counts gives each
-// block's first candidate index; candidate c finds its block by a binary
-// search over those in LDS.
-template <int P, int E>
+// left to the full top-k (done[r] = 0).
+//
+// Block regions come in column order and each is filled in lane (column)
+// order, so the candidates, read block after block, are in column order.
+// Thread t takes candidates [P t, P t + P): a scan of the block counts gives
+// each block's first candidate index, and the owner of each block marks its
+// candidates' block in an LDS map. A radix select finds the k-th largest
+// key, its first digit taken at the highest bit where the candidates' keys
+// differ (they cluster just above the row's threshold, and a fixed top digit
+// would send them all to a few bins). One scan of (larger, equal) counts then
+// places every selected column, ascending, equal keys by lower column, with
+// no sort.
+template <int P>
 __global__ __launch_bounds__(kMergeThreads) void cand_select_kernel(CandSelectArgs a) {
     constexpr int NT = kMergeThreads;
     constexpr int PB = kSelectMaxBlocks / NT;  // blocks per thread in the scan
     __shared__ int32_t s_off[kSelectMaxBlocks + 1];
-    __shared__ uint32_t s_tot[kMergeWaves];
+    __shared__ uint16_t s_blk[P * NT];  // block of each candidate
+    __shared__ uint32_t s_hist[2048];
+    __shared__ uint32_t s_wave[2 * kMergeWaves];
+    __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
     const int r = blockIdx.x;
     const int k = a.k;
@@ -243,69 +255,110 @@ __global__ __launch_bounds__(kMergeThreads) void cand_select_kernel(CandSelectAr
         mine += (uint32_t)c[j];
     }
     uint32_t total;
-    uint32_t off = block_scan<NT>(mine, s_tot, &total) - mine;
-#pragma unroll
-    for (int j = 0; j < PB; ++j) {
-        const int b = tid * PB + j;
-        if (b < nb) s_off[b] = (int)off;
-        off += (uint32_t)c[j];
-    }
-    if (tid == 0) s_off[nb] = (int)total;
-    if (total < (uint32_t)k || total > (uint32_t)a.cap) {
+    uint32_t off = block_scan<NT>(mine, s_wave, &total) - mine;
+    if (total < (uint32_t)k || total > (uint32_t)min(a.cap, P * NT)) {
         if (tid == 0) a.done[r] = 0;
         return;
     }
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+        const int b = tid * PB + j;
+        if (b < nb) {
+            s_off[b] = (int)off;
+            for (int q = 0; q < c[j]; ++q) s_blk[off + q] = (uint16_t)b;
+        }
+        off += (uint32_t)c[j];
+    }
     __syncthreads();
+    // gather this thread's candidates [c0, c0 + P) (clamped into the list)
+    const int c0 = tid * P;
     const float *row = a.cand + (int64_t)r * a.cand_ld * 2;
+    int64_t addr[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int ci = min(c0 + i, (int)total - 1);
+        const int blk = s_blk[ci];
+        addr[i] = 2 * ((int64_t)blk * a.bkv + ci - s_off[blk]);
+    }
     float2 v[P];
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const int ci = min(i * NT + tid, (int)total - 1);
-        int lo = 0, hi = nb - 1;  // the last block whose first index is <= ci
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= ci)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        v[i] = *reinterpret_cast<const float2 *>(row + 2 * ((int64_t)lo * a.bkv + ci - s_off[lo]));
-    }
+    for (int i = 0; i < P; ++i) v[i] = *reinterpret_cast<const float2 *>(row + addr[i]);
     uint32_t key[P];
-    int32_t id[P];
-    uint32_t nmine = 0;
+    bool live[P];
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-        const bool ok = i * NT + tid < (int)total;
         key[i] = order_key(v[i].x);
-        id[i] = ok ? (int32_t)v[i].y : -1;
-        nmine += ok;
+        live[i] = c0 + i < (int)total;
     }
-    select_k_ids<P, E>(key, id, nmine, k, out);
+    // k-th largest key: digits of up to 11 bits from the highest bit where the
+    // live keys differ down (a pass stops early when its bin is taken whole)
+    uint32_t kmax = 0, nkmin = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+        if (live[i]) {
+            kmax = max(kmax, key[i]);
+            nkmin = max(nkmin, ~key[i]);
+        }
+    block_max2<NT>(kmax, nkmin, s_wave);
+    const uint32_t diff = kmax ^ ~nkmin;
+    uint32_t kk = (uint32_t)k, prefix = kmax, mask = 0xffffffffu;
+    if (diff != 0) {
+        int top = 31 - __builtin_clz(diff);  // highest differing bit
+        mask = top == 31 ? 0u : ~((2u << top) - 1u);
+        prefix = kmax & mask;
+        auto kf = [&](int i) { return key[i]; };
+        auto lf = [&](int i) { return live[i]; };
+#pragma unroll 1
+        for (;;) {
+            const int shift = max(top - 10, 0);
+            const int nbins = 1 << (top - shift + 1);
+            const uint32_t cntb = radix_pass<NT, P>(kf, lf, prefix, mask, shift, nbins, kk, s_hist, s_wave, s_pick);
+            prefix |= s_pick[0] << shift;
+            mask |= (uint32_t)(nbins - 1) << shift;
+            kk -= s_pick[1];
+            if (cntb == kk || shift == 0) break;
+            top = shift - 1;
+        }
+    }
+    // ordered placement: slot = (larger before) + min(equal before, kk)
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const uint32_t km = key[i] & mask;
+        gt += live[i] && km > prefix;
+        eq += live[i] && km == prefix;
+    }
+    uint32_t tot;
+    const uint32_t packed = gt | (eq << 16);
+    const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
+    uint32_t gb = excl & 0xffffu, eb = excl >> 16;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        if (!live[i]) continue;
+        const uint32_t km = key[i] & mask;
+        const int col = (int)v[i].y;
+        if (km > prefix) {
+            out[gb + min(eb, kk)] = col;
+            ++gb;
+        } else if (km == prefix) {
+            if (eb < kk) out[gb + eb] = col;
+            ++eb;
+        }
+    }
     if (tid == 0) a.done[r] = 1;
 }
 
-template <int E>
-static void launch_cand(int P, const CandSelectArgs &a, int rows, hipStream_t st) {
-    const dim3 g(rows), b(kMergeThreads);
-    switch (P) {
-        case 2: hipLaunchKernelGGL((cand_select_kernel<2, E>), g, b, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((cand_select_kernel<4, E>), g, b, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((cand_select_kernel<8, E>), g, b, 0, st, a); break;
-        default: hipLaunchKernelGGL((cand_select_kernel<16, E>), g, b, 0, st, a); break;
-    }
-}
-
 int launch_cand_select(const CandSelectArgs &a, int num_rows, hipStream_t st) {
-    if (a.cap > 16 * kMergeThreads || a.k > 4 * kSortThreads * 4) return PML_ERR_SHAPE;
-    int P = 2;
-    while (P * kMergeThreads < a.cap) P <<= 1;
-    if (a.k <= 4 * kSortThreads)
-        launch_cand<4>(P, a, num_rows, st);
-    else if (a.k <= 8 * kSortThreads)
-        launch_cand<8>(P, a, num_rows, st);
+    if (a.cap > 16 * kMergeThreads) return PML_ERR_SHAPE;
+    const dim3 g(num_rows), b(kMergeThreads);
+    if (a.cap <= 2 * kMergeThreads)
+        hipLaunchKernelGGL(cand_select_kernel<2>, g, b, 0, st, a);
+    else if (a.cap <= 4 * kMergeThreads)
+        hipLaunchKernelGGL(cand_select_kernel<4>, g, b, 0, st, a);
+    else if (a.cap <= 8 * kMergeThreads)
+        hipLaunchKernelGGL(cand_select_kernel<8>, g, b, 0, st, a);
     else
-        launch_cand<16>(P, a, num_rows, st);
+        hipLaunchKernelGGL(cand_select_kernel<16>, g, b, 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 

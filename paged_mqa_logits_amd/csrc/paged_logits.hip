@@ -279,13 +279,14 @@ static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
 // Threshold of the fused top-k, one workgroup per row. A row with at most cap
 // visible columns takes every finite logit as a candidate (threshold
 // -FLT_MAX). A wider row scores an evenly spaced sample of its blocks
-// (kSampleTokens tokens) and takes the jr-th largest sampled value (the lower
-// bound of its radix bin) as the threshold, jr chosen so that about 2k of the
-// row's columns are expected at or above it. Any threshold gives the exact
+// (kSampleTokens tokens) and takes the lower bound of the radix bin that holds
+// the jr-th largest sampled value as the threshold, jr chosen so that about
+// 2k of the row's columns are expected at or above it (the search stops once
+// the bin adds at most a quarter of jr). Any threshold gives the exact
 // result: the selection falls back to the full top-k when the candidates
 // number fewer than k or more than cap. Also writes the row's width.
 constexpr int kThThreads = 512;
-constexpr int kSampleTokens = 2048;
+constexpr int kSampleTokens = 1024;
 
 template <bool FP4, int BKV>
 __global__ __launch_bounds__(kThThreads) void threshold_kernel(PagedArgs a, int k, int cap, float *theta,
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(kThThreads) void threshold_kernel(PagedArgs a, int 
         prefix |= s_pick[0] << shift;
         mask |= (uint32_t)(nbins - 1) << shift;
         kk -= s_pick[1];
-        if (cnt == kk) break;
+        if (cnt == kk || 4 * cnt <= jr) break;
     }
     if (tid == 0) {
         // the float whose order key is prefix (key 0, NaN, gives NaN: no candidates, the row falls back)

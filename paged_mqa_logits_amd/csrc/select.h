@@ -30,6 +30,39 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
     return v;
 }
 
+// Maximum of one uint32 per lane over the wave (DPP row shifts, then row
+// broadcasts); the result is valid in lane 63.
+__device__ __forceinline__ uint32_t wave_max_to_last(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return v;
+}
+
+// Workgroup maxima of (a, b) (s_wave: 2 * NT / 64 words; all threads get them).
+template <int NT>
+__device__ __forceinline__ void block_max2(uint32_t &a, uint32_t &b, uint32_t *s_wave) {
+    constexpr int NW = NT / kWave;
+    const int wave = threadIdx.x / kWave;
+    const uint32_t wa = wave_max_to_last(a), wb = wave_max_to_last(b);
+    if (lane_id() == kWave - 1) {
+        s_wave[wave] = wa;
+        s_wave[NW + wave] = wb;
+    }
+    __syncthreads();
+    a = 0;
+    b = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        a = max(a, s_wave[w]);
+        b = max(b, s_wave[NW + w]);
+    }
+    __syncthreads();
+}
+
 // Inclusive scan of one uint32 per thread over the workgroup; *total gets the
 // sum. Each wave scans its lanes, publishes its total, and every thread adds
 // the totals of the waves before its own.
