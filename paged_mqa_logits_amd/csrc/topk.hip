@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t s_hist[kBins];
     __shared__ uint32_t s_key[CAP];
     __shared__ int32_t s_pos[CAP];
-    __shared__ uint32_t s_wave[NW];
+    __shared__ uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
 
@@ -360,33 +360,71 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         }  // exact passes
     }
 
-    // remaining radix digits (11, 11, 10 bits from the top)
-#pragma unroll 1
-    for (int pass = first_pass; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nbins = pass == 2 ? 1024 : 2048;
-        for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
-        __syncthreads();
-        if (in_list) {
-            for (int i = tid; i < m; i += NT) {
-                const uint32_t key = s_key[i];
-                if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+    // remaining radix digits. In the list, the live keys (those in the bin
+    // picked so far) cluster: the digits start at the highest bit where they
+    // differ, and the search stops once the picked bin is taken whole (then T
+    // is a bin under mask, and keys compare under the mask). Over the row
+    // (list overflow) the digits are 11, 11, 10 bits from the top.
+    if (in_list) {
+        uint32_t kmax = 0, nkmin = 0;
+        for (int i = tid; i < m; i += NT) {
+            const uint32_t key = s_key[i];
+            if ((key & mask) == prefix) {
+                kmax = max(kmax, key);
+                nkmin = max(nkmin, ~key);
             }
+        }
+        block_max2<NT>(kmax, nkmin, s_wave);
+        const uint32_t diff = kmax ^ ~nkmin;
+        if (diff == 0) {
+            prefix = kmax;  // every live key equal
+            mask = 0xffffffffu;
         } else {
+            int top = 31 - __builtin_clz(diff);
+            mask = top == 31 ? 0u : ~((2u << top) - 1u);
+            prefix = kmax & mask;
+#pragma unroll 1
+            for (;;) {
+                const int shift = max(top - 10, 0);
+                const int nbins = 1 << (top - shift + 1);
+                for (int b = tid; b < nbins; b += NT) s_hist[b] = 0;
+                __syncthreads();
+                for (int i = tid; i < m; i += NT) {
+                    const uint32_t key = s_key[i];
+                    if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
+                }
+                __syncthreads();
+                pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+                const uint32_t cnt = s_hist[s_pick[0]];
+                prefix |= s_pick[0] << shift;
+                mask |= (uint32_t)(nbins - 1) << shift;
+                kk -= s_pick[1];
+                __syncthreads();
+                if (cnt == kk || shift == 0) break;
+                top = shift - 1;
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int pass = first_pass; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int nbins = pass == 2 ? 1024 : 2048;
+            for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
+            __syncthreads();
             for (int i = lo + tid; i < hi; i += NT) {
                 const uint32_t key = order_key(rowbase[i]);
                 if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
             }
+            __syncthreads();
+            pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+            prefix |= s_pick[0] << shift;
+            mask |= (uint32_t)(nbins - 1) << shift;
+            kk -= s_pick[1];
+            __syncthreads();
         }
-        __syncthreads();
-        pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
-        prefix |= s_pick[0] << shift;
-        mask |= (uint32_t)(nbins - 1) << shift;
-        kk -= s_pick[1];
-        __syncthreads();
     }
-    const uint32_t T = prefix;
-    const uint32_t need = kk;  // elements equal to T that are taken (>= 1)
+    const uint32_t T = prefix;  // the k-th key's bin under mask
+    const uint32_t need = kk;   // keys in that bin that are taken (>= 1)
     const uint32_t n_gt = (uint32_t)k - need;
 
     // ordered compaction: slot = (# greater before) + min(# equal before, need)
@@ -395,7 +433,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         const int i0 = min(tid * per, m), i1 = min(i0 + per, m);
         uint32_t gt = 0, eq = 0;
         for (int i = i0; i < i1; ++i) {
-            const uint32_t key = s_key[i];
+            const uint32_t key = s_key[i] & mask;
             gt += key > T;
             eq += key == T;
         }
@@ -404,7 +442,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
         uint32_t gb = excl & 0xffffu, eb = excl >> 16;
         for (int i = i0; i < i1; ++i) {
-            const uint32_t key = s_key[i];
+            const uint32_t key = s_key[i] & mask;
             if (key > T) {
                 out[gb + min(eb, need)] = s_pos[i];
                 ++gb;

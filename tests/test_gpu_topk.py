@@ -213,3 +213,31 @@ def test_prefill_topk_sampled():
     rows = np.array([0, 1, 2047, 2048, 2049, 2999, 3000, 4500, 5499])
     ref = oracle.ragged_logits(case, rows=rows)
     _acceptance(got[rows], ref, ks[rows], ke[rows], 2048, np.abs(case.weights[rows].double().numpy()).sum(1))
+
+
+@pytest.mark.parametrize("width", [32768, 65536, 131072])
+def test_wide_rows_patterns(width):
+    """Wide rows of several shapes (normal, ties, -inf / NaN mixed in, ascending, all
+    equal, tiny values) through the sampled path and its fallbacks, bit for bit."""
+    rng = np.random.default_rng(width)
+    rows = []
+    rows.append(rng.standard_normal(width))                       # normal
+    rows.append(np.round(rng.standard_normal(width) * 2))         # ties across segments
+    r = rng.standard_normal(width)
+    r[::7] = -np.inf
+    r[3::11] = np.nan
+    rows.append(r)                                                # -inf and NaN mixed in
+    rows.append(np.arange(width, dtype=np.float64))               # ascending
+    rows.append(np.zeros(width))                                  # all equal: the list overflows
+    rows.append(rng.standard_normal(width) * 1e-30)               # tiny values
+    L = np.stack(rows).astype(np.float32)
+    d = G.dev()
+    lt = torch.from_numpy(L).to(d)
+    ke = np.array([width, width, width - 5, width, width, width - 100], dtype=np.int32)
+    kt = torch.from_numpy(ke).to(d)
+    for k in (64, 2048, 4096):
+        G.banner(f"wide-row top-k width={width} k={k}")
+        got = pml.top_k_per_row(lt, kt, k, max_width=width)
+        torch.cuda.synchronize()
+        want = oracle.topk(L.astype(np.float64), ke, k)
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
