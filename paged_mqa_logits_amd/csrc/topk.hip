@@ -533,21 +533,23 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
             }
         }
         __syncthreads();
-        pick_bin_by<NT>([&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; }, nbins, kk, s_wave,
-                        s_pick);
+        auto count = [&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; };
+        pick_bin_by<NT>(count, nbins, kk, s_wave, s_pick);
+        const uint32_t cnt = count((int)s_pick[0]);
         prefix |= s_pick[0] << shift;
         mask |= (uint32_t)(nbins - 1) << shift;
         kk -= s_pick[1];
         __syncthreads();
+        if (cnt == kk) break;  // the picked bin is taken whole: keys compare under mask
     }
     const uint32_t T = prefix;
-    const uint32_t need = kk;  // elements equal to T that are taken (>= 1)
+    const uint32_t need = kk;  // keys in T's bin that are taken (>= 1)
     // ordered compaction: slot = (# greater before) + min(# equal before, need)
     const int per = (n + NT - 1) / NT;
     const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
     uint32_t gt = 0, eq = 0;
     for (int i = i0; i < i1; ++i) {
-        const uint32_t key = s_key[i];
+        const uint32_t key = s_key[i] & mask;
         gt += key > T;
         eq += key == T;
     }
@@ -556,7 +558,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
     uint32_t gb = excl & 0xffffu, eb = excl >> 16;
     for (int i = i0; i < i1; ++i) {
-        const uint32_t key = s_key[i];
+        const uint32_t key = s_key[i] & mask;
         if (key > T) {
             out[gb + min(eb, need)] = i;
             ++gb;
