@@ -16,6 +16,11 @@ rate plus the logits kernel against the HBM roofline, and a bounded sample of
 the same workload scored by the CPU oracle.
 
   python bench.py [--steps K] [--warmup W] [--all]
+
+--all adds one line per further workload, each timed the same way: uniform
+decode, MXFP4 keys, MXFP4 keys with fp4 q, the tiny decode, the 120K decode
+with bf16 logits plus the upcast, the fused logits + top-k call, the exact
+top-k merge over 8 context-parallel ranks, and ragged prefill logits.
 """
 from __future__ import annotations
 

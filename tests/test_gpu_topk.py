@@ -2,7 +2,7 @@
 
 * On shared input (the same fp32 logits on both sides) the selected set must
   equal the oracle's bit for bit, ties included.
-* Against the oracle's fp64 logits the spec acceptance holds: every
+* Against the oracle's fp64 logits the top-k acceptance holds: every
   selected index scores at least t_k - tau, every index scoring above t_k + tau
   is selected, and min(k, width) distinct in-range entries come first.
 """
