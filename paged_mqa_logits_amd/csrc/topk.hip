@@ -20,10 +20,12 @@
 //    the list is then below every key in it, so if the list holds at least k
 //    keys the top k are among them and the selection finishes in the list.
 //    The row is read about 1.1 times rather than three. The pass is bound by
-//    instruction issue, one row per CU: when the bucket lies above -inf its
-//    test is one float compare per element, every element is stored without
-//    a branch (non-candidates to a spare slot per lane), and order keys are
-//    formed only for the list, when the regions are packed.
+//    instruction issue, one row per CU, so when the bucket lies above -inf it
+//    walks the row in words (lane l holds positions r + 64 j + l): per word
+//    index one float compare, a ballot whose popcount advances the wave's
+//    count, and, for the candidates only, a slot from mbcnt and one LDS
+//    store of value and position. Order keys are formed only for the list,
+//    when the regions are packed.
 //  * Narrower rows, and rows where the sample misjudges (fewer than k
 //    candidates, or a region overflows), take the exact streaming passes: a
 //    full histogram fixes b, then every wave counts, then appends, the
@@ -89,6 +91,51 @@ __device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int 
     }
 }
 
+// Word walk of positions [ps, pe) of a row: in a round starting at r, lane l
+// holds the kWords values at r + j * kWave + l, so for each j the wave's 64
+// lanes hold consecutive positions and the (j, lane) order is position order.
+// f(p - bias, x, full) gets each of them, where the wave-uniform `full` says the
+// whole round lies below pe (otherwise lanes must check p < pe). Rounds alternate
+// between two register buffers as in wave_walk_raw; only a round that reaches
+// pe clamps its addresses, so the others load at a base plus fixed offsets.
+constexpr int kWords = 16;
+template <typename F>
+__device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, int pe, int bias, F &&f) {
+    if (ps >= pe) return;
+    const int lane = lane_id();
+    constexpr int kRound = kWave * kWords;
+    auto load = [&](float *x, int r) {
+        if (r + kRound <= pe) {
+            const float *src = rowbase + r + lane;
+#pragma unroll
+            for (int j = 0; j < kWords; ++j) x[j] = src[j * kWave];
+        } else {
+#pragma unroll
+            for (int j = 0; j < kWords; ++j) x[j] = rowbase[min(r + j * kWave + lane, pe - 1)];
+        }
+    };
+    auto process = [&](const float *x, int r) {
+        const int rb = r + lane - bias;
+        if (r + kRound <= pe) {  // two copies, so f sees `full` as a constant
+#pragma unroll
+            for (int j = 0; j < kWords; ++j) f(rb + j * kWave, x[j], true);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kWords; ++j) f(rb + j * kWave, x[j], false);
+        }
+    };
+    float xa[kWords], xb[kWords];
+    load(xa, ps);
+    for (int r = ps;; r += 2 * kRound) {
+        load(xb, r + kRound);
+        process(xa, r);
+        if (r + kRound >= pe) break;
+        load(xa, r + 2 * kRound);
+        process(xb, r + kRound);
+        if (r + 2 * kRound >= pe) break;
+    }
+}
+
 // The same walk with order keys and validity: f(p, key, valid) for the 4
 // elements at positions p .. p + 3.
 template <typename F>
@@ -119,15 +166,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     constexpr int NW = Cfg::NW;
     constexpr int CAP = Cfg::CAP;
     __shared__ uint32_t s_hist[kBins];
-    __shared__ uint32_t s_key[CAP];
-    __shared__ int32_t s_pos[CAP];
+    __shared__ uint32_t s_list[2 * CAP];  // keys, then positions: one array, so an entry's
+    uint32_t *const s_key = s_list;       // two stores share an address
+    int32_t *const s_pos = (int32_t *)(s_list + CAP);
     __shared__ uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform, and known to be
     const int r = blockIdx.x;
     if (a.skip && a.skip[r]) return;
     int lo = a.ks ? a.ks[r] : 0;
@@ -170,7 +218,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     } else {
         constexpr int RCAP = Cfg::RCAP;
         bool exact = true;
-        if (n >= kSampledMin) {
+        // (the word walk's positions stay below 2^31 when hi leaves two rounds of room)
+        if (n >= kSampledMin && hi <= 0x7fffffff - 2 * kWave * kWords) {
         // sampled pass: top-digit histogram of one 64-group chunk (1 KB, one
         // coalesced load per wave) in every kSampleDiv chunks of the wave's span
         // (chunk 8i + i % 8, so the sample is not periodic in the row)
@@ -211,38 +260,25 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         uint32_t cnt = 0;
         const bool raw = sprefix >= 0x00800000u;  // the list holds float bits until the pack
         if (raw) {
-            // Branch-free: every element is stored, a candidate at its slot of
-            // the region and any other element at this lane's spare slot in the
-            // (now idle) histogram; the order keys are formed in the pack.
+            // Word walk over the wave's positions: for each word index the
+            // ballot of the candidates gives every candidate its slot (the
+            // count before it), so only candidates are stored. A slot past the
+            // region is clamped to its last entry: the count then exceeds the
+            // region and the list is not used. Order keys are formed in the pack.
             const float tf = key_floor_float(sprefix);
-            const uint32_t spare = (uint32_t)tid;
-            const int qa = (lo + 3) >> 2, qb = hi >> 2;  // groups [qa, qb) lie inside [lo, hi)
-            wave_walk_raw(rowbase, wq0, wq1, [&](int q, const v4f &x, bool all_in) {
-                const int p0 = 4 * q;
-                bool c[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) c[e] = x[e] >= tf;
-                // wave-uniform: do all 64 groups of this step lie inside the row and the share?
-                const int qw = __builtin_amdgcn_readfirstlane(q - lane);
-                if (!(all_in && qw >= qa && qw + kWave <= qb)) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) c[e] = c[e] && q < wq1 && p0 + e >= lo && p0 + e < hi;
+            const uint32_t rbase = (uint32_t)wave * RCAP, rlast = rbase + RCAP - 1;
+            const int ps = max(4 * wq0, lo), pe = min(4 * wq1, hi);
+            wave_walk_words(rowbase, ps, pe, lo, [&](int pl, float x, bool full) {
+                const bool c = x >= tf && (full || pl < pe - lo);
+                const uint64_t bm = __builtin_amdgcn_ballot_w64(c);
+                if (c) {
+                    const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, rbase + cnt));
+                    const uint32_t slot = min(at, rlast);
+                    s_key[slot] = __float_as_uint(x);
+                    s_pos[slot] = pl;
                 }
-                const uint32_t cc = (uint32_t)c[0] + (uint32_t)c[1] + (uint32_t)c[2] + (uint32_t)c[3];
-                uint32_t pre, tot;
-                wave_prefix4(cc, pre, tot);
-                uint32_t at = cnt + pre;
-                const bool room = cnt + tot <= (uint32_t)RCAP;  // wave-uniform: no slot of this step overflows
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool w = c[e] && (room || at < (uint32_t)RCAP);
-                    uint32_t *kd = w ? &s_key[wave * RCAP + at] : &s_hist[spare];
-                    int32_t *pd = w ? &s_pos[wave * RCAP + at] : (int32_t *)&s_hist[NT + spare];
-                    *kd = __float_as_uint(x[e]);
-                    *pd = p0 + e - lo;
-                    at += c[e];
-                }
-                cnt += tot;
+                cnt = __builtin_amdgcn_readfirstlane(cnt + (uint32_t)__builtin_popcountll(bm));
             });
         } else {
             wave_walk(rowbase, lo, hi, wq0, wq1, [&](int p0, const uint32_t *key, const bool *ok) {
