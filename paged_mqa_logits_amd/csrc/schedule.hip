@@ -20,7 +20,10 @@
 // a piece's first row reads the piece's rows and extent from LDS, and a
 // sum-scan of the piece costs gives each piece's offset, and each chunk that
 // starts in the tile finds its piece by a binary search over those offsets.
-// Up to 1024 rows take one walk; more take two (the total first).
+// Up to 1024 rows take one walk; more take two (the total first). The walk is
+// cheap next to the searches, so ceil(C / 1024) workgroups (at most 64) each
+// walk all rows, and the entries are dealt to them in turn: about one search
+// per thread.
 #include "rows.h"
 
 namespace pml {
@@ -28,6 +31,7 @@ namespace pml {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedWaves = kSchedThreads / kWave;
 constexpr int kHalo = kGMax;  // rows past a tile that a piece starting in it may cover
+constexpr int kSchedMaxBlocks = 64;  // workgroups that share out the entries (each walks all rows)
 
 // Block-wide inclusive scan: wave shuffles, then one pass over the wave totals.
 template <typename T, typename Op>
@@ -123,7 +127,8 @@ __device__ __forceinline__ void write_tile(int32_t *sched, int C, long long T, l
     const long long qC = T / C, rC = T % C;
     const long long lo = first_chunk_at(carry, T, qC, rC, C);
     const long long hi = first_chunk_at(carry + tile_total, T, qC, rC, C);
-    for (long long c = lo + threadIdx.x; c < hi; c += kSchedThreads) {
+    const long long nb = gridDim.x;  // entries are dealt to the workgroups in turn
+    for (long long c = lo + (long long)threadIdx.x * nb + blockIdx.x; c < hi; c += nb * kSchedThreads) {
         const long long t = chunk_start(c, qC, rC, C);
         int l = 0, h = kSchedThreads - 1;
         while (l < h) {
@@ -148,7 +153,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         sh.run_carry = 0;
         sh.cost_carry = 0;
     }
-    if (tid < kPools * kPoolStride) sched[2 * W + 2 + tid] = 0;  // work counters (64-bit) and their padding
+    const bool first = blockIdx.x == 0;
+    if (first && tid < kPools * kPoolStride) sched[2 * W + 2 + tid] = 0;  // work counters (64-bit), padding
     __syncthreads();
     long long total;
     if (n <= kSchedThreads) {
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         __syncthreads();
         total = sh.cost_carry;
         if (total > 0) {
-            if (tid == 0) {
+            if (first && tid == 0) {
                 sched[2 * W] = n;
                 sched[2 * W + 1] = 0;
             }
@@ -182,8 +188,10 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         __syncthreads();
         if (total > 0) {
             if (tid == 0) {
-                sched[2 * W] = n;
-                sched[2 * W + 1] = 0;
+                if (first) {
+                    sched[2 * W] = n;
+                    sched[2 * W + 1] = 0;
+                }
                 sh.run_carry = 0;
                 sh.cost_carry = 0;
             }
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         }
     }
     // nothing to score: every entry is the end
-    for (int c = tid; c <= W; c += kSchedThreads) {
+    for (int c = blockIdx.x * kSchedThreads + tid; c <= W; c += gridDim.x * kSchedThreads) {
         sched[2 * c] = n;
         sched[2 * c + 1] = 0;
     }
@@ -227,8 +235,10 @@ extern "C" int paged_mqa_logits_metadata(const int32_t *context_lens, int num_ro
     if (block_kv != 32 && block_kv != 64) return PML_ERR_BLOCK_KV;
     if (paged_mqa_logits_schedule_rows(num_CUs) < 0) return PML_ERR_SHAPE;
     pml::RowView v{context_lens, indices, context_lens_2d ? 1 : 0, next_n, num_rows};
-    hipLaunchKernelGGL(pml::schedule_kernel, dim3(1), dim3(pml::kSchedThreads), 0,
-                       (hipStream_t)stream, v, block_kv, pml::kChunksPerCU * num_CUs, schedule);
+    const int W = pml::kChunksPerCU * num_CUs;
+    const int blocks = std::min((W + pml::kSchedThreads - 1) / pml::kSchedThreads, pml::kSchedMaxBlocks);
+    hipLaunchKernelGGL(pml::schedule_kernel, dim3(blocks), dim3(pml::kSchedThreads), 0, (hipStream_t)stream, v,
+                       block_kv, W, schedule);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
