@@ -11,15 +11,17 @@
 //    256-thread kernel reads the row once into LDS and selects there
 //    (topk_small_kernel: 37 KB of LDS, four rows per CU).
 //  * A row that fits the LDS candidate list is read once into it.
-//  * A row of 16K columns or more first takes a sampled pass: a histogram of the top 11 key
-//    bits over one 1-KB chunk in 8 picks a bucket b with a margin (about
-//    1.5 k keys at or above it); then one streaming pass appends, in position
-//    order, every element whose top digit is >= b into its wave's region of
-//    the list (wave ballots order a wave's elements; each wave's span of the
-//    row is contiguous), and the regions are packed together. Any key outside
-//    the list is then below every key in it, so if the list holds at least k
-//    keys the top k are among them and the selection finishes in the list.
-//    The row is read about 1.1 times rather than three. The pass is bound by
+//  * A row of 16K columns or more first takes a sampled pass: a histogram of
+//    the top 11 key bits over each wave's first 1024 positions (16 places
+//    spread over the row) picks a bucket b with a margin (about 1.5 k of the
+//    row's keys at or above it, by the sample's share). Then one streaming
+//    pass, which starts from the sample's registers, appends in position
+//    order every element whose top digit is >= b into its wave's region of
+//    the list (each wave's span of the row is contiguous), and the regions are
+//    packed together. Any key outside the list is then below every key in
+//    it, so if the list holds at least k keys the top k are among them and
+//    the selection finishes in the list. When the sample holds, the row is
+//    read once rather than three times. The pass is bound by
 //    instruction issue, one row per CU, so when the bucket lies above -inf it
 //    walks the row in words (lane l holds positions r + 64 j + l): per word
 //    index one float compare, a ballot whose popcount advances the wave's
@@ -48,7 +50,6 @@ struct TopkCfg {
     static constexpr int CAP = NT == 1024 ? 12288 : 8192;  // candidate list entries
     static constexpr int RCAP = CAP / NW;                   // one wave's region of the list
 };
-constexpr int kSampleDiv = 8;       // the sampled pass reads one 1-KB chunk in 8
 constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled path (measured:
                                     // 32K-64K rows 47 -> 35 us; narrower rows gain nothing)
 
@@ -98,22 +99,28 @@ __device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int 
 // whole round lies below pe (otherwise lanes must check p < pe). Rounds alternate
 // between two register buffers as in wave_walk_raw; only a round that reaches
 // pe clamps its addresses, so the others load at a base plus fixed offsets.
+// The caller loads the first round (load_words at ps) into xa.
 constexpr int kWords = 16;
+constexpr int kRound = kWave * kWords;
+
+// The round of words at r, for r < pe (addresses clamped to pe - 1 in a round that reaches pe).
+__device__ __forceinline__ void load_words(const float *rowbase, int r, int pe, float *x) {
+    const int lane = lane_id();
+    if (r + kRound <= pe) {
+        const float *src = rowbase + r + lane;
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) x[j] = src[j * kWave];
+    } else {
+#pragma unroll
+        for (int j = 0; j < kWords; ++j) x[j] = rowbase[min(r + j * kWave + lane, pe - 1)];
+    }
+}
+
 template <typename F>
-__device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, int pe, int bias, F &&f) {
+__device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, int pe, int bias, float *xa, F &&f) {
     if (ps >= pe) return;
     const int lane = lane_id();
-    constexpr int kRound = kWave * kWords;
-    auto load = [&](float *x, int r) {
-        if (r + kRound <= pe) {
-            const float *src = rowbase + r + lane;
-#pragma unroll
-            for (int j = 0; j < kWords; ++j) x[j] = src[j * kWave];
-        } else {
-#pragma unroll
-            for (int j = 0; j < kWords; ++j) x[j] = rowbase[min(r + j * kWave + lane, pe - 1)];
-        }
-    };
+    auto load = [&](float *x, int r) { load_words(rowbase, r, pe, x); };
     auto process = [&](const float *x, int r) {
         const int rb = r + lane - bias;
         if (r + kRound <= pe) {  // two copies, so f sees `full` as a constant
@@ -124,8 +131,7 @@ __device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, in
             for (int j = 0; j < kWords; ++j) f(rb + j * kWave, x[j], false);
         }
     };
-    float xa[kWords], xb[kWords];
-    load(xa, ps);
+    float xb[kWords];
     for (int r = ps;; r += 2 * kRound) {
         load(xb, r + kRound);
         process(xa, r);
@@ -219,40 +225,27 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         constexpr int RCAP = Cfg::RCAP;
         bool exact = true;
         // (the word walk's positions stay below 2^31 when hi leaves two rounds of room)
-        if (n >= kSampledMin && hi <= 0x7fffffff - 2 * kWave * kWords) {
-        // sampled pass: top-digit histogram of one 64-group chunk (1 KB, one
-        // coalesced load per wave) in every kSampleDiv chunks of the wave's span
-        // (chunk 8i + i % 8, so the sample is not periodic in the row)
+        if (n >= kSampledMin && hi <= 0x7fffffff - 2 * kRound) {
+        // sampled pass: the sample is each wave's first round of the walk (up
+        // to 1024 positions at the start of its span, 16 places spread over the
+        // row), loaded once: its top-digit histogram picks the bucket, then the
+        // append starts from the same registers.
+        const int ps = max(4 * wq0, lo), pe = min(4 * wq1, hi);
+        float x0[kWords];
+        if (ps < pe) load_words(rowbase, ps, pe, x0);
         for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         if (tid == 0) s_pick[0] = 0;  // bucket 0 (the whole row) if the sample runs short
+        if (lane == 0) s_wcnt[wave] = (uint32_t)max(0, min(kRound, pe - ps));
         __syncthreads();
-        {
-            const int nchunk = (wq1 - wq0 + kWave - 1) / kWave;
-            const int nsamp = (nchunk + kSampleDiv - 1) / kSampleDiv;
-            for (int i0 = 0; i0 < nsamp; i0 += kUnroll) {
-                v4f x[kUnroll];
-                int gq[kUnroll];
 #pragma unroll
-                for (int j = 0; j < kUnroll; ++j) {
-                    const int i = i0 + j;
-                    gq[j] = wq0 + kWave * (i * kSampleDiv + i % kSampleDiv) + lane;
-                    x[j] = (i < nsamp && gq[j] < wq1) ? *(const v4f *)(rowbase + 4 * (int64_t)gq[j])
-                                                      : v4f{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int j = 0; j < kUnroll; ++j) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int p = 4 * gq[j] + e;
-                        if (i0 + j < nsamp && gq[j] < wq1 && p >= lo && p < hi)
-                            atomicAdd(&s_hist[order_key(x[j][e]) >> 21], 1u);
-                    }
-                }
-            }
-        }
+        for (int j = 0; j < kWords; ++j)
+            if (ps + j * kWave + lane < pe) atomicAdd(&s_hist[order_key(x0[j]) >> 21], 1u);
+        uint32_t ns = 0;
+        for (int w = 0; w < NW; ++w) ns += s_wcnt[w];
         __syncthreads();
-        // the bucket of the t-th largest sampled key, t = 1.5 k / kSampleDiv + 16
-        pick_bin<NT>(s_hist, kBins, (uint32_t)(3 * k) / (2 * kSampleDiv) + 16, s_wave, s_pick);
+        // the bucket of the t-th largest sampled key: 1.5 k scaled to the sample, + 16
+        const uint32_t t = (uint32_t)((3ull * (uint64_t)k * ns) / (2ull * (uint64_t)n)) + 16;
+        pick_bin<NT>(s_hist, kBins, t, s_wave, s_pick);
         const uint32_t sprefix = s_pick[0] << 21;
         // one pass: ordered append into the wave's region [wave * RCAP, +RCAP).
         // Above the key of -inf the bucket test is one float compare per
@@ -267,8 +260,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             // region and the list is not used. Order keys are formed in the pack.
             const float tf = key_floor_float(sprefix);
             const uint32_t rbase = (uint32_t)wave * RCAP, rlast = rbase + RCAP - 1;
-            const int ps = max(4 * wq0, lo), pe = min(4 * wq1, hi);
-            wave_walk_words(rowbase, ps, pe, lo, [&](int pl, float x, bool full) {
+            wave_walk_words(rowbase, ps, pe, lo, x0, [&](int pl, float x, bool full) {
                 const bool c = x >= tf && (full || pl < pe - lo);
                 const uint64_t bm = __builtin_amdgcn_ballot_w64(c);
                 if (c) {
