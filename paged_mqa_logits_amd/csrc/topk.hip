@@ -502,21 +502,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
 }
 
-// Rows of at most CAP columns (max_width <= 8192): the row is read once into
-// LDS as order keys, three radix passes select the k-th key, and one block
-// scan places the selected positions (the list index is the position). Bin
-// counts never pass 8192, so the histogram keeps two 16-bit counters per word;
-// with no position array the workgroup needs 37 KB of LDS and four fit on a CU.
+// Rows of at most 8192 columns (max_width <= 8192): each thread holds the keys
+// of positions j * NT + tid (j < 32) in registers, loaded together, so the
+// row costs one memory round trip. The first radix pass histograms them as
+// they arrive; the later passes read the registers again (bin counts never
+// pass 8192, so the histogram keeps two 16-bit counters per word, 4 KB of
+// LDS). The placement walks the row in chunks of 64 positions (round j, wave
+// w): per chunk two ballots give every lane its count of greater and equal
+// keys before it, on top of the chunk's base from one block scan over all
+// chunks' counts, so selected positions go to consecutive slots in order.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
-    constexpr int CAP = TopkCfg<NT>::CAP;
-    static_assert(CAP < 65536, "16-bit bin counters");
+    constexpr int kMaxCols = 8192;
+    constexpr int kPer = kMaxCols / NT;  // keys per thread
+    constexpr int kChunks = kPer * NW;   // 64-position chunks of a full row
+    static_assert(kChunks <= NT, "one chunk count per thread in the scan");
     __shared__ uint32_t s_hist[kBins / 2];
-    __shared__ uint32_t s_key[CAP];
+    __shared__ uint32_t s_base[kChunks];  // packed (greater | equal << 16) before each chunk
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r = blockIdx.x;
     if (a.skip && a.skip[r]) return;
     int lo = a.ks ? a.ks[r] : 0;
@@ -528,7 +536,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     const int64_t ldc = a.ld < 0x7fffffff ? a.ld : 0x7fffffff;
     lo = (int)min<int64_t>(max(lo, 0), ldc);
     hi = (int)min<int64_t>(max(hi, lo), ldc);
-    hi = (int)min<int64_t>(hi, (int64_t)lo + min(a.max_width, CAP));
+    hi = (int)min<int64_t>(hi, (int64_t)lo + min(a.max_width, kMaxCols));
     const int n = hi - lo;
     const int k = a.k;
     int32_t *out = a.out + (int64_t)r * a.out_ld;
@@ -537,31 +545,42 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
         return;
     }
     const float *row = a.logits + (int64_t)r * a.ld + lo;
-    // 8 loads in flight per thread (addresses clamped into the row)
-    for (int i0 = 0; i0 < n; i0 += 8 * NT) {
-        float x[8];
+    uint32_t key[kPer];
+    {
+        float x[kPer];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = row[min(i0 + j * NT + tid, n - 1)];
+        for (int j = 0; j < kPer; ++j)
+            if (j * NT < n) x[j] = row[min(j * NT + tid, n - 1)];
+        for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (i0 + j * NT + tid < n) s_key[i0 + j * NT + tid] = order_key(x[j]);
+        for (int j = 0; j < kPer; ++j) {
+            key[j] = 0;
+            if (j * NT < n && j * NT + tid < n) {
+                key[j] = order_key(x[j]);
+                const uint32_t bin = key[j] >> 21;
+                atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
+            }
+        }
     }
+    __syncthreads();
     uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
+    auto count = [&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; };
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
         const int nbins = pass == 2 ? 1024 : 2048;
-        for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
-        __syncthreads();  // (also publishes the keys before the first pass)
-        for (int i = tid; i < n; i += NT) {
-            const uint32_t key = s_key[i];
-            if ((key & mask) == prefix) {
-                const uint32_t bin = (key >> shift) & (nbins - 1);
-                atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
-            }
+        if (pass > 0) {
+            for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if (j * NT < n && j * NT + tid < n && (key[j] & mask) == prefix) {
+                    const uint32_t bin = (key[j] >> shift) & (nbins - 1);
+                    atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
+                }
+            __syncthreads();
         }
-        __syncthreads();
-        auto count = [&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; };
         pick_bin_by<NT>(count, nbins, kk, s_wave, s_pick);
         const uint32_t cnt = count((int)s_pick[0]);
         prefix |= s_pick[0] << shift;
@@ -572,28 +591,38 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     }
     const uint32_t T = prefix;
     const uint32_t need = kk;  // keys in T's bin that are taken (>= 1)
-    // ordered compaction: slot = (# greater before) + min(# equal before, need)
-    const int per = (n + NT - 1) / NT;
-    const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
-    uint32_t gt = 0, eq = 0;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = s_key[i] & mask;
-        gt += key > T;
-        eq += key == T;
+    // chunk (j, w) = positions j * NT + 64 w + [0, 64): counts, one block scan, placement
+    auto greater = [&](int j) { return j * NT < n && j * NT + tid < n && (key[j] & mask) > T; };
+    auto equal = [&](int j) { return j * NT < n && j * NT + tid < n && (key[j] & mask) == T; };
+    uint32_t mine = 0;  // thread t < kChunks: packed counts of chunk t
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (j * NT >= n) break;
+        const uint32_t g = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(greater(j)));
+        const uint32_t e = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(equal(j)));
+        if (lane == 0) s_base[j * NW + wave] = g | (e << 16);
     }
+    __syncthreads();
+    const int nch = ((n + NT - 1) / NT) * NW;  // chunks written above
+    if (tid < nch) mine = s_base[tid];
     uint32_t tot;
-    const uint32_t packed = gt | (eq << 16);
-    const uint32_t excl = block_scan<NT>(packed, s_wave, &tot) - packed;
-    uint32_t gb = excl & 0xffffu, eb = excl >> 16;
-    for (int i = i0; i < i1; ++i) {
-        const uint32_t key = s_key[i] & mask;
-        if (key > T) {
-            out[gb + min(eb, need)] = i;
-            ++gb;
-        } else if (key == T) {
-            if (eb < need) out[gb + eb] = i;
-            ++eb;
-        }
+    const uint32_t excl = block_scan<NT>(mine, s_wave, &tot) - mine;
+    if (tid < nch) s_base[tid] = excl;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        if (j * NT >= n) break;
+        const uint32_t base = s_base[j * NW + wave];
+        const bool gt = greater(j), eq = equal(j);
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(gt), em = __builtin_amdgcn_ballot_w64(eq);
+        const uint32_t gb = (base & 0xffffu) +
+                            __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
+        const uint32_t eb = (base >> 16) +
+                            __builtin_amdgcn_mbcnt_hi((uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
+        if (gt)
+            out[gb + min(eb, need)] = j * NT + tid;
+        else if (eq && eb < need)
+            out[gb + eb] = j * NT + tid;
     }
 }
 
