@@ -22,8 +22,8 @@
 // starts in the tile finds its piece by a binary search over those offsets.
 // Up to 1024 rows take one walk; more take two (the total first). The walk is
 // cheap next to the searches, so ceil(C / 1024) workgroups (at most 64) each
-// walk all rows, and the entries are dealt to them in turn: about one search
-// per thread.
+// walk all rows and write an equal share of the entries: about one search per
+// thread.
 #include "rows.h"
 
 namespace pml {
@@ -127,8 +127,10 @@ __device__ __forceinline__ void write_tile(int32_t *sched, int C, long long T, l
     const long long qC = T / C, rC = T % C;
     const long long lo = first_chunk_at(carry, T, qC, rC, C);
     const long long hi = first_chunk_at(carry + tile_total, T, qC, rC, C);
-    const long long nb = gridDim.x;  // entries are dealt to the workgroups in turn
-    for (long long c = lo + (long long)threadIdx.x * nb + blockIdx.x; c < hi; c += nb * kSchedThreads) {
+    // the workgroups take consecutive equal shares of [lo, hi), so each writes whole lines
+    const long long per = (hi - lo + gridDim.x - 1) / gridDim.x;
+    const long long c0 = lo + per * blockIdx.x, c1 = c0 + per < hi ? c0 + per : hi;
+    for (long long c = c0 + threadIdx.x; c < c1; c += kSchedThreads) {
         const long long t = chunk_start(c, qC, rC, C);
         int l = 0, h = kSchedThreads - 1;
         while (l < h) {
