@@ -178,6 +178,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
+    __shared__ uint32_t s_small[kWave];  // the keys of a small picked bin
+    __shared__ uint32_t s_nsmall;
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -427,8 +429,41 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                 prefix |= s_pick[0] << shift;
                 mask |= (uint32_t)(nbins - 1) << shift;
                 kk -= s_pick[1];
+                if (tid == 0) s_nsmall = 0;
                 __syncthreads();
                 if (cnt == kk || shift == 0) break;
+                if (cnt <= (uint32_t)kWave) {
+                    // A bin of at most 64 keys: gather them and let one wave sort
+                    // them (descending, bitonic) instead of more radix passes.
+                    for (int i = tid; i < m; i += NT) {
+                        const uint32_t key = s_key[i];
+                        if ((key & mask) == prefix) s_small[atomicAdd(&s_nsmall, 1u)] = key;
+                    }
+                    __syncthreads();
+                    if (wave == 0) {
+                        uint32_t v = (uint32_t)lane < cnt ? s_small[lane] : 0u;  // 0: below every key
+#pragma unroll
+                        for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+                            for (int j = size >> 1; j > 0; j >>= 1) {
+                                const uint32_t o = (uint32_t)lane_xor((int32_t)v, j);
+                                const bool keep_max = ((lane & size) == 0) == ((lane & j) == 0);
+                                v = keep_max ? max(v, o) : min(v, o);
+                            }
+                        }
+                        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)kk - 1);
+                        const uint32_t above = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v > t));
+                        if (lane == 0) {
+                            s_pick[0] = t;
+                            s_pick[1] = kk - above;
+                        }
+                    }
+                    __syncthreads();
+                    prefix = s_pick[0];
+                    mask = 0xffffffffu;
+                    kk = s_pick[1];
+                    break;
+                }
                 top = shift - 1;
             }
         }
