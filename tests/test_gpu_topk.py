@@ -241,3 +241,30 @@ def test_wide_rows_patterns(width):
         torch.cuda.synchronize()
         want = oracle.topk(L.astype(np.float64), ke, k)
         np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+def test_wide_rows_offsets_and_edges():
+    """The sampled path with row spans that start anywhere (unaligned ks), spans from
+    16K (the sample is the whole span) to 40K, a row that is mostly -inf (the bucket
+    falls to -inf and the append compares order keys), and globally descending
+    rows (each wave's first round over-estimates the threshold), bit for bit."""
+    rng = np.random.default_rng(4242)
+    ld = 48000
+    widths = [16384, 16385, 17000, 20000, 33001, 40000, 24000, 30000]
+    ks = np.array([0, 1, 3, 5000, 7, 2, 13, 4097], dtype=np.int32)
+    ke = ks + np.array(widths, dtype=np.int32)
+    L = rng.standard_normal((len(widths), ld)).astype(np.float32) * 3
+    L[2] = -np.inf
+    L[2, rng.choice(ld, 3000, replace=False)] = rng.standard_normal(3000)  # 3000 finite values
+    L[3] = np.linspace(5, -5, ld, dtype=np.float32)                           # descending
+    L[6] = np.round(L[6])                                                       # heavy ties
+    L[7, ks[7]: ke[7]] = np.linspace(-1, 1, widths[7], dtype=np.float32)[::-1]  # descending span
+    d = G.dev()
+    lt = torch.from_numpy(L).to(d)
+    for k in (1, 2048, 4096):
+        G.banner(f"wide-row top-k with offsets k={k}")
+        got = pml.top_k_per_row(lt, torch.from_numpy(ke).to(d), k, ks=torch.from_numpy(ks).to(d),
+                                max_width=max(widths))
+        torch.cuda.synchronize()
+        want = oracle.topk(L.astype(np.float64), ke, k, ks=ks)
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
