@@ -50,6 +50,7 @@ struct TopkCfg {
     static constexpr int CAP = NT == 1024 ? 12288 : 8192;  // candidate list entries
     static constexpr int RCAP = CAP / NW;                   // one wave's region of the list
 };
+constexpr int kSmallMaxCols = 8192;  // rows up to this wide take topk_small_kernel
 constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled path (measured:
                                     // 32K-64K rows 47 -> 35 us; narrower rows gain nothing)
 
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
-    constexpr int kMaxCols = 8192;
+    constexpr int kMaxCols = kSmallMaxCols;
     constexpr int kPer = kMaxCols / NT;  // keys per thread
     constexpr int kChunks = kPer * NW;   // 64-position chunks of a full row
     static_assert(kChunks <= NT, "one chunk count per thread in the scan");
@@ -663,7 +664,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
 
 // Launch the top-k over num_rows rows (arguments validated by the caller).
 int launch_topk(const TopkArgs &a, int num_rows, hipStream_t st) {
-    if (a.max_width <= TopkCfg<256>::CAP)
+    if (a.max_width <= kSmallMaxCols)
         hipLaunchKernelGGL(topk_small_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
     else
         hipLaunchKernelGGL(topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
