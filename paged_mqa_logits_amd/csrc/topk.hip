@@ -12,7 +12,7 @@
 //    (topk_small_kernel: 37 KB of LDS, four rows per CU).
 //  * A row that fits the LDS candidate list is read once into it.
 //  * A row of 16K columns or more first takes a sampled pass: a histogram of
-//    the top 11 key bits over each wave's first 1024 positions (16 places
+//    the top 11 key bits over each wave's first 512 positions (16 places
 //    spread over the row) picks a bucket b with a margin (about 1.5 k of the
 //    row's keys at or above it, by the sample's share). Then one streaming
 //    pass, which starts from the sample's registers, appends in position
@@ -103,6 +103,7 @@ __device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int 
 // The caller loads the first round (load_words at ps) into xa.
 constexpr int kWords = 16;
 constexpr int kRound = kWave * kWords;
+constexpr int kSampleWords = 8;  // of a wave's first round, the words the bucket is sampled from
 
 // The round of words at r, for r < pe (addresses clamped to pe - 1 in a round that reaches pe).
 __device__ __forceinline__ void load_words(const float *rowbase, int r, int pe, float *x) {
@@ -229,19 +230,20 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         bool exact = true;
         // (the word walk's positions stay below 2^31 when hi leaves two rounds of room)
         if (n >= kSampledMin && hi <= 0x7fffffff - 2 * kRound) {
-        // sampled pass: the sample is each wave's first round of the walk (up
-        // to 1024 positions at the start of its span, 16 places spread over the
-        // row), loaded once: its top-digit histogram picks the bucket, then the
-        // append starts from the same registers.
+        // sampled pass: the sample is the first half of each wave's first round
+        // of the walk (up to 512 positions at the start of its span, 16 places
+        // spread over the row). The round is loaded once: its top-digit
+        // histogram picks the bucket, then the append starts from the same
+        // registers.
         const int ps = max(4 * wq0, lo), pe = min(4 * wq1, hi);
         float x0[kWords];
         if (ps < pe) load_words(rowbase, ps, pe, x0);
         for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         if (tid == 0) s_pick[0] = 0;  // bucket 0 (the whole row) if the sample runs short
-        if (lane == 0) s_wcnt[wave] = (uint32_t)max(0, min(kRound, pe - ps));
+        if (lane == 0) s_wcnt[wave] = (uint32_t)max(0, min(kSampleWords * kWave, pe - ps));
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < kWords; ++j)
+        for (int j = 0; j < kSampleWords; ++j)
             if (ps + j * kWave + lane < pe) atomicAdd(&s_hist[order_key(x0[j]) >> 21], 1u);
         uint32_t ns = 0;
         for (int w = 0; w < NW; ++w) ns += s_wcnt[w];
