@@ -7,10 +7,10 @@
 // One workgroup per row, radix select on an order-preserving 32-bit key (NaN
 // lowest, -0 == +0) followed by an ordered compaction, so positions come out
 // ascending without a sort:
-//  * When every row fits the 8192-entry list (max_width <= 8192) a compact
-//    256-thread kernel reads the row once into LDS and selects there
-//    (topk_small_kernel: 37 KB of LDS, four rows per CU).
-//  * A row that fits the LDS candidate list is read once into it.
+//  * When every row has at most 8192 columns (max_width <= 8192) a compact
+//    256-thread kernel holds the row's keys in registers and selects there
+//    (topk_small_kernel: 4.6 KB of LDS, six rows per CU).
+//  * Otherwise a row that fits the LDS candidate list is read once into it.
 //  * A row of 16K columns or more first takes a sampled pass: a histogram of
 //    the top 11 key bits over each wave's first 512 positions (16 places
 //    spread over the row) picks a bucket b with a margin (about 1.5 k of the
@@ -32,8 +32,10 @@
 //    candidates, or a region overflows), take the exact streaming passes: a
 //    full histogram fixes b, then every wave counts, then appends, the
 //    candidates.
-//  * The remaining 11 + 10 key bits are selected inside the list, then one
-//    block scan over it places every selected element.
+//  * The remaining key bits are selected inside the list: radix digits from
+//    the highest bit where the live keys differ, until the picked bin is
+//    taken whole or holds at most 64 keys (one wave then sorts those). One
+//    block scan over the list places every selected element.
 //  * If the candidates overflow the list (heavy ties), the selection finishes
 //    with passes over the row itself.
 #include "select.h"
