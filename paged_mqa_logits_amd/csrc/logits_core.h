@@ -104,12 +104,18 @@ __device__ __forceinline__ void load_contig(const uint8_t *k, const float *k_sca
 // read land in distinct banks.
 __device__ __forceinline__ int q_lds_off(int h, int c) { return h * PML_HEAD_DIM + ((c ^ (h & 7)) << 4); }
 
+struct NoWait {
+    __device__ void operator()() const {}
+};
+
 // Stage q and w of rows r0 .. r0 + g - 1 into LDS (the whole workgroup). All
 // loads are issued before the first LDS store, so staging costs one memory
-// latency rather than one per round of the thread loop.
-template <int NTH = kLThreads>
+// latency rather than one per round of the thread loop. before_store runs
+// between the loads and the stores (a barrier that frees the LDS rows, say,
+// which the loads then overlap).
+template <int NTH = kLThreads, typename B = NoWait>
 __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int64_t r0, int g, uint8_t *s_q,
-                                           float *s_w) {
+                                           float *s_w, B before_store = B()) {
     constexpr int kChunks = kQBytes / 16;               // 16-B chunks per row
     constexpr int kPer = (kGMax * kChunks + NTH - 1) / NTH;  // chunks per thread, at most
     constexpr int kWPer = (kGMax * PML_HEADS + NTH - 1) / NTH;
@@ -124,6 +130,7 @@ __device__ __forceinline__ void stage_rows(const uint8_t *q, const float *w, int
 #pragma unroll
     for (int k = 0; k < kWPer; ++k)
         if (tid + k * NTH < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * NTH];
+    before_store();
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = tid + k * NTH;
@@ -147,10 +154,10 @@ constexpr int kQ4Scales = PML_HEADS * PML_HEAD_DIM / 32;  // 256
 __device__ __forceinline__ int q4_lds_off(int h, int c) { return h * (PML_HEAD_DIM / 2) + ((c ^ ((h >> 2) & 3)) << 4); }
 
 // Stage fp4 q (values and scales) and w of rows r0 .. r0 + g - 1 into LDS,
-// every load issued before the first store.
-template <int NTH = kLThreads>
+// every load issued before the first store (before_store as in stage_rows).
+template <int NTH = kLThreads, typename B = NoWait>
 __device__ __forceinline__ void stage_rows_q4(const uint8_t *qv, const uint8_t *qs, const float *w, int64_t r0,
-                                              int g, uint8_t *s_q, float *s_w) {
+                                              int g, uint8_t *s_q, float *s_w, B before_store = B()) {
     constexpr int kVC = kQ4Values / 16, kSC = kQ4Scales / 16, kRow = kVC + kSC;  // 16-B chunks
     constexpr int kPer = (kGMax * kRow + NTH - 1) / NTH;
     constexpr int kWPer = (kGMax * PML_HEADS + NTH - 1) / NTH;
@@ -171,6 +178,7 @@ __device__ __forceinline__ void stage_rows_q4(const uint8_t *qv, const uint8_t *
 #pragma unroll
     for (int k = 0; k < kWPer; ++k)
         if (tid + k * NTH < g * PML_HEADS) wv[k] = w[r0 * PML_HEADS + tid + k * NTH];
+    before_store();
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int i = tid + k * NTH;

@@ -156,13 +156,20 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 #pragma unroll
         for (int u = 0; u < kDepth; ++u) okb[u] = fetch_block<FP4, BKV>(a, bt_row, b0 + min(u, last), kb[u]);
     }
+    // The piece's loads (first key blocks, q, w, lengths) are all issued
+    // before the barrier at which every wave is done with the previous piece's
+    // rows, so waiting for the slowest wave overlaps their latency.
+    const int vis_t = tid < g ? a.rows.visible(r0 + tid) : 0;
+    float th_t = 0.f;
+    if constexpr (CAND) th_t = tid < g ? a.theta[r0 + tid] : 0.f;
+    auto wait_prev = [] { barrier_lds(); };
     if constexpr (Q4)
-        stage_rows_q4<kPThreads>(a.q, a.qs, a.w, r0, g, s_q, s_w);
+        stage_rows_q4<kPThreads>(a.q, a.qs, a.w, r0, g, s_q, s_w, wait_prev);
     else
-        stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w);
-    if (tid < g) s_vis[tid] = a.rows.visible(r0 + tid);
+        stage_rows<kPThreads>(a.q, a.w, r0, g, s_q, s_w, wait_prev);
+    if (tid < g) s_vis[tid] = vis_t;
     if constexpr (CAND)
-        if (tid < g) s_th[tid] = a.theta[r0 + tid];
+        if (tid < g) s_th[tid] = th_t;
     barrier_lds();
     const int vis_lane = lds_ld<int>(&s_vis[lane_id() % kGMax]);  // lane i: visible length of row i
     if (nmy > 0) {
@@ -202,7 +209,7 @@ __device__ __forceinline__ void run_chunks(const PagedArgs &a, int e0, int e1, u
         const int rn = r0 + g;  // the next piece, if the range goes on
         const bool last_piece = !(rn < n && (rn < end_r || (rn == end_r && end_b > 0)));
         if (blk_lo < blk_hi) {
-            barrier_lds();  // every wave is done with the previous piece
+            // (run_piece holds the barrier after which the previous piece's rows are free)
             const int64_t bt_row = r0 / a.rows.next_n;
             // this wave's blocks: a contiguous quarter of [blk_lo, blk_hi), so
             // its block-table entries share scalar-cache lines
