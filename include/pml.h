@@ -200,9 +200,9 @@ int mqa_logits(const void *q, int M, int num_heads, int head_dim, const void *k,
  *   next_n     >= 1; must be 1 when ks is given.
  *   k          1..4096 (else PML_ERR_K).
  *   max_width  upper bound of ke - ks over all rows (the selector's
- *              max_seq_len). Rows up to 8192 wide take a variant that keeps the
- *              whole row on chip. Wider rows are an error of the caller and are
- *              cut to max_width.
+ *              max_seq_len). With max_width <= 8192 every row takes a variant
+ *              that keeps the whole row in registers. Wider rows are an error
+ *              of the caller and are cut to max_width.
  *   out        int32 [num_rows][out_ld], out_ld >= k: per row the selected
  *              positions minus ks in ascending order, then -1 up to k.
  *              Order of selection: larger value first, equal values by lower
