@@ -214,6 +214,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     int first_pass = 0;  // radix digits already fixed: 0, or 1 after the streaming histogram
     int m = 0;           // entries in the candidate list (position order, positions relative to lo)
     bool in_list = true;
+    bool ranged = false;  // the list's key range (max of key and of ~key) is known from the pack
+    uint32_t rkmax = 0, rnkmin = 0;
 
     // this wave's share of the 16-B groups covering [lo, hi)
     const int gq0 = lo >> 2, gq1 = (hi + 3) >> 2;
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             constexpr int kPer = RCAP / kWave;
             uint32_t kv[kPer];
             int32_t pv[kPer];
+            uint32_t lmax = 0, lnmin = 0;
 #pragma unroll
             for (int u = 0; u < kPer; ++u) {
                 const uint32_t i = lane + u * kWave;
@@ -320,7 +323,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                     kv[u] = s_key[wave * RCAP + i];
                     if (raw) kv[u] = order_key(__uint_as_float(kv[u]));
                     pv[u] = s_pos[wave * RCAP + i];
+                    lmax = max(lmax, kv[u]);
+                    lnmin = max(lnmin, ~kv[u]);
                 }
+            }
+            // the list's key range rides on the pack's barriers (read after the next one)
+            lmax = wave_max_to_last(lmax);
+            lnmin = wave_max_to_last(lnmin);
+            if (lane == kWave - 1) {
+                s_wave[wave] = lmax;
+                s_wave[NW + wave] = lnmin;
             }
             __syncthreads();
 #pragma unroll
@@ -332,8 +344,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                 }
             }
             m = (int)total;  // all three digits are selected inside the list
+            ranged = true;
         }
         __syncthreads();
+        if (ranged) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                rkmax = max(rkmax, s_wave[w]);
+                rnkmin = max(rnkmin, s_wave[NW + w]);
+            }
+        }
         exact = over || total < (uint32_t)k;
         }  // sampled path
         if (exact) {
@@ -401,15 +421,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     // is a bin under mask, and keys compare under the mask). Over the row
     // (list overflow) the digits are 11, 11, 10 bits from the top.
     if (in_list) {
-        uint32_t kmax = 0, nkmin = 0;
-        for (int i = tid; i < m; i += NT) {
-            const uint32_t key = s_key[i];
-            if ((key & mask) == prefix) {
-                kmax = max(kmax, key);
-                nkmin = max(nkmin, ~key);
+        uint32_t kmax = rkmax, nkmin = rnkmin;
+        if (!ranged) {
+            for (int i = tid; i < m; i += NT) {
+                const uint32_t key = s_key[i];
+                if ((key & mask) == prefix) {
+                    kmax = max(kmax, key);
+                    nkmin = max(nkmin, ~key);
+                }
             }
+            block_max2<NT>(kmax, nkmin, s_wave);
         }
-        block_max2<NT>(kmax, nkmin, s_wave);
         const uint32_t diff = kmax ^ ~nkmin;
         if (diff == 0) {
             prefix = kmax;  // every live key equal
