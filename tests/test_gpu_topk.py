@@ -268,3 +268,25 @@ def test_wide_rows_offsets_and_edges():
         torch.cuda.synchronize()
         want = oracle.topk(L.astype(np.float64), ke, k, ks=ks)
         np.testing.assert_array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("width", [65536, 131072])
+def test_wide_rows_fine_ties(width):
+    """Values on a 2^-10 grid: the list's keys repeat about a dozen times each, so
+    the bins the selection picks are small but hold ties at the k-th value (the
+    one-wave finish then takes only some of the equal keys, the lower positions)."""
+    rng = np.random.default_rng(width + 7)
+    rows = 6
+    L = (np.round(rng.standard_normal((rows, width)) * 1024) / 1024).astype(np.float32)
+    L[1] = np.round(L[1] * 64) / 64          # coarser grid: larger tie groups
+    n3 = width // 3
+    L[2, 0:3 * n3:3] = L[2, 1:3 * n3:3]       # pairs of equal values side by side
+    ke = np.array([width, width - 1, width, width - 333, width, width - 4096], dtype=np.int32)
+    d = G.dev()
+    lt = torch.from_numpy(L).to(d)
+    for k in (2048, 4096, 777):
+        G.banner(f"wide-row fine ties width={width} k={k}")
+        got = pml.top_k_per_row(lt, torch.from_numpy(ke).to(d), k, max_width=width)
+        torch.cuda.synchronize()
+        want = oracle.topk(L.astype(np.float64), ke, k)
+        np.testing.assert_array_equal(got.cpu().numpy(), want)
