@@ -107,8 +107,9 @@ def topk(scores: np.ndarray, ke, k: int, ks=None) -> np.ndarray:
     rows = scores.shape[0]
     out = np.full((rows, k), -1, dtype=np.int32)
     for r in range(rows):
-        lo = 0 if ks is None else int(ks[r])
-        hi = int(ke[r])
+        ld = scores.shape[1]
+        lo = 0 if ks is None else min(max(int(ks[r]), 0), ld)  # bounds clamped into the row
+        hi = min(max(int(ke[r]), lo), ld)
         v = scores[r, lo:hi].astype(np.float64)
         idx = np.arange(len(v))
         order = np.lexsort((idx, -v))

@@ -265,9 +265,16 @@ void pml_oracle_topk(const double *scores, int rows, int64_t ld,
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int r = 0; r < rows; ++r) {
-        int lo = ks ? ks[r] : 0;
-        int hi = ke[r];
-        int n = hi > lo ? hi - lo : 0;
+        /* Row bounds outside the row are clamped: the start to [0, ld], the
+         * end to [start, ld]; positions count from the clamped start. The
+         * pages only ever pass in-range bounds (forward_cpu reads
+         * logits[r, ks:ke]); clamping is the reading that keeps every read
+         * inside the row, and the pack below uses the same rule. */
+        int64_t lo = ks ? ks[r] : 0;
+        lo = lo < 0 ? 0 : (lo > ld ? ld : lo);
+        int64_t hi = ke[r];
+        hi = hi < lo ? lo : (hi > ld ? ld : hi);
+        int n = (int)(hi - lo);
         cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (n > 0 ? n : 1));
         int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (k > 0 ? k : 1));
         for (int j = 0; j < n; ++j) {
@@ -329,7 +336,7 @@ void pml_oracle_dcp_pack(const float *logits, int rows, int64_t ld, const int32_
 {
     for (int r = 0; r < rows; ++r) {
         int64_t lo = ks ? ks[r] : 0;
-        lo = lo < 0 ? 0 : (lo > ld ? ld : lo); /* row starts clamped to [0, ld], as for the top-k */
+        lo = lo < 0 ? 0 : (lo > ld ? ld : lo); /* the top-k's bound rule: starts clamped to [0, ld] */
         for (int j = 0; j < k; ++j) {
             int64_t idx = topk[(int64_t)r * topk_ld + j];
             float *o = packed + ((int64_t)r * k + j) * 2;

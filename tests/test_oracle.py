@@ -385,3 +385,22 @@ def test_fp4q_equals_fp8q_when_exact_in_fp8():
     c2 = syn.PagedCase(**{**case.__dict__, "q_scale": case.q_scale.clone()})
     c2.q_scale[0, 5, 1] += 1
     assert not np.array_equal(oracle.paged_logits(c2)[0], a[0])
+
+
+# --------------------------------------------------------------------------
+# row bounds outside the row (hand-worked, tests/golden/topk_bounds_hand_worked.json)
+
+BOUNDS = os.path.join(os.path.dirname(__file__), "golden", "topk_bounds_hand_worked.json")
+
+
+def test_golden_topk_out_of_range_bounds_are_clamped():
+    g = json.load(open(BOUNDS))
+    row = np.array(g["row"], dtype=np.float64)
+    assert row.shape[0] == g["ld"]
+    for c in g["topk"]:
+        s = row[None, :]
+        ke = np.array([c["ke"]], np.int32)
+        ks = None if c["ks"] is None else np.array([c["ks"]], np.int32)
+        got = oracle.topk(s, ke, c["k"], ks=ks)
+        assert got[0].tolist() == c["expected"], c["derivation"]
+        assert brute.topk(s, ke, c["k"], ks=ks)[0].tolist() == c["expected"], c["derivation"]

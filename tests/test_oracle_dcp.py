@@ -161,3 +161,17 @@ def test_pack_reads_row_start_and_pads():
                 assert p[r, j, 1] == (idx // 2) * 6 + 2 + idx % 2
             else:
                 assert p[r, j, 0] == -np.inf and p[r, j, 1] == -1.0
+
+
+def test_golden_pack_out_of_range_row_starts_are_clamped():
+    """Row starts below 0 or past the row: the top-k's bound rule (start clamped
+    to [0, ld]), hand-worked in tests/golden/topk_bounds_hand_worked.json."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "topk_bounds_hand_worked.json")))
+    p = g["pack"]
+    row = np.array(g["row"], dtype=np.float32)
+    for c in p["cases"]:
+        tk = np.array([c["topk"]], np.int32)
+        got = oracle.dcp_pack(row[None, :], tk, p["rank"], p["world"], p["interleave"],
+                              ks=np.array([c["ks"]], np.int32))
+        want = np.array([[float(x) for x in pair] for pair in c["expected"]], np.float32)
+        assert np.array_equal(got[0], want), c["derivation"]
