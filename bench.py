@@ -99,12 +99,13 @@ class PagedBench:
         self.kv = [case.kv_cache.to(d) for _ in range(max(1, copies))]
         self.num_cus = num_cus or pml.default_num_workers()
         self.sched = torch.empty(pml.schedule_rows(self.num_cus), 2, dtype=torch.int32, device=d)
+        self.ws = torch.empty(pml.logits_workspace_size(case.rows, self.num_cus), dtype=torch.uint8, device=d)
         self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
         self.bf16 = bf16
         self.fused = fused
         self.nev = 5 if bf16 else (3 if fused else 4)
         if fused:
-            need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, case.topk)
+            need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, case.topk, self.num_cus)
             self.ws = torch.empty(need, dtype=torch.uint8, device=d)
         if bf16:
             assert case.next_n == 1
@@ -134,7 +135,7 @@ class PagedBench:
         pml.fp8_fp4_paged_mqa_logits(self.q, self.kv[i % len(self.kv)], self.w, self.lens, self.bt, self.sched,
                                      c.max_ctx, self.indices, kv_format=c.kv_format, block_kv=c.block_kv,
                                      next_n=c.next_n, logits=self.logits_bf16 if self.bf16 else self.logits,
-                                     q_scale=self.q_scale)
+                                     q_scale=self.q_scale, workspace=self.ws)
         if ev is not None:
             ev[2].record()
         if self.bf16:

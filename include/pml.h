@@ -71,11 +71,12 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
 #define PML_MAX_TOPK 4096
 
 /*
- * paged_mqa_logits_metadata - split the paged-logits work for persistent
+ * paged_mqa_logits_metadata - split the paged-logits work over persistent
  * workgroups ("get_paged_mqa_logits_metadata(context_lens, block_kv, num_SMs,
  * indices=)", [Attention][DSA] Route SM100 sparse-indexer decode ... , Purpose
- * and Changes; the schedule is sized by the number of SMs and a row slice gets
- * its own schedule, sparse_attn_indexer page, _varlen_decode_rows).
+ * and Changes; the schedule has one row per worker plus one, the caller reads
+ * the worker count back as schedule.shape[0] - 1, and a row slice gets its own
+ * schedule, sparse_attn_indexer page, _varlen_decode_rows).
  *
  *   context_lens     int32. With indices or next_n == 1: [num_rows], the
  *                    tokens each row sees. Otherwise [num_rows / next_n]
@@ -93,17 +94,16 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
  *   num_CUs          number of persistent workgroups the logits call will
  *                    launch (1 .. 2^20, else PML_ERR_SHAPE; e.g. 2 per
  *                    compute unit).
- *   schedule         int32 [paged_mqa_logits_schedule_rows(num_CUs)][2]
- *                    output, 16-B aligned (else PML_ERR_ALIGN). The
- *                    (row-piece, key-block) units, ordered by piece then
- *                    block, are cut into C = 8 * num_CUs chunks of about equal
- *                    cost. Entry c < C is the (first row of its row-piece,
- *                    block offset) where chunk c starts; entry C is
- *                    (num_rows, 0). The entries after it hold the logits
- *                    call's work counters, which this call sets to zero. A
- *                    row-piece is at most 8 consecutive rows of one group.
- *                    Units are weighted by (2 + rows in the piece) so chunks
- *                    cost about the same.
+ *   schedule         int32 [num_CUs + 1][2] output, 16-B aligned (else
+ *                    PML_ERR_ALIGN). The (row-piece, key-block) units, ordered
+ *                    by piece then block, are cut into num_CUs ranges of about
+ *                    equal cost; entry c < num_CUs is the (first row of its
+ *                    row-piece, block offset) where range c starts, and entry
+ *                    num_CUs is (num_rows, 0). A row-piece is at most 8
+ *                    consecutive rows of one group; units are weighted by
+ *                    (4 + rows in the piece) so ranges cost about the same.
+ *                    The logits calls only read it, so one schedule serves any
+ *                    number of calls, concurrent ones included.
  * The schedule is valid only for the same context_lens, indices, next_n,
  * block_kv and num_CUs.
  */
@@ -112,18 +112,25 @@ int paged_mqa_logits_metadata(const int32_t *context_lens, int num_rows, int nex
                               int num_CUs, int32_t *schedule, void *stream);
 
 /* Rows of [2] int32 entries in the schedule for num_CUs workgroups (host
- * only, no GPU call): 8 * num_CUs + 129. -1 when num_CUs is outside
- * 1 .. 2^20. */
+ * only, no GPU call): num_CUs + 1. -1 when num_CUs is outside 1 .. 2^20. */
 int paged_mqa_logits_schedule_rows(int num_CUs);
 
 /*
  * fp8_fp4_paged_mqa_logits - score every visible token of a paged key cache
  * ("fp8_fp4_paged_mqa_logits((q, q_scale), kv_cache, weights, seq_lens,
  * block_table, schedule, max_model_len, indices)", sparse_attn_indexer page,
- * _varlen_decode_rows; FP8 q with its per-token scale folded into weights,
- * forward_cuda).
+ * _varlen_decode_rows; FP8 q with its per-token scale folded into weights and
+ * FP4 q as a (values, scales) pair, forward_cuda).
  *
- *   q                fp8 codes [num_rows][num_heads][head_dim], 16-B aligned.
+ *   q                16-B aligned. With q_scale NULL: fp8 codes
+ *                    [num_rows][num_heads][head_dim]. With q_scale: packed
+ *                    e2m1 values [num_rows][num_heads][head_dim / 2], element
+ *                    2i in the low nibble of byte i (the MXFP4 key layout
+ *                    applied to q, this library's reading of the FP4 pair).
+ *   q_scale          NULL (fp8 q), or e8m0 [num_rows][num_heads][head_dim / 32],
+ *                    one per 32 consecutive elements, 16-B aligned (else
+ *                    PML_ERR_ALIGN); requires kv_format PML_KV_MXFP4 (else
+ *                    PML_ERR_UNSUPPORTED).
  *   num_rows, next_n, context_lens, context_lens_2d, indices
  *                    as for the metadata call (same values it was given).
  *   num_heads        must be 64; head_dim must be 128 (else PML_ERR_SHAPE).
@@ -136,32 +143,39 @@ int paged_mqa_logits_schedule_rows(int num_CUs);
  *   block_table      int32 [table rows][block_table_ld]; row r reads table row
  *                    r / next_n (with indices: its own row, and rows of one
  *                    group must hold the same entries). Entries of blocks a
- *                    row does not see are never read. block_table_cols
- *                    (<= ld) bounds the block index; beyond it a block scores NaN.
- *   schedule, num_CUs the metadata call's output and its num_CUs (schedule
- *                    16-B aligned); the kernel launches num_CUs workgroups.
- *                    Workgroup w first takes chunks [7w, 7w + 7); the last
- *                    num_CUs chunks are dealt out at run time through the
- *                    schedule's work counters, so that workgroups slowed by
- *                    their neighbours take fewer. Every call advances the
- *                    counters by a fixed amount and reads them modulo it, so
- *                    one schedule serves any number of calls queued one after
- *                    another; calls that share a schedule must not run at the
- *                    same time (calls on one stream never do).
+ *                    row does not see are never used (a few past a row's last
+ *                    visible block may be read ahead, within block_table_cols).
+ *                    block_table_cols (<= ld) bounds the block index; beyond it
+ *                    a block scores NaN.
+ *   schedule, num_CUs the metadata call's output (read only) and its num_CUs
+ *                    (schedule 16-B aligned); the kernel launches num_CUs
+ *                    workgroups, workgroup c scoring schedule range c.
  *   max_ctx          output columns (>= every visible length).
  *   logits           fp32 [num_rows][logits_ld] output, 16-B aligned,
  *                    logits_ld >= max_ctx and a multiple of 4. Columns
  *                    [0, vis(r)) get the score, [vis(r), max_ctx) get -inf,
  *                    [max_ctx, logits_ld) are not written.
+ *   workspace        device scratch of at least
+ *                    fp8_fp4_paged_mqa_logits_workspace_size(num_rows, num_CUs)
+ *                    bytes, 256-B aligned (else PML_ERR_WORKSPACE /
+ *                    PML_ERR_ALIGN). Its contents need no initialisation and
+ *                    are garbage afterwards. Calls that run at the same time
+ *                    need separate workspaces (they may share the schedule).
+ *                    The call first writes, per row, u = sum_h w[h] q[h] as
+ *                    four scaled fp8 pieces into it (codes [num_rows][4][128],
+ *                    then e8m0 scales [num_rows][4][4]): the scores' linear
+ *                    half, sum_h w_h <q_h, k>, runs on the matrix core as
+ *                    <u, k>.
  */
-int fp8_fp4_paged_mqa_logits(const void *q, int num_rows, int next_n, int num_heads,
-                             int head_dim, const void *kv_cache, int kv_format, int block_kv,
-                             int64_t page_stride_bytes, int64_t num_pages, const float *weights,
-                             const int32_t *context_lens, int context_lens_2d,
+size_t fp8_fp4_paged_mqa_logits_workspace_size(int num_rows, int num_CUs);
+int fp8_fp4_paged_mqa_logits(const void *q, const uint8_t *q_scale, int num_rows, int next_n,
+                             int num_heads, int head_dim, const void *kv_cache, int kv_format,
+                             int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                             const float *weights, const int32_t *context_lens, int context_lens_2d,
                              const int32_t *block_table, int64_t block_table_ld,
-                             int block_table_cols, int32_t *schedule, int num_CUs,
-                             const int32_t *indices, int max_ctx, float *logits,
-                             int64_t logits_ld, void *stream);
+                             int block_table_cols, const int32_t *schedule, int num_CUs,
+                             const int32_t *indices, int max_ctx, float *logits, int64_t logits_ld,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * mqa_logits - non-paged (ragged prefill) logits: a dense [M][N] matrix whose
@@ -217,10 +231,10 @@ int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const in
                   int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * fp8_fp4_paged_mqa_logits_bf16 - the same call as fp8_fp4_paged_mqa_logits,
- * writing bf16 logits (the SM100 kernel's output type; sparse_attn_indexer
- * page, as_fp32_logits and _varlen_decode_rows). Every argument means what it
- * means there, except:
+ * fp8_fp4_paged_mqa_logits_bf16 - the same call as fp8_fp4_paged_mqa_logits
+ * with fp8 q (no q_scale argument), writing bf16 logits (the SM100 kernel's
+ * output type; sparse_attn_indexer page, as_fp32_logits and
+ * _varlen_decode_rows). Every argument means what it means there, except:
  *   logits     bf16 bits [num_rows][logits_ld] (uint16_t), 16-B aligned;
  *              logits_ld >= max_ctx and a multiple of 8 (else
  *              PML_ERR_STRIDE). Each value is the fp32 logit rounded to the
@@ -235,25 +249,14 @@ int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int next_n, int n
                                   const float *weights, const int32_t *context_lens,
                                   int context_lens_2d, const int32_t *block_table,
                                   int64_t block_table_ld, int block_table_cols,
-                                  int32_t *schedule, int num_CUs,
+                                  const int32_t *schedule, int num_CUs,
                                   const int32_t *indices, int max_ctx, uint16_t *logits,
-                                  int64_t logits_ld, void *stream);
+                                  int64_t logits_ld, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /*
- * fp8_fp4_paged_mqa_logits_fp4q - the paged logits with fp4 q: the indexer's
- * FP4 path passes q as a (values, scales) pair (sparse_attn_indexer page,
- * forward_cuda; the pair is forwarded to fp8_fp4_paged_mqa_logits in
- * _varlen_decode_rows). The layout is this library's reading: the MXFP4 key
- * layout applied to q.
- *   q_values   packed e2m1 [num_rows][num_heads][head_dim / 2], element 2i in
- *              the low nibble of byte i; 16-B aligned.
- *   q_scales   e8m0 [num_rows][num_heads][head_dim / 32], one per 32
- *              consecutive elements; 16-B aligned (else PML_ERR_ALIGN; NULL
- *              with rows is PML_ERR_NULL).
- *   kv_format  must be PML_KV_MXFP4 (else PML_ERR_UNSUPPORTED).
- * Every other argument means what it means for fp8_fp4_paged_mqa_logits, and
- * the logits are fp32. Both operands of the scaled MFMA are e2m1, which gfx950
- * runs at twice the fp8 rate.
+ * fp8_fp4_paged_mqa_logits_fp4q - fp8_fp4_paged_mqa_logits with the fp4 q
+ * pair required (q_scales NULL with rows is PML_ERR_NULL); a thin alias.
  */
 int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scales, int num_rows,
                                   int next_n, int num_heads, int head_dim, const void *kv_cache,
@@ -261,9 +264,10 @@ int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scal
                                   int64_t num_pages, const float *weights,
                                   const int32_t *context_lens, int context_lens_2d,
                                   const int32_t *block_table, int64_t block_table_ld,
-                                  int block_table_cols, int32_t *schedule, int num_CUs,
+                                  int block_table_cols, const int32_t *schedule, int num_CUs,
                                   const int32_t *indices, int max_ctx, float *logits,
-                                  int64_t logits_ld, void *stream);
+                                  int64_t logits_ld, void *workspace, size_t workspace_bytes,
+                                  void *stream);
 
 /*
  * fp8_fp4_paged_mqa_logits_topk - the paged logits and their per-row top-k in
@@ -281,11 +285,12 @@ int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scal
  *              bit for bit.
  *   workspace  device scratch of at least
  *              fp8_fp4_paged_mqa_logits_topk_workspace_size(num_rows, max_ctx,
- *              block_kv, k) bytes, 256-B aligned (else PML_ERR_WORKSPACE /
- *              PML_ERR_ALIGN). Its contents need no initialisation and are
- *              garbage afterwards. Layout, each region 256-B aligned:
- *              thresholds fp32 [num_rows], widths int32 [num_rows], done flags
- *              int32 [num_rows], candidate counts int32 [num_rows][nb], then
+ *              block_kv, k, num_CUs) bytes, 256-B aligned (else
+ *              PML_ERR_WORKSPACE / PML_ERR_ALIGN). Its contents need no
+ *              initialisation and are garbage afterwards. Layout: the logits
+ *              call's workspace, then, each region 256-B aligned: thresholds
+ *              fp32 [num_rows], widths int32 [num_rows], done flags int32
+ *              [num_rows], candidate counts int32 [num_rows][nb], then
  *              candidate lists fp32 [num_rows][nb * block_kv][2], with
  *              nb = ceil(max_ctx / block_kv).
  * How: a first kernel scores an evenly spaced sample of each wide row's blocks
@@ -296,14 +301,15 @@ int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scal
  * there are k to 4k of them; every other row goes through the full top-k over
  * the written logits, so the result is exact for any data.
  */
-size_t fp8_fp4_paged_mqa_logits_topk_workspace_size(int num_rows, int max_ctx, int block_kv, int k);
+size_t fp8_fp4_paged_mqa_logits_topk_workspace_size(int num_rows, int max_ctx, int block_kv, int k,
+                                                     int num_CUs);
 int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int next_n, int num_heads,
                                   int head_dim, const void *kv_cache, int kv_format,
                                   int block_kv, int64_t page_stride_bytes, int64_t num_pages,
                                   const float *weights, const int32_t *context_lens,
                                   int context_lens_2d, const int32_t *block_table,
                                   int64_t block_table_ld, int block_table_cols,
-                                  int32_t *schedule, int num_CUs,
+                                  const int32_t *schedule, int num_CUs,
                                   const int32_t *indices, int max_ctx, float *logits,
                                   int64_t logits_ld, int k, int32_t *topk, int64_t topk_ld,
                                   void *workspace, size_t workspace_bytes, void *stream);

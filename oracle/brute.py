@@ -143,3 +143,43 @@ def dcp_merge(gathered: np.ndarray, k: int) -> np.ndarray:
         sel = np.sort(ids[order[:k]])
         out[r, : len(sel)] = sel
     return out
+
+
+def _row_keys(case, r: int):
+    """Row r's visible keys, dequantised, as float64 [vis, D] (block-table gather)."""
+    lens = case.context_lens.numpy().astype(np.int64)
+    bt = case.block_table.numpy()
+    nn = case.next_n
+    vis = lens.reshape(-1)[r] if (case.lens_2d or nn == 1) else lens[r // nn] - nn + (r % nn) + 1
+    vis = max(0, int(vis))
+    if vis == 0:
+        return np.zeros((0, case.D))
+    nblk = -(-vis // case.block_kv)
+    return np.concatenate([dequant_page_tokens(case, int(bt[r // nn, b])) for b in range(nblk)])[:vis]
+
+
+def paged_mass(case) -> np.ndarray:
+    """Absolute mass of every score, sum_h |w[r,h]| sum_d |q[r,h,d]| |k[s,d]|, as
+    float64 [rows, max_ctx] (0 where masked): the sum of the magnitudes of all
+    the products the score adds, the scale of any rounding in its evaluation."""
+    q = np.abs(q_dequant(case))
+    w = np.abs(case.weights.numpy().astype(np.float64))
+    out = np.zeros((case.rows, case.max_ctx))
+    for r in range(case.rows):
+        K = np.abs(_row_keys(case, r))
+        if len(K):
+            out[r, : len(K)] = K @ (w[r] @ q[r])
+    return out
+
+
+def ragged_mass(case) -> np.ndarray:
+    """paged_mass for a ragged case: [M, N], 0 outside [ks, ke)."""
+    q = np.abs(fp8_e4m3_np(case.q.numpy()))
+    w = np.abs(case.weights.numpy().astype(np.float64))
+    K = np.abs(fp8_e4m3_np(case.k.numpy()) * case.k_scale.numpy().astype(np.float64)[:, None])
+    out = np.zeros((case.M, case.N))
+    for r in range(case.M):
+        a, b = max(0, int(case.ks[r])), min(case.N, int(case.ke[r]))
+        if b > a:
+            out[r, a:b] = K[a:b] @ (w[r] @ q[r])
+    return out

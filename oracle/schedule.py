@@ -13,12 +13,12 @@ content is this library's own definition, stated here in plain Python:
 * A piece's extent is the largest visible length among its rows; it has
   ``nblk = ceil(extent / block_kv)`` key blocks, each costing ``COST_BASE + g``
   (g = rows in the piece: a page read and the fixed work of a step, then g
-  rows of scoring; a one-row block takes about a third of a six-row one).
-* Units (piece, block) are ordered by piece then block and cut into C chunks
-  (a fixed number per logits workgroup). Chunk c starts at the unit holding
-  cost offset floor(c * T / C) of the total T; entry C is the end sentinel
-  (num_rows, 0). The device output appends the logits call's work counters,
-  which start at zero.
+  rows of scoring; a one-row block takes about half the time of a six-row
+  one).
+* Units (piece, block) are ordered by piece then block and cut into C
+  ranges, one per logits workgroup. Range c starts at the unit holding cost
+  offset floor(c * T / C) of the total T; entry C is the end sentinel
+  (num_rows, 0).
 
 Entries are (first row of the piece, block offset within the piece).
 """
@@ -27,7 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 G_MAX = 8
-COST_BASE = 2
+COST_BASE = 4
 
 
 def visible_lengths(context_lens: np.ndarray, num_rows: int, next_n: int, lens_2d: bool) -> np.ndarray:

@@ -10,7 +10,7 @@ fp8_fp4_paged_mqa_logits, mqa_logits and the per-row top-k selector):
 
 * ``paged_mqa_logits_metadata(context_lens, block_kv, num_cus, indices=None, next_n=1)``
 * ``fp8_fp4_paged_mqa_logits(q, kv_cache, weights, context_lens, block_table, schedule,
-  max_model_len, indices=None, ...)``
+  max_model_len, indices=None, q_scale=None, workspace=None, ...)``
 * ``mqa_logits(q, k, k_scale, weights, cu_seqlen_ks, cu_seqlen_ke)``
 * ``top_k_per_row(logits, ke, k, ks=None, next_n=1, max_width=None)``
 """
@@ -61,17 +61,20 @@ def lib() -> ctypes.CDLL:
         L.paged_mqa_logits_metadata.argtypes = [P, I, I, I, P, I, I, P, P]
         L.paged_mqa_logits_schedule_rows.argtypes = [I]
         L.paged_mqa_logits_schedule_rows.restype = I
-        L.fp8_fp4_paged_mqa_logits.argtypes = [P, I, I, I, I, P, I, I, I64, I64, P, P, I, P, I64, I, P,
-                                               I, P, I, P, I64, P]
+        # (q, q_scale), rows .. logits_ld, workspace, bytes, stream
+        body = [I, I, I, I, P, I, I, I64, I64, P, P, I, P, I64, I, P, I, P, I, P, I64]
+        L.fp8_fp4_paged_mqa_logits.argtypes = [P, P] + body + [P, SZ, P]
+        L.fp8_fp4_paged_mqa_logits_workspace_size.argtypes = [I, I]
+        L.fp8_fp4_paged_mqa_logits_workspace_size.restype = SZ
         if hasattr(L, "fp8_fp4_paged_mqa_logits_bf16"):
-            L.fp8_fp4_paged_mqa_logits_bf16.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes
+            L.fp8_fp4_paged_mqa_logits_bf16.argtypes = [P] + body + [P, SZ, P]
             L.as_fp32_logits.argtypes = [P, I, I64, I, P, P, I64, P]
         if hasattr(L, "fp8_fp4_paged_mqa_logits_topk"):
-            L.fp8_fp4_paged_mqa_logits_topk.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes[:-1] + [I, P, I64, P, SZ, P]
-            L.fp8_fp4_paged_mqa_logits_topk_workspace_size.argtypes = [I, I, I, I]
+            L.fp8_fp4_paged_mqa_logits_topk.argtypes = [P] + body + [I, P, I64, P, SZ, P]
+            L.fp8_fp4_paged_mqa_logits_topk_workspace_size.argtypes = [I, I, I, I, I]
             L.fp8_fp4_paged_mqa_logits_topk_workspace_size.restype = SZ
         if hasattr(L, "fp8_fp4_paged_mqa_logits_fp4q"):
-            L.fp8_fp4_paged_mqa_logits_fp4q.argtypes = [P, P] + L.fp8_fp4_paged_mqa_logits.argtypes[1:]
+            L.fp8_fp4_paged_mqa_logits_fp4q.argtypes = L.fp8_fp4_paged_mqa_logits.argtypes
         if hasattr(L, "mqa_logits"):
             L.mqa_logits.argtypes = [P, I, I, I, P, P, I, P, P, P, P, I64, P]
         if hasattr(L, "top_k_per_row"):
@@ -148,8 +151,8 @@ def paged_mqa_logits_metadata(context_lens: torch.Tensor, block_kv: int, num_cus
                               indices: torch.Tensor | None = None, next_n: int = 1,
                               out: torch.Tensor | None = None) -> torch.Tensor:
     """Work split of the paged-logits call for num_cus workgroups: int32
-    [schedule_rows(num_cus), 2] on the device (chunk entries, end entry, work
-    counters)."""
+    [num_cus + 1, 2] on the device (one range start per workgroup, then the
+    end); read only by the logits calls."""
     _dev(context_lens, "context_lens", _I32)
     context_lens = context_lens.contiguous()
     if indices is not None:
@@ -168,7 +171,7 @@ def paged_mqa_logits_metadata(context_lens: torch.Tensor, block_kv: int, num_cus
 
 
 def schedule_rows(num_cus: int) -> int:
-    """Rows of the [rows, 2] schedule tensor for num_cus logits workgroups."""
+    """Rows of the [rows, 2] schedule tensor for num_cus logits workgroups (num_cus + 1)."""
     n = lib().paged_mqa_logits_schedule_rows(int(num_cus))
     if n < 0:
         raise ValueError(f"num_cus {num_cus} outside 1 .. 2^20")
@@ -176,17 +179,27 @@ def schedule_rows(num_cus: int) -> int:
 
 
 def schedule_workers(schedule: torch.Tensor) -> int:
-    """Workgroups a schedule tensor was made for (the inverse of schedule_rows)."""
-    per = schedule_rows(2) - schedule_rows(1)
-    W = (schedule.shape[0] - schedule_rows(1)) // per + 1
-    if schedule.dim() != 2 or schedule.shape[1] != 2 or W < 1 or schedule_rows(W) != schedule.shape[0]:
+    """Workgroups a schedule tensor was made for: schedule.shape[0] - 1."""
+    if schedule.dim() != 2 or schedule.shape[1] != 2 or schedule.shape[0] < 2:
         raise ValueError(f"schedule of shape {tuple(schedule.shape)} is not a metadata output")
-    return W
+    return schedule.shape[0] - 1
 
 
 def logits_ld(max_ctx: int) -> int:
     """Row stride used when the binding allocates the logits (a multiple of 4 floats)."""
     return max(4, (max_ctx + 3) // 4 * 4)
+
+
+def logits_workspace_size(rows: int, num_cus: int) -> int:
+    """Bytes of scratch one paged-logits call needs."""
+    return int(lib().fp8_fp4_paged_mqa_logits_workspace_size(rows, num_cus))
+
+
+def _workspace(ws, need: int, device) -> tuple:
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace", (torch.uint8,))
+    return ws, ws.numel()
 
 
 def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
@@ -196,13 +209,16 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
                              block_kv: int = 64, next_n: int = 1,
                              logits: torch.Tensor | None = None,
                              out_dtype: torch.dtype = torch.float32,
-                             q_scale: torch.Tensor | None = None) -> torch.Tensor:
+                             q_scale: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Paged logits [rows, ld >= max_model_len], fp32 or bf16 (``out_dtype``, or
     the dtype of a given ``logits``); columns past each row's visible length are
     -inf. ``kv_cache`` is [num_pages, page_stride_bytes] uint8 (a row stride
     larger than the page is allowed). With ``q_scale`` (uint8 e8m0 [rows, heads,
     head_dim / 32]) q is packed e2m1 [rows, heads, head_dim / 2] (MXFP4 keys,
-    fp32 logits)."""
+    fp32 logits). ``workspace``: uint8 scratch of at least
+    ``logits_workspace_size(rows, schedule rows - 1)`` bytes (allocated when
+    None)."""
     _dev(q, "q", _FP8_TYPES)
     _dev(kv_cache, "kv_cache", (torch.uint8,))
     _dev(weights, "weights", _F32)
@@ -240,17 +256,16 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     num_cus = schedule_workers(schedule)
     if not schedule.is_contiguous():
         raise ValueError("schedule must be contiguous")
-    if q_scale is not None:
-        call, lead = lib().fp8_fp4_paged_mqa_logits_fp4q, (_p(q), _p(q_scale))
-    elif logits.dtype == torch.float32:
-        call, lead = lib().fp8_fp4_paged_mqa_logits, (_p(q),)
+    ws, wbytes = _workspace(workspace, logits_workspace_size(rows, num_cus), q.device)
+    tail = (rows, next_n, q.shape[1], head_dim, _p(kv_cache), kv_format, block_kv,
+            kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
+            block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
+            max_model_len, _p(logits), logits.stride(0), _p(ws), wbytes, _stream())
+    if logits.dtype == torch.float32:
+        st = lib().fp8_fp4_paged_mqa_logits(_p(q), _p(q_scale), *tail)
     else:
-        call, lead = lib().fp8_fp4_paged_mqa_logits_bf16, (_p(q),)
-    _check(call(
-        *lead, rows, next_n, q.shape[1], head_dim, _p(kv_cache), kv_format, block_kv,
-        kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
-        block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
-        max_model_len, _p(logits), logits.stride(0), _stream()), "fp8_fp4_paged_mqa_logits")
+        st = lib().fp8_fp4_paged_mqa_logits_bf16(_p(q), *tail)
+    _check(st, "fp8_fp4_paged_mqa_logits")
     return logits
 
 
@@ -366,8 +381,8 @@ def stable_topk_from_gathered_candidates(gathered: torch.Tensor, k: int,
     return out
 
 
-def fused_topk_workspace_size(rows: int, max_model_len: int, block_kv: int, k: int) -> int:
-    return int(lib().fp8_fp4_paged_mqa_logits_topk_workspace_size(rows, max_model_len, block_kv, k))
+def fused_topk_workspace_size(rows: int, max_model_len: int, block_kv: int, k: int, num_cus: int) -> int:
+    return int(lib().fp8_fp4_paged_mqa_logits_topk_workspace_size(rows, max_model_len, block_kv, k, num_cus))
 
 
 def fp8_fp4_paged_mqa_logits_topk(q: torch.Tensor, kv_cache: torch.Tensor, weights: torch.Tensor,
@@ -399,14 +414,13 @@ def fp8_fp4_paged_mqa_logits_topk(q: torch.Tensor, kv_cache: torch.Tensor, weigh
         logits = torch.empty(rows, logits_ld(max_model_len), dtype=torch.float32, device=q.device)
     if out is None:
         out = torch.empty(rows, max(k, 1), dtype=torch.int32, device=q.device)
-    need = fused_topk_workspace_size(rows, max_model_len, block_kv, k)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     num_cus = schedule_workers(schedule)
+    ws, wbytes = _workspace(workspace, fused_topk_workspace_size(rows, max_model_len, block_kv, k, num_cus),
+                            q.device)
     _check(lib().fp8_fp4_paged_mqa_logits_topk(
         _p(q), rows, next_n, q.shape[1], q.shape[2], _p(kv_cache), kv_format, block_kv,
         kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
         block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
-        max_model_len, _p(logits), logits.stride(0), k, _p(out), out.stride(0), _p(workspace),
-        workspace.numel() * workspace.element_size(), _stream()), "fp8_fp4_paged_mqa_logits_topk")
+        max_model_len, _p(logits), logits.stride(0), k, _p(out), out.stride(0), _p(ws), wbytes,
+        _stream()), "fp8_fp4_paged_mqa_logits_topk")
     return logits, out

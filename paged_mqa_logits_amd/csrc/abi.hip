@@ -11,7 +11,7 @@ extern "C" const char *pml_status_string(int status) {
     case PML_ERR_STRIDE: return "page stride, table or output leading dimension too small or misaligned";
     case PML_ERR_ALIGN: return "a pointer breaks the 16-byte alignment";
     case PML_ERR_K: return "top-k k must be in [1, 4096]";
-    case PML_ERR_WORKSPACE: return "top-k workspace missing or smaller than required";
+    case PML_ERR_WORKSPACE: return "workspace missing or smaller than required";
     case PML_ERR_FORMAT: return "kv_format must be PML_KV_FP8 or PML_KV_MXFP4";
     case PML_ERR_UNSUPPORTED: return "argument combination not supported";
     case PML_ERR_HIP: return "a kernel launch failed (see hipGetLastError)";
@@ -19,4 +19,4 @@ extern "C" const char *pml_status_string(int status) {
     }
 }
 
-extern "C" int pml_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+extern "C" int pml_version(void) { return 2 * 10000 + 0 * 100 + 0; }

@@ -6,6 +6,17 @@
 // The fp8 per-token scale is positive, so it moves out of the ReLU; MXFP4
 // pages carry per-32-element e8m0 scales that the scaled MFMA applies.
 //
+// The ReLU is split as 2 max(0, x) = x + |x|. The linear half summed over the
+// heads is one dot product, sum_h w_h <q_h, k> = <u, k> with u = sum_h w_h q_h,
+// which runs on the matrix core: u is held as four fp8 pieces with one e8m0
+// scale per 32 elements each (u = p0 + p1 + p2 + p3 up to about 2^-16 of each
+// element), and one MFMA scores the 4 pieces of 4 rows against a 16-token
+// slice. The other half costs one VALU instruction per (head, token) value
+// (an FMA with an abs modifier): on gfx950 a wave64 VALU instruction takes
+// about 4.6 SIMD cycles and every MFMA about 10 of the same issue port, so
+// the epilogue, not the matrix core, set the speed of the two-instruction
+// ReLU-and-weight form.
+//
 // Work split (gfx950): a workgroup of 4 waves scores a row-piece (up to kGMax
 // rows of one request) against key blocks; q and w of the piece sit in LDS,
 // shared by the 4 waves. Each wave takes whole key blocks on its own: the
@@ -193,6 +204,124 @@ __device__ __forceinline__ void stage_rows_q4(const uint8_t *qv, const uint8_t *
         if (tid + k * NTH < g * PML_HEADS) s_w[tid + k * NTH] = wv[k];
 }
 
+// ---- the linear half: u = sum_h w_h q_h as four scaled fp8 pieces ----------
+//
+// Piece image of a row in LDS: 4 pseudo-heads (the pieces) of 128 fp8 codes,
+// laid out and swizzled as q (pseudo-head 4 i + p of row i at q_lds_off), so
+// that the A operand of pieces of rows 4m .. 4m+3 is load_a(s_u, m); then one
+// e8m0 byte per (pseudo-head, 32-element block), 4 per pseudo-head.
+// In HBM (the logits call's workspace) a row's pieces are [4][128] codes
+// followed, in a second array, by [4][4] scale bytes.
+constexpr int kPieces = 4;
+constexpr int kUBytes = kPieces * PML_HEAD_DIM;          // codes of one row: 512
+constexpr int kUScales = kPieces * (PML_HEAD_DIM / 32);  // scale bytes of one row: 16
+
+// Stage the pieces of rows r0 .. r0 + g - 1 (codes [rows][512], scales
+// [rows][16]) into the LDS image (the whole workgroup; loads first, then
+// before_store, then the stores).
+template <int NTH = kLThreads, typename B = NoWait>
+__device__ __forceinline__ void stage_pieces(const uint8_t *codes, const uint8_t *scales, int64_t r0, int g,
+                                             uint8_t *s_u, uint8_t *s_us, B before_store = B()) {
+    constexpr int kChunks = kUBytes / 16;                          // 32 per row
+    constexpr int kPer = (kGMax * (kChunks + 1) + NTH - 1) / NTH;  // + one chunk of scales per row
+    const int tid = threadIdx.x;
+    const int n = g * (kChunks + 1);
+    v4i x[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * NTH;
+        if (i < n) {
+            const int row = i / (kChunks + 1), c = i % (kChunks + 1);
+            x[k] = c < kChunks ? *(const v4i *)(codes + (r0 + row) * kUBytes + c * 16)
+                               : *(const v4i *)(scales + (r0 + row) * kUScales);
+        }
+    }
+    before_store();
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = tid + k * NTH;
+        if (i < n) {
+            const int row = i / (kChunks + 1), c = i % (kChunks + 1);
+            if (c < kChunks)
+                lds_st<v4i>(s_u + q_lds_off(kPieces * row + c / 8, c % 8), x[k]);
+            else
+                lds_st<v4i>(s_us + row * kUScales, x[k]);
+        }
+    }
+}
+
+// u[d] = sum_h w_h q_h[d] (fp32, heads in order) of the staged rows 0 .. g-1
+// and its four pieces, written to the LDS image (s_u, s_us). Piece p of a
+// 32-element block takes the e8m0 scale 2^e with e = floor(log2 m) - 7 for the
+// largest magnitude m of what the earlier pieces left (so its codes stay
+// below 256, within e4m3), rounds the rest over 2^e to fp8 and subtracts the
+// rounded value, which is exact in fp32. Each piece removes about 4 significant
+// bits, so after four the remainder is about 2^-16 of the element or less.
+// Q4: q is fp4 (values and e8m0 scales, stage_rows_q4's image).
+// The workgroup (NTH threads) runs it; callers put a barrier between the
+// staging of q / w and this, and between this and reads of the image.
+template <bool Q4, int NTH = kLThreads>
+__device__ __forceinline__ void derive_pieces(const uint8_t *s_q, const float *s_w, int g, uint8_t *s_u,
+                                              uint8_t *s_us) {
+    static_assert(NTH % 32 == 0, "32 threads per row");
+    const int tid = threadIdx.x;
+    for (int it = tid; it < kGMax * 32; it += NTH) {
+        const int row = it >> 5, dq = it & 31;  // elements d = 4 dq .. 4 dq + 3 of row `row`
+        const bool live = row < g;
+        float u[4] = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+            const uint8_t *qr = s_q + row * kQBytes;
+            const float *wr = s_w + row * PML_HEADS;
+#pragma unroll 8
+            for (int h = 0; h < PML_HEADS; ++h) {
+                const float wh = lds_ld<float>(wr + h);
+                float qv[4];
+                if constexpr (Q4) {
+                    const int c = dq >> 3;  // 32-element block
+                    const int sb = lds_ld<uint8_t>(qr + kQ4Values + 4 * h + c);
+                    const float sc = sb == 255 ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(1.0f, sb - 127);
+                    const uint32_t two = lds_ld<uint16_t>(qr + q4_lds_off(h, c) + 2 * (dq & 7));
+                    const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 0);
+                    const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 1);
+                    qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
+                } else {
+                    const uint32_t four = lds_ld<uint32_t>(qr + q_lds_off(h, dq >> 2) + 4 * (dq & 3));
+                    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(four, false);
+                    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(four, true);
+                    qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) u[j] = __builtin_fmaf(wh, qv[j], u[j]);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            float m = fmaxf(fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
+                            fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
+            // the 8 threads of a 32-element block are 8 consecutive lanes
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 8 : -127;  // m in [2^(e+7), 2^(e+8))
+            e = max(e, -127);
+            const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
+            const int lo2 = __builtin_amdgcn_cvt_pk_fp8_f32(u[0] * inv, u[1] * inv, 0, false);
+            const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(u[2] * inv, u[3] * inv, lo2, true);
+            const v2f d01 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+            const v2f d23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+            u[0] -= __builtin_amdgcn_ldexpf(d01[0], e);
+            u[1] -= __builtin_amdgcn_ldexpf(d01[1], e);
+            u[2] -= __builtin_amdgcn_ldexpf(d23[0], e);
+            u[3] -= __builtin_amdgcn_ldexpf(d23[1], e);
+            if (live) {
+                const int ph = kPieces * row + p;  // pseudo-head
+                lds_st<int>(s_u + q_lds_off(ph, dq >> 2) + 4 * (dq & 3), codes);
+                if ((dq & 7) == 0) lds_st<uint8_t>(s_us + ph * 4 + (dq >> 3), (uint8_t)(e + 127));
+            }
+        }
+    }
+}
+
 // A operand of fp4 q (heads 16 ht + lane % 16, k-block lane / 16: one 16-B
 // chunk, the upper half of the operand unused) and its e8m0 scale in bits 0-7.
 __device__ __forceinline__ v8i load_a_q4(const uint8_t *s_qrow, int ht, int &scale) {
@@ -243,16 +372,13 @@ __device__ __forceinline__ float reduce_slices(float *p) {  // p[BlockCfg::NT]
     }
 }
 
-// Score one staged row against the block in registers; returns twice this
-// lane's sum over all 64 heads for token out_token(lane) (before the key
-// scale; the factor 2 is exact and the caller folds 1/2 into the scale).
-constexpr int kPipe = 2;  // MFMAs issued ahead of the epilogue that reads them
+constexpr int kPipe = 3;  // MFMAs issued ahead of the epilogue that reads them
 
 // MFMA of one 16-token slice t. fp8 x fp8 takes the unscaled opcode: the
-// scaled form costs an extra VALU instruction per MFMA (it loads the scales),
-// measured as about a fifth more SIMD time for MFMA plus epilogue. MXFP4 keys
-// need their e8m0 block scales, with fp8 A at unit scale (`a_scale` = 127) or
-// fp4 A (Q4) at its own e8m0 scale: e2m1 x e2m1 runs at twice the fp8 rate.
+// scaled form costs an extra VALU instruction per MFMA (it loads the scales).
+// MXFP4 keys need their e8m0 block scales, with fp8 A at unit scale (`a_scale`
+// = 127) or fp4 A (Q4) at its own e8m0 scale: e2m1 x e2m1 runs at twice the
+// fp8 rate.
 template <bool FP4, int BKV, bool Q4 = false>
 __device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i &a, int t, int a_scale) {
     if constexpr (FP4) {
@@ -268,17 +394,102 @@ __device__ __forceinline__ v4f mfma_slice(const KeyRegs<FP4, BKV> &k_, const v8i
     }
 }
 
-template <bool FP4, int BKV, bool Q4 = false>
+// The transpose of the linear half: L[t] (lane group G = quad row G, tokens
+// 16t + j) to M[G] (token out_token(lane) in lane `lane`).
+template <int NT>
+__device__ __forceinline__ void lin_transpose(float *L, float *M) {
+    if constexpr (NT == 4) {
+        // L[t] row G = values of quad row G at tokens 16t + j; after the swaps,
+        // M[G] row t holds them, i.e. token 16t + j sits in lane 16t + j
+        swap32(L[0], L[2]);
+        swap32(L[1], L[3]);
+        swap16(L[0], L[1]);
+        swap16(L[2], L[3]);
+        M[0] = L[0];
+        M[1] = L[1];
+        M[2] = L[2];
+        M[3] = L[3];
+    } else {
+        // block_kv 32: token 16t + j belongs in lane 32t + j (out_token)
+        float A = L[0], B = L[1 % NT];
+        swap32(A, B);  // A: rows (0, 1, 0, 1) of quad rows 0/1; B: quad rows 2/3
+        float A2 = A, B2 = B;
+        swap16(A, A2);  // A: quad row 0 in lane groups 0 and 2; A2: quad row 1
+        swap16(B, B2);
+        M[0] = A;
+        M[1] = A2;
+        M[2] = B;
+        M[3] = B2;
+    }
+}
+
+// The linear half of rows 4m .. 4m+3 against the block: A is their pieces
+// (row 4m + G's piece p in A-row 4G + p, with its e8m0 scale), so lane group G
+// of the result of slice t holds row 4m + G's four piece dots for token
+// 16t + lane % 16 in its four registers; their sum is <u, k> of that row and
+// token (before the key scale). A transpose of lane groups against slices
+// (permlane swaps, as in reduce_slices) then leaves row 4m + G's values in
+// M[G] with token out_token(lane) in lane `lane`, the layout score_row
+// returns, so a row adds its own M[G] after its reduction, whatever its place
+// in the quad. fp8 keys take unit B scales (their fp32 per-token scale is
+// applied with the rest of the score).
+template <bool FP4, int BKV>
+__device__ __forceinline__ void lin_quad(const KeyRegs<FP4, BKV> &k_, const uint8_t *s_u, const uint8_t *s_us,
+                                         int m, float *M) {  // M[4]
+    using C = BlockCfg<FP4, BKV>;
+    const int lane = lane_id();
+    v8i a = load_a<false>(s_u, m);
+    int sc = lds_ld<uint8_t>(s_us + (16 * m + (lane & 15)) * 4 + (lane >> 4));
+    v4f d[C::NT];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+        if constexpr (FP4) {
+            const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3], 0, 0, 0, 0};
+            d[t] = mfma_scaled<4>(a, b, sc, (int)(k_.sc[t] & 0xffu));
+        } else {
+            const v8i b = v8i{k_.v[t][0][0], k_.v[t][0][1], k_.v[t][0][2], k_.v[t][0][3],
+                              k_.v[t][1][0], k_.v[t][1][1], k_.v[t][1][2], k_.v[t][1][3]};
+            d[t] = mfma_scaled<0>(a, b, sc, 127);
+        }
+    }
+    float L[C::NT];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) L[t] = (d[t][0] + d[t][1]) + (d[t][2] + d[t][3]);
+    lin_transpose<C::NT>(L, M);
+}
+
+
+// Score one staged row against the block in registers: this lane's
+// sum_h w_h |x_h|, x_h = <q_h, k>, for token out_token(lane), before the key
+// scale. With the linear half <u, k> (lin_quad) it gives twice the score,
+//   2 sum_h w_h max(0, x_h) = <u, k> + sum_h w_h |x_h|;
+// the factor 2 is exact and the caller folds 1/2 into the scale. The sum here
+// costs one FMA with an abs modifier per (head, token) value.
+//
+// With LIN the row also scores the linear half of its quad m (as lin_quad,
+// into M[0..3]): its MFMAs lead the row's MFMA stream and their sums and
+// transpose trail it, so they overlap the row's own work instead of forming a
+// dependent chain of their own.
+template <bool FP4, int BKV, bool Q4 = false, bool LIN = false>
 __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const uint8_t *s_qrow,
-                                           const float *s_wrow) {
+                                           const float *s_wrow, const uint8_t *s_u = nullptr,
+                                           const uint8_t *s_us = nullptr, int m = 0, float *M = nullptr) {
     static_assert(!Q4 || FP4, "fp4 q pairs with MXFP4 keys");
     using C = BlockCfg<FP4, BKV>;
     const int lane = lane_id();
     const int grp = lane >> 4;
+    constexpr int NL = LIN ? C::NT : 0;  // leading MFMAs of the linear half
     float p[C::NT];
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t) p[t] = 0.f;
-    // all LDS operands of the row first: one wait instead of one per head tile
+    // LDS operands in the order of use (the linear half's, then head tile 0,
+    // 1, ...): compiler barriers keep the reads in this order, so each MFMA
+    // waits only for the reads before it
+    [[maybe_unused]] v8i al;
+    int sl = 0;
+    if constexpr (LIN) {
+        al = load_a<false>(s_u, m);
+        sl = lds_ld<uint8_t>(s_us + (16 * m + (lane & 15)) * 4 + (lane >> 4));
+        asm volatile("" ::: "memory");
+    }
     v8i av[4];
     v4f wv[4];
     [[maybe_unused]] int asc[4];  // fp4 q: A scale per head tile
@@ -289,41 +500,67 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
         else
             av[ht] = load_a<FP4>(s_qrow, ht);
         wv[ht] = lds_ld<v4f>(s_wrow + 16 * ht + 4 * grp);
+        asm volatile("" ::: "memory");
     }
-    // MFMA k = (head tile k / NT, slice k % NT) is issued kPipe steps before
-    // its epilogue, so the matrix core works while the VALU folds earlier
-    // results and few wait states are padded between an MFMA and its reader.
-    // The MFMA intrinsics have no side effects, so empty volatile asm
-    // statements pin the order: each MFMA takes an operand (its A tile, or
-    // for MXFP4 the unit A scale) that the asm before it claims to rewrite,
-    // and each epilogue reads its result only after the asm that follows the
-    // next MFMAs. (fp4 q: the operand is the head tile's A scale.)
+    // MFMA k (after the NL linear ones: head tile (k - NL) / NT, slice
+    // (k - NL) % NT) is issued kPipe steps before its epilogue, so the matrix
+    // core works while the VALU folds earlier results, and enough independent
+    // instructions separate an MFMA from its reader that few wait states are
+    // padded. The MFMA intrinsics have no side effects, so empty volatile asm
+    // statements pin the order: each MFMA takes an operand (its A tile, or for
+    // MXFP4 the unit A scale) that an asm before it claims to rewrite, and that
+    // asm also reads the previous epilogue's result, so epilogues stay between
+    // the MFMAs. (fp4 q: the operand is the head tile's A scale.)
     constexpr int NK = 4 * C::NT;
-    v4f d[NK];
+    v4f d[NL + NK];
+    [[maybe_unused]] float L[C::NT];
     int unit = 127;  // e8m0 1.0
+    float last = 0.f;  // the accumulator the previous epilogue wrote
 #pragma unroll
-    for (int k = 0; k < NK + kPipe; ++k) {
-        if (k < NK) {
+    for (int k = 0; k < NL + NK + kPipe; ++k) {
+        if (k < NL) {
+            asm volatile("" : "+v"(sl) : "v"(last));
+            if constexpr (FP4) {
+                const v8i b = v8i{k_.v[k][0][0], k_.v[k][0][1], k_.v[k][0][2], k_.v[k][0][3], 0, 0, 0, 0};
+                d[k] = mfma_scaled<4>(al, b, sl, (int)(k_.sc[k] & 0xffu));
+            } else {
+                const v8i b = v8i{k_.v[k][0][0], k_.v[k][0][1], k_.v[k][0][2], k_.v[k][0][3],
+                                  k_.v[k][1][0], k_.v[k][1][1], k_.v[k][1][2], k_.v[k][1][3]};
+                d[k] = mfma_scaled<0>(al, b, sl, 127);
+            }
+        } else if (k < NL + NK) {
+            const int j = k - NL;
             if constexpr (Q4) {
-                asm volatile("" : "+v"(asc[k / C::NT]));
-                d[k] = mfma_slice<FP4, BKV, true>(k_, av[k / C::NT], k % C::NT, asc[k / C::NT]);
+                asm volatile("" : "+v"(asc[j / C::NT]) : "v"(last));
+                d[k] = mfma_slice<FP4, BKV, true>(k_, av[j / C::NT], j % C::NT, asc[j / C::NT]);
             } else {
                 if constexpr (FP4)
-                    asm volatile("" : "+v"(unit));
+                    asm volatile("" : "+v"(unit) : "v"(last));
                 else
-                    asm volatile("" : "+v"(av[k / C::NT]));
-                d[k] = mfma_slice<FP4, BKV>(k_, av[k / C::NT], k % C::NT, unit);
+                    asm volatile("" : "+v"(av[j / C::NT]) : "v"(last));
+                d[k] = mfma_slice<FP4, BKV>(k_, av[j / C::NT], j % C::NT, unit);
             }
         }
         if (k >= kPipe) {
-            const int e = k - kPipe, ht = e / C::NT, t = e % C::NT;
+            const int e = k - kPipe;
             asm volatile("" : "+v"(d[e]));
-            // d + |d| = 2 ReLU(d) is one add with an abs modifier (fmaxf would
-            // canonicalise its input first); the factor 2 is taken out at the end
+            if (e < NL) {
+                L[e] = (d[e][0] + d[e][1]) + (d[e][2] + d[e][3]);
+                last = L[e];
+            } else {
+                const int j = e - NL, ht = j / C::NT, t = j % C::NT;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p[t] = __builtin_fmaf(wv[ht][i], d[e][i] + __builtin_fabsf(d[e][i]), p[t]);
+                for (int i = 0; i < 4; ++i) {
+                    if (ht == 0 && i == 0)
+                        p[t] = wv[ht][i] * __builtin_fabsf(d[e][i]);
+                    else
+                        p[t] = __builtin_fmaf(wv[ht][i], __builtin_fabsf(d[e][i]), p[t]);
+                }
+                last = p[t];
+            }
         }
     }
+    if constexpr (LIN) lin_transpose<C::NT>(L, M);
     return reduce_slices<FP4, BKV>(p);
 }
 

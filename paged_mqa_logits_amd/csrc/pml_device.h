@@ -16,12 +16,11 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
-constexpr int kGMax = 8;        // rows of one piece scored against a shared key block
-constexpr int kCostBase = 2;    // schedule weight of a block: kCostBase + rows
-constexpr int kChunksPerCU = 8;   // schedule chunks per logits workgroup
-constexpr int kStaticChunks = 7;  // of which each workgroup's own run covers this many
-constexpr int kPools = 8;                 // counters the remaining chunks are handed out from
-constexpr int kPoolStride = 32;           // int32 between counters (one 128-byte line each)
+#ifndef PML_GMAX
+#define PML_GMAX 8
+#endif
+constexpr int kGMax = PML_GMAX;  // rows of one piece scored against a shared key block
+constexpr int kCostBase = 4;    // schedule weight of a block: kCostBase + rows
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

@@ -39,24 +39,35 @@ struct RaggedArgs {
 
 // One step of a wave's block loop (see wave_step of the paged kernel); every
 // row of the piece is stored, -inf outside its [lo, hi) (lane i of lo_lane /
-// hi_lane holds the bounds of row i).
+// hi_lane holds the bounds of row i). Rows go in quads, the linear half of a
+// quad scored once (lin_quad).
 template <bool PF>
 __device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g, int b,
                                             const KeyRegs<false, 64> &kc, int bp, KeyRegs<false, 64> &kp,
-                                            const uint8_t *s_q, const float *s_w, int lo_lane, int hi_lane,
-                                            WaveSlot<64> &sl, int &mask, int &col0p) {
+                                            const uint8_t *s_q, const float *s_w, const uint8_t *s_u,
+                                            const uint8_t *s_us, int lo_lane, int hi_lane, WaveSlot<64> &sl,
+                                            int &mask, int &col0p) {
     touch<false, 64>(kc);
     flush_slot<64>(sl, mask, row0, col0p, a.N, a.out, a.out_ld);
     if constexpr (PF) load_contig(a.k, a.k_scale, a.N, bp * 64, kp);
     const int lane = lane_id();
     const int s = b * 64 + lane;
     const float scale = 0.5f * __uint_as_float(kc.sc[0]);  // 1/2: see score_row
-    for (int i = 0; i < g; ++i) {
-        const int lo = __builtin_amdgcn_readlane(lo_lane, i);
-        const int hi = __builtin_amdgcn_readlane(hi_lane, i);
-        float v = score_row<false, 64>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS) * scale;
-        if (s < lo || s >= hi) v = -__builtin_inff();
-        lds_st<float>(&sl.v[i][lane], v);
+    for (int q0 = 0; q0 < g; q0 += 4) {
+        float M[4];
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+            const int i = q0 + G;
+            if (i >= g) break;
+            const int lo = __builtin_amdgcn_readlane(lo_lane, i);
+            const int hi = __builtin_amdgcn_readlane(hi_lane, i);
+            const float sr = G == 0 ? score_row<false, 64, false, true>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS,
+                                                                        s_u, s_us, q0 >> 2, M)
+                                    : score_row<false, 64>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS);
+            float v = (sr + M[G]) * scale;
+            if (s < lo || s >= hi) v = -__builtin_inff();
+            lds_st<float>(&sl.v[i][lane], v);
+        }
     }
     mask = (1 << g) - 1;
     col0p = b * 64;
@@ -66,6 +77,8 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
     constexpr int BKV = 64;
     __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
     __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_u[kGMax * kUBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_us[kGMax * kUScales];
     __shared__ int s_lo[kGMax];
     __shared__ int s_hi[kGMax];
     __shared__ __attribute__((aligned(16))) WaveSlot<BKV> s_slot[kCW];
@@ -118,6 +131,8 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
         s_hi[tid] = min(max(a.ke[row0 + tid], lo), N);
     }
     barrier_lds();
+    derive_pieces<false>(s_q, s_w, g, s_u, s_us);
+    barrier_lds();
 
     const int lo_lane = lds_ld<int>(&s_lo[lane_id() % kGMax]);  // lane i: bounds of row i
     const int hi_lane = lds_ld<int>(&s_hi[lane_id() % kGMax]);
@@ -128,8 +143,8 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
     KeyRegs<false, BKV> k0, k1, k2;
     int mask = 0, col0p = 0;
     auto step = [&](const KeyRegs<false, BKV> &kc, int j, KeyRegs<false, BKV> &kp, auto pf) {
-        ragged_step<decltype(pf)::value>(a, row0, g, b0 + kCW * j, kc, b0 + kCW * (j + 2), kp, s_q, s_w, lo_lane, hi_lane,
-                                         sl, mask, col0p);
+        ragged_step<decltype(pf)::value>(a, row0, g, b0 + kCW * j, kc, b0 + kCW * (j + 2), kp, s_q, s_w, s_u, s_us,
+                                         lo_lane, hi_lane, sl, mask, col0p);
     };
     constexpr std::true_type PF{};
     constexpr std::false_type NOPF{};

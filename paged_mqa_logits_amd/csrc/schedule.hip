@@ -1,27 +1,25 @@
-// paged_mqa_logits_metadata: split (row-piece, key-block) units into chunks
-// that the persistent workgroups of the paged-logits kernel take in turn.
+// paged_mqa_logits_metadata: split the (row-piece, key-block) units of the
+// paged-logits call into one range per persistent workgroup.
 //
-// The pages fix only that the schedule is sized by the number of persistent
-// workers and that a row slice needs its own ("vllm.model_executor.layers.
-// sparse_attn_indexer", _varlen_decode_rows). Content (this library's): units
-// are ordered by piece then block; a block of a piece with g rows costs
-// kCostBase + g. The work is cut into C = kChunksPerCU * num_CUs chunks:
-// chunk c starts at the unit holding cost offset floor(c * T / C) of the
-// total T, and entry C is (num_rows, 0). After it come kPools 64-bit work
-// counters of the logits call, one per 128-byte line, set to zero here.
-// Logits workgroup w first runs chunks [kStaticChunks * w, kStaticChunks *
-// (w + 1)) as one range; the remaining chunks are handed out through the
-// counters, so a workgroup that runs slow (on a compute unit shared with heavy
-// work, say) takes fewer of them.
+// The pages fix that the schedule has one row per persistent worker plus one
+// (a caller reads the worker count back as schedule.shape[0] - 1) and that a
+// row slice needs its own ("vllm.model_executor.layers.sparse_attn_indexer",
+// _varlen_decode_rows). Content (this library's): units are ordered by piece
+// then block; a block of a piece with g rows costs kCostBase + g. The work is
+// cut into W = num_CUs ranges: entry c is the unit holding cost offset
+// floor(c * T / W) of the total T, as (first row of its piece, block offset),
+// and entry W is (num_rows, 0). Logits workgroup c scores the units from
+// entry c to entry c + 1. The logits call only reads the schedule, so one
+// schedule serves any number of calls, at the same time too.
 //
 // One workgroup of 1024 threads walks the rows in tiles of 1024: every
 // thread loads its row's visible length and group-end flag into LDS (plus a
 // halo of kGMax rows), a max-scan finds each row's group start, the thread of
 // a piece's first row reads the piece's rows and extent from LDS, and a
-// sum-scan of the piece costs gives each piece's offset, and each chunk that
-// starts in the tile finds its piece by a binary search over those offsets.
+// sum-scan of the piece costs gives each piece's offset, and each entry that
+// falls in the tile finds its piece by a binary search over those offsets.
 // Up to 1024 rows take one walk; more take two (the total first). The walk is
-// cheap next to the searches, so ceil(C / 1024) workgroups (at most 64) each
+// cheap next to the searches, so ceil(W / 1024) workgroups (at most 64) each
 // walk all rows and write an equal share of the entries: about one search per
 // thread.
 #include "rows.h"
@@ -156,7 +154,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
         sh.cost_carry = 0;
     }
     const bool first = blockIdx.x == 0;
-    if (first && tid < kPools * kPoolStride) sched[2 * W + 2 + tid] = 0;  // work counters (64-bit), padding
     __syncthreads();
     long long total;
     if (n <= kSchedThreads) {
@@ -237,7 +234,7 @@ extern "C" int paged_mqa_logits_metadata(const int32_t *context_lens, int num_ro
     if (block_kv != 32 && block_kv != 64) return PML_ERR_BLOCK_KV;
     if (paged_mqa_logits_schedule_rows(num_CUs) < 0) return PML_ERR_SHAPE;
     pml::RowView v{context_lens, indices, context_lens_2d ? 1 : 0, next_n, num_rows};
-    const int W = pml::kChunksPerCU * num_CUs;
+    const int W = num_CUs;
     const int blocks = std::min((W + pml::kSchedThreads - 1) / pml::kSchedThreads, pml::kSchedMaxBlocks);
     hipLaunchKernelGGL(pml::schedule_kernel, dim3(blocks), dim3(pml::kSchedThreads), 0, (hipStream_t)stream, v,
                        block_kv, W, schedule);
@@ -246,5 +243,5 @@ extern "C" int paged_mqa_logits_metadata(const int32_t *context_lens, int num_ro
 
 extern "C" int paged_mqa_logits_schedule_rows(int num_CUs) {
     if (num_CUs < 1 || num_CUs > (1 << 20)) return -1;
-    return pml::kChunksPerCU * num_CUs + 1 + pml::kPools * pml::kPoolStride / 2;
+    return num_CUs + 1;
 }

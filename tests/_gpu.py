@@ -100,6 +100,40 @@ def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, weights_rows: torch.Te
         raise AssertionError(f"{what}: {bad.sum()} cells out of tolerance, e.g. {[(tuple(x), gpu[tuple(x)], ref[tuple(x)]) for x in i]}")
 
 
+# Exactly representable inputs (exactify_*): every product and partial sum of
+# the plain evaluation is exact in fp32, but the linear half of the score runs
+# on the matrix core as <sum_h w_h q_h, k>, and the fp8 MFMA may drop low bits
+# of products far below the largest in a dot product (by up to about 1e-4 of
+# the dot product's sum of |products|, measured on full-range random operands).
+# That sum is at most the cell's absolute mass (oracle.brute.paged_mass), and the
+# linear half enters the score with a factor 1/2, so such cells must match the
+# oracle within MASS_FRAC of their mass: far below the acceptance tolerance, and
+# far below what a wrong index, page or mask produces.
+MASS_FRAC = 2.0 ** -14
+
+
+def assert_within_mass(gpu: np.ndarray, ref: np.ndarray, mass: np.ndarray, what: str = "",
+                       frac: float = MASS_FRAC, rel: float = 0.0) -> None:
+    """Masked cells exactly -inf; others |gpu - ref| <= frac * mass + rel * |ref|."""
+    assert gpu.shape == ref.shape == mass.shape, (gpu.shape, ref.shape, mass.shape)
+    assert not np.any(gpu == SENTINEL), f"{what}: unwritten cells"
+    masked = np.isneginf(ref)
+    bad_mask = masked != np.isneginf(gpu)
+    assert not bad_mask.any(), f"{what}: -inf pattern differs at {np.argwhere(bad_mask)[:5]}"
+    fin = ~masked
+    err = np.where(fin, np.abs(gpu.astype(np.float64) - np.where(fin, ref, 0.0)), 0.0)
+    bound = frac * mass + rel * np.abs(np.where(fin, ref, 0.0))
+    if fin.any():
+        ratio = float(np.max(np.where(fin, err / np.maximum(mass, 1e-300), 0.0)))
+        print(f"[gpu-check] {what or 'logits'}: max err/mass {ratio:.3g} over {int(fin.sum())} cells, "
+              f"{int((fin & (err > 0)).sum())} inexact", flush=True)
+    bad = fin & ~(err <= bound)
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} cells beyond the mass bound, e.g. "
+                             f"{[(tuple(x), gpu[tuple(x)], ref[tuple(x)], mass[tuple(x)]) for x in i]}")
+
+
 def exactify_fp8_case(case: syn.PagedCase, seed: int) -> None:
     """Make every product and partial sum exact in fp32: integer fp8 codes in
     [-8, 8], power-of-two scales 2^-4..2^2 and weights in (1/8)Z within [-4, 4]

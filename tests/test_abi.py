@@ -22,7 +22,8 @@ def test_header_declares_the_four_calls():
     for n in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
               "top_k_per_row_workspace_size", "pml_status_string", "pml_version",
               "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
-              "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q"):
+              "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q",
+              "fp8_fp4_paged_mqa_logits_workspace_size", "paged_mqa_logits_schedule_rows"):
         assert n in names
 
 
@@ -33,16 +34,35 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_schedule_rows():
+    """The schedule has one row per worker plus the end, so a caller reads the
+    worker count back as schedule.shape[0] - 1 (sparse_attn_indexer page,
+    _varlen_decode_rows)."""
     L = pml.lib()
     for W in (1, 7, 512, 1 << 20):
-        assert L.paged_mqa_logits_schedule_rows(W) == 8 * W + 129
-        assert pml.schedule_rows(W) == 8 * W + 129
+        assert L.paged_mqa_logits_schedule_rows(W) == W + 1
+        assert pml.schedule_rows(W) == W + 1
     for W in (0, -3, (1 << 20) + 1):
         assert L.paged_mqa_logits_schedule_rows(W) == -1
     import torch
-    assert pml.schedule_workers(torch.empty(pml.schedule_rows(37), 2)) == 37
+    sched = torch.empty(pml.schedule_rows(37), 2)
+    assert pml.schedule_workers(sched) == 37 == sched.shape[0] - 1
     with pytest.raises(ValueError):
-        pml.schedule_workers(torch.empty(pml.schedule_rows(37) + 1, 2))
+        pml.schedule_workers(torch.empty(1, 2))
+
+
+def _ws_bytes(rows, W):
+    r = lambda b: (b + 255) // 256 * 256
+    # pieces of u per row (4 x 128 fp8 codes, then 4 x 4 e8m0 scale bytes), a split
+    # point per range (2 x int32) and 8 pool counters 128 bytes apart
+    return r(512 * rows) + r(16 * rows) + r(8 * W) + r(8 * 128)
+
+
+def test_logits_workspace_size():
+    f = pml.lib().fp8_fp4_paged_mqa_logits_workspace_size
+    for rows in (0, 1, 135, 4097):
+        for W in (1, 4, 512, 1 << 20):
+            assert f(rows, W) == _ws_bytes(rows, W)
+    assert f(-1, 512) == 0 and f(4, 0) == 0 and f(4, (1 << 20) + 1) == 0
 
 
 def test_status_strings_and_version():
@@ -57,10 +77,13 @@ P = ctypes.c_void_p
 FAKE = P(0x1000)  # never dereferenced: every call below fails validation first
 
 
+WS = P(0x100000)  # 256-B aligned, never dereferenced
+
+
 def _paged(**kw):
-    a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
+    a = dict(q=FAKE, qs=None, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
              w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
-             max_ctx=512, out=FAKE, ld=512, stream=None)
+             max_ctx=512, out=FAKE, ld=512, ws=WS, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return pml.lib().fp8_fp4_paged_mqa_logits(*a.values())
 
@@ -73,9 +96,18 @@ def _paged(**kw):
     (dict(ld=514, max_ctx=513), 5), (dict(pages=0), 5), (dict(bt_cols=9), 5),
     (dict(fmt=1, bkv=32, stride=32 * 68 - 16), 5),
     (dict(q=P(0x1001)), 6), (dict(out=P(0x1004)), 6), (dict(sched=P(0x1008)), 6),
+    # q_scale (fp4 q) needs MXFP4 keys and 16-B alignment
+    (dict(qs=FAKE), 10), (dict(qs=P(0x1008), fmt=1, bkv=32, stride=32 * 68), 6),
+    # the workspace: missing, one byte too small for 4 rows and 4 workgroups, misaligned
+    (dict(ws=None), 8), (dict(ws_bytes=_ws_bytes(4, 4) - 1), 8), (dict(ws=P(0x100010)), 6),
 ])
 def test_paged_validation(kw, code):
     assert _paged(**kw) == code
+
+
+def test_paged_workspace_exact_size_passes_validation():
+    # the smallest valid workspace gets past every host check (a NULL block table is then the first error)
+    assert _paged(ws_bytes=_ws_bytes(4, 4), bt=None) == 1
 
 
 def test_paged_zero_rows_is_ok_without_gpu():
@@ -143,7 +175,7 @@ def test_merge_zero_rows_and_largest_pairs():
 def _paged_bf16(**kw):
     a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
              w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
-             max_ctx=512, out=FAKE, ld=512, stream=None)
+             max_ctx=512, out=FAKE, ld=512, ws=WS, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return pml.lib().fp8_fp4_paged_mqa_logits_bf16(*a.values())
 
@@ -151,6 +183,7 @@ def _paged_bf16(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(H=32), 2), (dict(fmt=2), 9), (dict(bkv=16), 3), (dict(q=None), 1), (dict(out=None), 1),
     (dict(ld=508), 5), (dict(ld=516, max_ctx=512), 5), (dict(ld=500), 5), (dict(out=P(0x1008)), 6),
+    (dict(ws=None), 8),
 ])
 def test_paged_bf16_validation(kw, code):
     assert _paged_bf16(**kw) == code
@@ -183,13 +216,14 @@ def test_upcast_empty_is_ok():
 def _paged_fp4q(**kw):
     a = dict(q=FAKE, qs=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=1, bkv=32, stride=32 * 68, pages=10,
              w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
-             max_ctx=256, out=FAKE, ld=256, stream=None)
+             max_ctx=256, out=FAKE, ld=256, ws=WS, ws_bytes=1 << 20, stream=None)
     a.update(kw)
     return pml.lib().fp8_fp4_paged_mqa_logits_fp4q(*a.values())
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(fmt=0, bkv=64, stride=64 * 132), 10), (dict(fmt=0, bkv=64, stride=64 * 132, rows=0), 10),
+    (dict(ws=None), 8),
     (dict(qs=None), 1), (dict(q=None), 1), (dict(qs=P(0x1008)), 6), (dict(H=32), 2), (dict(bkv=16), 3),
     (dict(ld=252), 5),
 ])
@@ -204,7 +238,7 @@ def test_paged_fp4q_zero_rows():
 def _fused(**kw):
     a = dict(q=FAKE, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
              w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
-             max_ctx=512, out=FAKE, ld=512, k=64, topk=FAKE, topk_ld=64, ws=P(0x10000),
+             max_ctx=512, out=FAKE, ld=512, k=64, topk=FAKE, topk_ld=64, ws=P(0x100000),
              ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return pml.lib().fp8_fp4_paged_mqa_logits_topk(*a.values())
@@ -212,7 +246,7 @@ def _fused(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(k=0), 7), (dict(k=4097), 7), (dict(H=32), 2), (dict(bkv=16), 3), (dict(topk=None), 1),
-    (dict(topk_ld=63), 5), (dict(ws=None), 8), (dict(ws_bytes=100), 8), (dict(ws=P(0x10010)), 6),
+    (dict(topk_ld=63), 5), (dict(ws=None), 8), (dict(ws_bytes=100), 8), (dict(ws=P(0x100010)), 6),
     (dict(q=None), 1), (dict(ld=500), 5),
 ])
 def test_fused_validation(kw, code):
@@ -221,10 +255,12 @@ def test_fused_validation(kw, code):
 
 def test_fused_workspace_size():
     f = pml.lib().fp8_fp4_paged_mqa_logits_topk_workspace_size
-    # 3 x [rows] int32 regions + counts [rows][nb] + pairs [rows][nb * bkv][2], each 256-B aligned
-    rows, mc, bkv, k = 135, 131072, 64, 2048
+    # the logits call's workspace, then 3 x [rows] int32 regions + counts [rows][nb]
+    # + pairs [rows][nb * bkv][2], each 256-B aligned
+    rows, mc, bkv, k, W = 135, 131072, 64, 2048, 512
     nb = mc // bkv
     r = lambda b: (b + 255) // 256 * 256
-    assert f(rows, mc, bkv, k) == 3 * r(4 * rows) + r(4 * rows * nb) + r(8 * rows * nb * bkv)
-    assert f(rows, mc, 48, k) == 0 and f(rows, mc, bkv, 0) == 0 and f(-1, mc, bkv, k) == 0
+    logits_ws = pml.lib().fp8_fp4_paged_mqa_logits_workspace_size(rows, W)
+    assert f(rows, mc, bkv, k, W) == logits_ws + 3 * r(4 * rows) + r(4 * rows * nb) + r(8 * rows * nb * bkv)
+    assert f(rows, mc, 48, k, W) == 0 and f(rows, mc, bkv, 0, W) == 0 and f(-1, mc, bkv, k, W) == 0
     assert _fused(rows=0, topk=None, ws=None) == 0

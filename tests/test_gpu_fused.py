@@ -20,9 +20,10 @@ from tests import _gpu as G
 pytestmark = pytest.mark.gpu
 
 
-def _ws_done(ws: torch.Tensor, rows: int) -> np.ndarray:
-    reg = (4 * rows + 255) // 256 * 256  # thresholds, widths, done flags: [rows] each
-    return ws[2 * reg: 2 * reg + 4 * rows].view(torch.int32).cpu().numpy()
+def _ws_done(ws: torch.Tensor, rows: int, num_cus: int) -> np.ndarray:
+    base = pml.logits_workspace_size(rows, num_cus)  # the logits call's region comes first
+    reg = (4 * rows + 255) // 256 * 256  # then thresholds, widths, done flags: [rows] each
+    return ws[base + 2 * reg: base + 2 * reg + 4 * rows].view(torch.int32).cpu().numpy()
 
 
 def _check(case, k, t=None):
@@ -35,7 +36,7 @@ def _check(case, k, t=None):
     ke = t["lens"].reshape(-1)
     nn = 1 if case.lens_2d else case.next_n
     ref_topk = pml.top_k_per_row(ref_logits, ke, k, next_n=nn, max_width=case.max_ctx)
-    need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, k)
+    need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, k, pml.schedule_workers(sched))
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=d)  # garbage-filled: no initialisation needed
     logits, topk = pml.fp8_fp4_paged_mqa_logits_topk(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched,
                                                      case.max_ctx, k, t["indices"], kv_format=case.kv_format,
@@ -47,7 +48,7 @@ def _check(case, k, t=None):
     np.testing.assert_array_equal(got, ref_topk.cpu().numpy())
     vis = np.minimum(syn.vis_per_row(case), case.max_ctx)
     np.testing.assert_array_equal(got, oracle.topk(L.astype(np.float64), vis, k))
-    done = _ws_done(ws, case.rows)
+    done = _ws_done(ws, case.rows, pml.schedule_workers(sched))
     print(f"[gpu-check] fused top-k k={k}: {int(done.sum())} of {case.rows} rows from candidates", flush=True)
     return done, vis
 

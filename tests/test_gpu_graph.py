@@ -25,11 +25,12 @@ def test_captured_step_matches_eager_on_every_replay():
     sched = torch.empty(pml.schedule_rows(W), 2, dtype=torch.int32, device=d)
     logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
     topk = torch.empty(case.rows, 64, dtype=torch.int32, device=d)
+    ws = torch.empty(pml.logits_workspace_size(case.rows, W), dtype=torch.uint8, device=d)
 
     def step(x, c):
         pml.paged_mqa_logits_metadata(x["lens"], c.block_kv, W, indices=x["indices"], out=sched)
         pml.fp8_fp4_paged_mqa_logits(x["q"], x["kv"], x["w"], x["lens"], x["bt"], sched, c.max_ctx, x["indices"],
-                                     kv_format=c.kv_format, block_kv=c.block_kv, logits=logits)
+                                     kv_format=c.kv_format, block_kv=c.block_kv, logits=logits, workspace=ws)
         pml.top_k_per_row(logits, x["lens"], 64, max_width=c.max_ctx, out=topk)
 
     G.banner("graph capture of the decode step")
@@ -45,6 +46,7 @@ def test_captured_step_matches_eager_on_every_replay():
         sched.fill_(-7)
         logits.fill_(123.0)
         topk.fill_(-5)
+        ws.fill_(0x7F)
         if rep % 2:
             oth = torch.empty(other.rows, pml.logits_ld(other.max_ctx), dtype=torch.float32, device=d)
             pml.fp8_fp4_paged_mqa_logits(u["q"], u["kv"], u["w"], u["lens"], u["bt"],

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import oracle
+from oracle import brute
 from oracle import schedule as spec
 import paged_mqa_logits_amd as pml
 import pml_synth as syn
@@ -27,11 +28,9 @@ def _sched_case(lens, next_n, indices, bkv, W, lens_2d=False):
     it = None if indices is None else torch.as_tensor(np.asarray(indices), dtype=torch.int32).to(d)
     got = pml.paged_mqa_logits_metadata(lt, bkv, W, indices=it, next_n=next_n).cpu().numpy()
     rows = lt.numel() if (lens_2d or indices is not None or next_n == 1) else lt.numel() * next_n
-    C = 8 * W  # chunks
-    assert pml.schedule_rows(W) == C + 129
-    want = spec.schedule(np.asarray(lens), rows, next_n, lens_2d, indices, bkv, C)
-    np.testing.assert_array_equal(got[: C + 1], want)
-    assert not got[C + 1:].any()  # work counters start at zero
+    assert got.shape == (W + 1, 2)  # one range per workgroup, then the end
+    want = spec.schedule(np.asarray(lens), rows, next_n, lens_2d, indices, bkv, W)
+    np.testing.assert_array_equal(got, want)
 
 
 @pytest.mark.parametrize("seed", range(4))
@@ -100,18 +99,20 @@ def test_uniform_next_n(lens_2d, fmt):
     _check_case(case)
 
 
-def test_exact_arithmetic_bitwise():
-    """Integer-valued codes, power-of-two scales, weights in (1/8)Z: every sum is
-    exact in fp32, so the GPU must equal the oracle bit for bit."""
+def test_exact_arithmetic():
+    """Integer-valued codes, power-of-two scales, weights in (1/8)Z: every sum of
+    the plain evaluation is exact in fp32, so the GPU may differ from the oracle
+    only by what the matrix core drops in the linear half (tests/_gpu.py,
+    MASS_FRAC): this pins indexing, paging, grouping and masking independently
+    of the acceptance tolerance."""
     case = syn.make_paged_case([900, 64, 200, 1], [4, 2, 9, 1], seed=400, max_ctx=960)
     G.exactify_fp8_case(case, seed=401)
     G.banner("exact arithmetic fp8")
     gpu = G.run_paged(case)
-    ref = oracle.paged_logits(case).astype(np.float32)
-    np.testing.assert_array_equal(gpu, ref)
+    G.assert_within_mass(gpu, oracle.paged_logits(case), brute.paged_mass(case), "exact fp8")
 
 
-def test_exact_arithmetic_bitwise_fp4():
+def test_exact_arithmetic_fp4():
     case = syn.make_paged_case([500, 33, 96], [3, 1, 5], seed=410, kv_format=1, block_kv=32, max_ctx=512)
     kv = case.kv_cache.numpy()
     sc = kv[:, 32 * 64: 32 * 68]
@@ -124,8 +125,7 @@ def test_exact_arithmetic_bitwise_fp4():
     case.weights.copy_(torch.randint(-32, 33, case.weights.shape, generator=g).float() / 8)
     G.banner("exact arithmetic fp4")
     gpu = G.run_paged(case)
-    ref = oracle.paged_logits(case).astype(np.float32)
-    np.testing.assert_array_equal(gpu, ref)
+    G.assert_within_mass(gpu, oracle.paged_logits(case), brute.paged_mass(case), "exact fp4")
 
 
 # --------------------------------------------------------------------------
@@ -143,33 +143,50 @@ def test_grouping_and_worker_count_do_not_change_bits():
         np.testing.assert_array_equal(G.run_paged(case, t, num_cus=W), base)
 
 
-def test_schedule_reuse_across_calls():
-    """One schedule serves call after call (every layer of a step): its chunk
-    entries stay as the metadata call wrote them, each logits call advances
-    the work counters by the same amount, and the logits are the same bits."""
+def test_schedule_is_read_only_and_shared_by_concurrent_calls():
+    """One schedule serves many calls (every layer of a step), concurrent ones
+    too: the logits calls only read it. Two calls on two streams that share
+    the schedule, each with its own workspace, give the bits of the
+    single-stream call, which matches the oracle."""
     case = syn.make_paged_case([9000, 4100, 700, 12000], [3, 1, 6, 2], seed=520, max_ctx=12288)
-    t = G.upload(case)
-    G.banner("work counters: reuse of one schedule")
+    other = syn.make_paged_case([9000, 4100, 700, 12000], [3, 1, 6, 2], seed=521, max_ctx=12288)
+    t, u = G.upload(case), G.upload(other)
+    u["lens"], u["indices"], u["bt"] = t["lens"], t["indices"], t["bt"]  # same rows: same schedule
+    kv_u = u["kv"]
+    G.banner("schedule shared by two streams, separate workspaces")
+    d = G.dev()
     W = 37
-    C = 8 * W
     sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, W, indices=t["indices"])
-    entries = sched[: C + 1].clone()
-    ctr0 = sched[C + 1:].clone().view(torch.int64)
-    assert not ctr0.any()
-    outs, ctrs = [], []
-    for _ in range(3):
-        out = torch.full((case.rows, pml.logits_ld(case.max_ctx)), G.SENTINEL, dtype=torch.float32, device=G.dev())
-        pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx, t["indices"],
-                                     kv_format=case.kv_format, block_kv=case.block_kv, logits=out)
+    before = sched.clone()
+    ld = pml.logits_ld(case.max_ctx)
+
+    def call(x, kv, out, ws):
+        pml.fp8_fp4_paged_mqa_logits(x["q"], kv, x["w"], x["lens"], x["bt"], sched, case.max_ctx, x["indices"],
+                                     kv_format=case.kv_format, block_kv=case.block_kv, logits=out, workspace=ws)
+
+    need = pml.logits_workspace_size(case.rows, W)
+    ref_a = torch.full((case.rows, ld), G.SENTINEL, dtype=torch.float32, device=d)
+    ref_b = torch.full_like(ref_a, G.SENTINEL)
+    call(t, t["kv"], ref_a, None)
+    call(u, kv_u, ref_b, None)
+    torch.cuda.synchronize()
+    assert torch.equal(sched, before), "the logits call wrote to the schedule"
+    G.assert_logits_close(ref_a[:, : case.max_ctx].cpu().numpy(), oracle.paged_logits(case), case.weights)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        out_a = torch.full_like(ref_a, G.SENTINEL)
+        out_b = torch.full_like(ref_a, G.SENTINEL)
+        ws_a = torch.full((need,), 0x5A, dtype=torch.uint8, device=d)  # garbage: no initialisation needed
+        ws_b = torch.full((need,), 0xA5, dtype=torch.uint8, device=d)
         torch.cuda.synchronize()
-        assert torch.equal(sched[: C + 1], entries), "chunk entries changed by the logits call"
-        ctrs.append(sched[C + 1:].clone().view(torch.int64).cpu())
-        outs.append(out[:, : case.max_ctx].cpu().numpy())
-    assert ctrs[0].any()
-    assert torch.equal(ctrs[1], 2 * ctrs[0]) and torch.equal(ctrs[2], 3 * ctrs[0])
-    G.assert_logits_close(outs[0], oracle.paged_logits(case), case.weights)
-    for o in outs[1:]:
-        np.testing.assert_array_equal(o, outs[0])
+        with torch.cuda.stream(s1):
+            call(t, t["kv"], out_a, ws_a)
+        with torch.cuda.stream(s2):
+            call(u, kv_u, out_b, ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.view(torch.int32), ref_a.view(torch.int32)), f"stream 1, rep {rep}"
+        assert torch.equal(out_b.view(torch.int32), ref_b.view(torch.int32)), f"stream 2, rep {rep}"
+    assert torch.equal(sched, before)
 
 
 def test_plain_decode_equals_varlen_arange():
@@ -242,7 +259,7 @@ def test_no_rows_is_a_no_op():
     d = G.dev()
     lens = torch.zeros(0, dtype=torch.int32, device=d)
     sched = pml.paged_mqa_logits_metadata(lens, 64, 8)
-    assert sched.cpu().numpy().tolist() == [[0, 0]] * pml.schedule_rows(8)
+    assert sched.cpu().numpy().tolist() == [[0, 0]] * 9
     out = pml.fp8_fp4_paged_mqa_logits(torch.zeros(0, 64, 128, dtype=torch.uint8, device=d),
                                        torch.zeros(1, 64 * 132, dtype=torch.uint8, device=d),
                                        torch.zeros(0, 64, device=d), lens,

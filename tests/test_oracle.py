@@ -404,3 +404,25 @@ def test_golden_topk_out_of_range_bounds_are_clamped():
         got = oracle.topk(s, ke, c["k"], ks=ks)
         assert got[0].tolist() == c["expected"], c["derivation"]
         assert brute.topk(s, ke, c["k"], ks=ks)[0].tolist() == c["expected"], c["derivation"]
+
+
+def test_mass_bounds_the_score_and_equals_it_for_nonnegative_terms():
+    """brute.paged_mass / ragged_mass (the error scale of the exact-input GPU
+    tests): |score| <= mass always, and mass == score when every q, k and w is
+    non-negative (then no ReLU clips and no product is negative)."""
+    case = syn.make_paged_case([300, 70], [3, 1], seed=31, max_ctx=320)
+    m, L = brute.paged_mass(case), oracle.paged_logits(case)
+    fin = np.isfinite(L)
+    assert np.all(np.abs(L[fin]) <= m[fin] * (1 + 1e-12)) and np.all(m[~fin] == 0)
+    pos = syn.make_paged_case([300, 70], [3, 1], seed=32, max_ctx=320)
+    pos.q.copy_(pos.q & 0x7F)                      # clear the sign bits
+    kv = pos.kv_cache.numpy()
+    kv[:, : 64 * 128] &= np.where(kv[:, : 64 * 128] == syn.FP8_NAN, 0xFF, 0x7F).astype(np.uint8)
+    pos.weights.abs_()
+    m2, L2 = brute.paged_mass(pos), oracle.paged_logits(pos)
+    f2 = np.isfinite(L2)
+    np.testing.assert_allclose(m2[f2], L2[f2], rtol=1e-12)
+    rc = syn.make_ragged_case([40, 30], seed=33)
+    mr, Lr = brute.ragged_mass(rc), oracle.ragged_logits(rc)
+    fr = np.isfinite(Lr)
+    assert np.all(np.abs(Lr[fr]) <= mr[fr] * (1 + 1e-12))
