@@ -49,7 +49,8 @@ enum pml_status {
     PML_ERR_WORKSPACE = 8,     /* workspace missing or smaller than required           */
     PML_ERR_FORMAT = 9,        /* kv_format is neither PML_KV_FP8 nor PML_KV_MXFP4      */
     PML_ERR_UNSUPPORTED = 10,  /* an argument combination this version does not handle */
-    PML_ERR_HIP = 11           /* a kernel launch failed                               */
+    PML_ERR_HIP = 11,          /* a kernel launch failed                               */
+    PML_ERR_SCRATCH = 12       /* input larger than the allocation-free call's scratch */
 };
 
 /* Key-cache formats (sparse_attn_indexer page, _gather_workspace_shapes and
@@ -229,6 +230,26 @@ size_t top_k_per_row_workspace_size(int num_rows, int max_width, int k);
 int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
                   const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
                   int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fp8_fp4_paged_mqa_logits_noalloc - fp8_fp4_paged_mqa_logits without the
+ * workspace arguments, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid it). The
+ * call's scratch is a static array in device memory, one per GPU, held until
+ * the process ends; this call allocates nothing. Limits: num_rows <= 4096 and
+ * num_CUs <= 4096 (else PML_ERR_SCRATCH, nothing launched). All calls on one
+ * GPU share the array, so calls that overlap on one GPU (on different streams)
+ * race; calls in stream order do not. Every other argument, check and result
+ * is as for fp8_fp4_paged_mqa_logits.
+ */
+int fp8_fp4_paged_mqa_logits_noalloc(const void *q, const uint8_t *q_scale, int num_rows, int next_n,
+                                     int num_heads, int head_dim, const void *kv_cache, int kv_format,
+                                     int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                     const float *weights, const int32_t *context_lens,
+                                     int context_lens_2d, const int32_t *block_table,
+                                     int64_t block_table_ld, int block_table_cols,
+                                     const int32_t *schedule, int num_CUs, const int32_t *indices,
+                                     int max_ctx, float *logits, int64_t logits_ld, void *stream);
 
 /*
  * fp8_fp4_paged_mqa_logits_bf16 - the same call as fp8_fp4_paged_mqa_logits

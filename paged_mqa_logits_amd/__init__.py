@@ -32,7 +32,7 @@ _LIB_PATH = Path(__file__).resolve().parent / "libpml.so"
 _lib = None
 
 # status codes that mean "bad argument" (ValueError); the rest are RuntimeError
-_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10}
+_ARG_ERRORS = {1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 12}
 
 
 class PmlError(RuntimeError):
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.fp8_fp4_paged_mqa_logits.argtypes = [P, P] + body + [P, SZ, P]
         L.fp8_fp4_paged_mqa_logits_workspace_size.argtypes = [I, I]
         L.fp8_fp4_paged_mqa_logits_workspace_size.restype = SZ
+        if hasattr(L, "fp8_fp4_paged_mqa_logits_noalloc"):
+            L.fp8_fp4_paged_mqa_logits_noalloc.argtypes = [P, P] + body + [P]
         if hasattr(L, "fp8_fp4_paged_mqa_logits_bf16"):
             L.fp8_fp4_paged_mqa_logits_bf16.argtypes = [P] + body + [P, SZ, P]
             L.as_fp32_logits.argtypes = [P, I, I64, I, P, P, I64, P]
@@ -87,7 +89,7 @@ def lib() -> ctypes.CDLL:
         for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
                      "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
                      "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q",
-                     "fp8_fp4_paged_mqa_logits_topk"):
+                     "fp8_fp4_paged_mqa_logits_topk", "fp8_fp4_paged_mqa_logits_noalloc"):
             if hasattr(L, name):
                 getattr(L, name).restype = I
         L.pml_status_string.argtypes = [I]
@@ -218,7 +220,9 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     head_dim / 32]) q is packed e2m1 [rows, heads, head_dim / 2] (MXFP4 keys,
     fp32 logits). ``workspace``: uint8 scratch of at least
     ``logits_workspace_size(rows, schedule rows - 1)`` bytes (allocated when
-    None)."""
+    None), or ``"static"`` for the allocation-free call
+    (fp8_fp4_paged_mqa_logits_noalloc: the library's per-GPU scratch, up to
+    4096 rows and 4096 workgroups)."""
     _dev(q, "q", _FP8_TYPES)
     _dev(kv_cache, "kv_cache", (torch.uint8,))
     _dev(weights, "weights", _F32)
@@ -256,11 +260,18 @@ def fp8_fp4_paged_mqa_logits(q: torch.Tensor, kv_cache: torch.Tensor, weights: t
     num_cus = schedule_workers(schedule)
     if not schedule.is_contiguous():
         raise ValueError("schedule must be contiguous")
-    ws, wbytes = _workspace(workspace, logits_workspace_size(rows, num_cus), q.device)
-    tail = (rows, next_n, q.shape[1], head_dim, _p(kv_cache), kv_format, block_kv,
+    args = (rows, next_n, q.shape[1], head_dim, _p(kv_cache), kv_format, block_kv,
             kv_cache.stride(0), kv_cache.shape[0], _p(weights), _p(context_lens), l2d, _p(block_table),
             block_table.stride(0), block_table.shape[1], _p(schedule), num_cus, _p(indices),
-            max_model_len, _p(logits), logits.stride(0), _p(ws), wbytes, _stream())
+            max_model_len, _p(logits), logits.stride(0))
+    if isinstance(workspace, str):
+        if workspace != "static" or logits.dtype != torch.float32:
+            raise ValueError('workspace="static" (the allocation-free call) writes fp32 logits')
+        _check(lib().fp8_fp4_paged_mqa_logits_noalloc(_p(q), _p(q_scale), *args, _stream()),
+               "fp8_fp4_paged_mqa_logits_noalloc")
+        return logits
+    ws, wbytes = _workspace(workspace, logits_workspace_size(rows, num_cus), q.device)
+    tail = args + (_p(ws), wbytes, _stream())
     if logits.dtype == torch.float32:
         st = lib().fp8_fp4_paged_mqa_logits(_p(q), _p(q_scale), *tail)
     else:

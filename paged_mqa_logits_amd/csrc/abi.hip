@@ -15,6 +15,7 @@ extern "C" const char *pml_status_string(int status) {
     case PML_ERR_FORMAT: return "kv_format must be PML_KV_FP8 or PML_KV_MXFP4";
     case PML_ERR_UNSUPPORTED: return "argument combination not supported";
     case PML_ERR_HIP: return "a kernel launch failed (see hipGetLastError)";
+    case PML_ERR_SCRATCH: return "input larger than the static scratch of the allocation-free call";
     default: return "unknown status";
     }
 }

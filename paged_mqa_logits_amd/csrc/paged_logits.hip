@@ -22,6 +22,8 @@
 //    is read through the scalar cache; the counters only by vector atomics.
 //  * Columns past each row's last visible block are filled with -inf by the
 //    workgroups after their units (row-strided).
+#include <mutex>
+
 #include "logits_core.h"
 #include "rows.h"
 #include "select.h"
@@ -622,6 +624,70 @@ extern "C" int fp8_fp4_paged_mqa_logits(const void *q, const uint8_t *q_scale, i
                         page_stride_bytes, num_pages, weights, context_lens, context_lens_2d, block_table,
                         block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx, logits, logits_ld,
                         false, workspace, workspace_bytes, stream);
+}
+
+// ---- the allocation-free variant -------------------------------------------
+//
+// The logits call's scratch in a file-scope device array, for callers that
+// cannot allocate (code under graph capture, tight serving loops). Each GPU the
+// library runs on holds its own copy until the process ends. Its address is
+// looked up once per device with hipGetSymbolAddress (the array's name is not
+// a device address in host code) and that pointer is what the kernels get.
+// Every call on one GPU shares the array: the call's first kernel rewrites
+// all of it that the call reads (pieces, split points, zeroed counters), and
+// calls that overlap on one GPU race.
+constexpr int kNoAllocMaxRows = 4096;
+constexpr int kNoAllocMaxCUs = 4096;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[(kNoAllocMaxRows * (pml::kUBytes + pml::kUScales) +
+                                                  kNoAllocMaxCUs * 8 + pml::kPools * pml::kPoolStride * 4 + 4 * 256 +
+                                                  255) / 256 * 256];
+static void *g_scratch[kMaxDevices];
+static int g_scratch_rc[kMaxDevices];
+static std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's scratch pointer (looked up on its first use), or NULL
+// with *rc set when the lookup failed.
+static void *device_scratch(int *rc) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *rc = PML_ERR_HIP;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch[dev] = e == hipSuccess ? ptr : nullptr;
+        g_scratch_rc[dev] = e == hipSuccess ? PML_OK : PML_ERR_HIP;
+    });
+    *rc = g_scratch_rc[dev];
+    return g_scratch[dev];
+}
+
+extern "C" int fp8_fp4_paged_mqa_logits_noalloc(const void *q, const uint8_t *q_scale, int num_rows, int next_n,
+                                                int num_heads, int head_dim, const void *kv_cache, int kv_format,
+                                                int block_kv, int64_t page_stride_bytes, int64_t num_pages,
+                                                const float *weights, const int32_t *context_lens,
+                                                int context_lens_2d, const int32_t *block_table,
+                                                int64_t block_table_ld, int block_table_cols,
+                                                const int32_t *schedule, int num_CUs, const int32_t *indices,
+                                                int max_ctx, float *logits, int64_t logits_ld, void *stream) {
+    if (num_rows > kNoAllocMaxRows || num_CUs > kNoAllocMaxCUs) return PML_ERR_SCRATCH;
+    const size_t need = fp8_fp4_paged_mqa_logits_workspace_size(num_rows < 0 ? 0 : num_rows, num_CUs < 1 ? 1 : num_CUs);
+    if (need > sizeof(scratch)) return PML_ERR_SCRATCH;
+    if (num_rows <= 0) {  // nothing to score (or a bad size): no scratch needed, same checks as the main call
+        return fp8_fp4_paged_mqa_logits(q, q_scale, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format,
+                                        block_kv, page_stride_bytes, num_pages, weights, context_lens,
+                                        context_lens_2d, block_table, block_table_ld, block_table_cols, schedule,
+                                        num_CUs, indices, max_ctx, logits, logits_ld, nullptr, 0, stream);
+    }
+    int rc = PML_OK;
+    void *ptr = device_scratch(&rc);
+    if (!ptr) return rc == PML_OK ? PML_ERR_HIP : rc;
+    return fp8_fp4_paged_mqa_logits(q, q_scale, num_rows, next_n, num_heads, head_dim, kv_cache, kv_format, block_kv,
+                                    page_stride_bytes, num_pages, weights, context_lens, context_lens_2d,
+                                    block_table, block_table_ld, block_table_cols, schedule, num_CUs, indices, max_ctx,
+                                    logits, logits_ld, ptr, sizeof(scratch), stream);
 }
 
 extern "C" int fp8_fp4_paged_mqa_logits_bf16(const void *q, int num_rows, int next_n, int num_heads,

@@ -264,3 +264,19 @@ def test_fused_workspace_size():
     assert f(rows, mc, bkv, k, W) == logits_ws + 3 * r(4 * rows) + r(4 * rows * nb) + r(8 * rows * nb * bkv)
     assert f(rows, mc, 48, k, W) == 0 and f(rows, mc, bkv, 0, W) == 0 and f(-1, mc, bkv, k, W) == 0
     assert _fused(rows=0, topk=None, ws=None) == 0
+
+
+def _noalloc(**kw):
+    a = dict(q=FAKE, qs=None, rows=4, next_n=1, H=64, D=128, kv=FAKE, fmt=0, bkv=64, stride=64 * 132, pages=10,
+             w=FAKE, lens=FAKE, l2d=0, bt=FAKE, bt_ld=8, bt_cols=8, sched=FAKE, cus=4, idx=None,
+             max_ctx=512, out=FAKE, ld=512, stream=None)
+    a.update(kw)
+    return pml.lib().fp8_fp4_paged_mqa_logits_noalloc(*a.values())
+
+
+def test_noalloc_limits_and_validation_without_gpu():
+    # beyond the static scratch: rejected on the host, nothing launched
+    assert _noalloc(rows=4097) == 12 and _noalloc(cus=4097) == 12
+    assert pml.status_string(12) != "unknown status"
+    # the checks of the main call, before any device query
+    assert _noalloc(rows=0) == 0 and _noalloc(rows=-1) == 2 and _noalloc(H=32, rows=0) == 2
