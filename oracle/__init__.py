@@ -61,6 +61,8 @@ def _bind(path) -> ctypes.CDLL:
     L.pml_oracle_topk.restype = None
     L.pml_oracle_topk.argtypes = [u8p, ctypes.c_int, ctypes.c_int64, u8p, u8p, ctypes.c_int, u8p]
     L.pml_oracle_num_threads.restype = ctypes.c_int
+    L.pml_oracle_visible_lengths.restype = None
+    L.pml_oracle_visible_lengths.argtypes = [u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
     L.pml_oracle_dcp_global_id.restype = ctypes.c_int64
     L.pml_oracle_dcp_global_id.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.pml_oracle_dcp_pack.restype = None
@@ -128,6 +130,16 @@ def paged_logits(case, rows=None, col_begin: int = 0, col_end: int | None = None
             kv.shape[1], kv.shape[0], _ptr(lens), int(case.lens_2d), case.next_n,
             _ptr(bt), bt.shape[1] if bt.ndim == 2 else 0, _ptr(rows), len(rows),
             col_begin, col_end, _ptr(out))
+    return out
+
+
+def visible_lengths(case) -> np.ndarray:
+    """Tokens each row of a ``pml_synth.PagedCase`` sees (int64 [rows]): the
+    end of its unmasked span, the bound its top-k takes."""
+    lens = _np(case.context_lens, np.int32)
+    out = np.empty(case.rows, dtype=np.int64)
+    if case.rows:
+        lib().pml_oracle_visible_lengths(_ptr(lens), int(case.lens_2d), case.next_n, case.rows, _ptr(out))
     return out
 
 

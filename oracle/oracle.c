@@ -114,6 +114,14 @@ static int64_t visible(const int32_t *lens, int lens_2d, int next_n, int r)
     return v < 0 ? 0 : v;
 }
 
+/* The visible length of every row [0, rows), by the rule above: the row's
+ * last unmasked column plus one, so the bound a top-k over the row takes. */
+void pml_oracle_visible_lengths(const int32_t *lens, int lens_2d, int next_n, int rows, int64_t *out)
+{
+    for (int r = 0; r < rows; ++r)
+        out[r] = visible(lens, lens_2d, next_n, r);
+}
+
 /* Element d of head h of one query row. fp8 q (qsrow NULL): the e4m3 code.
  * fp4 q (the indexer's FP4 path passes q as a (values, scales) pair,
  * sparse_attn_indexer page, forward_cuda; the layout read here is the

@@ -155,3 +155,60 @@ def exactify_fp8_case(case: syn.PagedCase, seed: int) -> None:
 
 def oracle_rows(case, rows) -> np.ndarray:
     return oracle.paged_logits(case, rows=np.asarray(rows))
+
+
+_NAMED = {
+    "tiny_decode": syn.config_tiny_decode,
+    "uniform_decode": syn.config_uniform_decode,
+    "varlen_fp8": syn.config_varlen_fp8,
+    "varlen_fp4": syn.config_varlen_fp4,
+    "varlen_fp4_q4": lambda: syn.config_varlen_fp4(q_fp4=True),
+}
+_CASES = {}
+_FULL = {}
+
+
+def named_case(name: str):
+    """A named workload, generated once per test session (callers must not modify it)."""
+    if name not in _CASES:
+        _CASES[name] = _NAMED[name]()
+    return _CASES[name]
+
+
+def oracle_full(name: str) -> np.ndarray:
+    """fp64 oracle logits of every row of a named workload, computed once per session."""
+    if name not in _FULL:
+        _FULL[name] = oracle.paged_logits(named_case(name))
+    return _FULL[name]
+
+
+def check_whole_output(gpu: np.ndarray, case) -> np.ndarray:
+    """-inf exactly past each row's visible length (the oracle's rule), finite before it."""
+    vis = oracle.visible_lengths(case)
+    cols = np.arange(gpu.shape[1])[None, :]
+    assert np.all(np.isneginf(gpu[cols >= vis[:, None]]))
+    assert np.all(np.isfinite(gpu[cols < vis[:, None]]))
+    return vis
+
+
+def topk_acceptance(sel: np.ndarray, ref: np.ndarray, vis, k: int, wsum, rel: float = REL, abs_: float = ABS,
+                    factor: float = 1.0) -> None:
+    """The top-k acceptance against fp64 scores, row by row: every selected
+    index scores at least the oracle's k-th score minus tau, every score above
+    the k-th plus tau is selected (tau the per-logit tolerance at the k-th
+    score, times factor), and the selection has min(k, vis) distinct valid
+    indices followed by -1."""
+    for i in range(ref.shape[0]):
+        n = int(vis[i])
+        m = min(k, n)
+        s = sel[i]
+        assert np.all(s[m:] == -1), i
+        got = s[:m]
+        assert np.all((got >= 0) & (got < n)) and len(np.unique(got)) == m, i
+        if m == 0:
+            continue
+        sc = ref[i, :n]
+        tk = np.sort(sc)[::-1][m - 1]
+        tau = factor * (rel * abs(tk) + abs_ * wsum[i])
+        assert np.all(sc[got] >= tk - tau), i
+        assert np.all(np.isin(np.nonzero(sc > tk + tau)[0], got)), i

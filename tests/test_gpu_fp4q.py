@@ -1,6 +1,6 @@
 """Paged logits with fp4 q (e2m1 values, per-32 e8m0 scales) over MXFP4 keys on the GPU.
 
-* Small varlen / uniform cases and the 64K MXFP4 decode config (sampled rows)
+* Small varlen / uniform cases and the 64K MXFP4 decode config (every row)
   within the logits tolerance of the oracle.
 * Exactly representable inputs (power-of-two scales, w in (1/8)Z): bit for bit.
 * The same real q given as fp8 codes and as fp4 (values, scales) scores the
@@ -72,13 +72,9 @@ def test_fp4q_equals_fp8q():
     np.testing.assert_array_equal(G.run_paged(case), G.run_paged(c8))
 
 
-def test_fp4q_config_sampled():
-    case = syn.config_varlen_fp4(q_fp4=True)
-    G.banner(f"fp4 q varlen MXFP4 64K rows={case.rows}")
+def test_fp4q_config_full():
+    case = G.named_case("varlen_fp4_q4")
+    G.banner(f"fp4 q varlen MXFP4 64K: all {case.rows} rows")
     gpu = G.run_paged(case)
-    vis = syn.vis_per_row(case)
-    cols = np.arange(case.max_ctx)[None, :]
-    assert np.all(np.isneginf(gpu[cols >= vis[:, None]]))
-    assert np.all(np.isfinite(gpu[cols < vis[:, None]]))
-    rows = np.sort(np.random.default_rng(997).choice(case.rows, 8, replace=False))
-    G.assert_logits_close(gpu[rows], G.oracle_rows(case, rows), case.weights[rows], "fp4q config")
+    G.check_whole_output(gpu, case)
+    G.assert_logits_close(gpu, G.oracle_full("varlen_fp4_q4"), case.weights, "fp4q config")

@@ -46,7 +46,7 @@ def _check(case, k, t=None):
     np.testing.assert_array_equal(L.view(np.uint32), ref_logits.cpu().numpy()[:, : case.max_ctx].view(np.uint32))
     got = topk.cpu().numpy()
     np.testing.assert_array_equal(got, ref_topk.cpu().numpy())
-    vis = np.minimum(syn.vis_per_row(case), case.max_ctx)
+    vis = np.minimum(oracle.visible_lengths(case), case.max_ctx)
     np.testing.assert_array_equal(got, oracle.topk(L.astype(np.float64), vis, k))
     done = _ws_done(ws, case.rows, pml.schedule_workers(sched))
     print(f"[gpu-check] fused top-k k={k}: {int(done.sum())} of {case.rows} rows from candidates", flush=True)
@@ -107,7 +107,7 @@ def test_fused_uniform_config(k):
 
 
 def test_fused_varlen_120k_config():
-    case = syn.config_varlen_fp8()
+    case = G.named_case("varlen_fp8")
     G.banner(f"fused varlen 120K rows={case.rows}")
     done, vis = _check(case, case.topk)
     _count(done, vis, case.topk)
@@ -115,7 +115,7 @@ def test_fused_varlen_120k_config():
 
 
 def test_fused_mxfp4_config():
-    case = syn.config_varlen_fp4()
+    case = G.named_case("varlen_fp4")
     G.banner(f"fused MXFP4 64K rows={case.rows}")
     _count(*_check(case, case.topk), case.topk)
 

@@ -2,8 +2,8 @@
 
 Cases span several key blocks per row, ragged last blocks, groups longer than
 one row-piece, uniform next_n > 1 with 1-D and 2-D lengths, fp8 and MXFP4
-caches at block_kv 32 and 64, and the five named workloads (the two small ones
-in full, the large ones on sampled rows plus whole-output properties).
+caches at block_kv 32 and 64, and the four paged named workloads, every row
+of each compared element by element.
 """
 import numpy as np
 import pytest
@@ -277,26 +277,18 @@ def test_uniform_decode_config_full():
     _check_case(case)
 
 
-def _sampled(case, n_rows, seed):
+def _full(name):
+    """Every row of a named workload against the oracle, element by element."""
+    case = G.named_case(name)
+    G.banner(f"{name}: all {case.rows} rows ({syn.scored_pairs(case)} pairs)")
     gpu = G.run_paged(case)
-    vis = syn.vis_per_row(case)
-    # whole-output properties
-    cols = np.arange(case.max_ctx)[None, :]
-    assert np.all(np.isneginf(gpu[cols >= vis[:, None]]))
-    assert np.all(np.isfinite(gpu[cols < vis[:, None]]))
-    rows = np.sort(np.random.default_rng(seed).choice(case.rows, n_rows, replace=False))
-    ref = G.oracle_rows(case, rows)
-    G.assert_logits_close(gpu[rows], ref, case.weights[rows])
-    return gpu
+    G.check_whole_output(gpu, case)
+    G.assert_logits_close(gpu, G.oracle_full(name), case.weights, name)
 
 
-def test_varlen_fp8_config_sampled():
-    case = syn.config_varlen_fp8()
-    G.banner(f"varlen fp8 120K rows={case.rows}")
-    _sampled(case, 6, 1)
+def test_varlen_fp8_config_full():
+    _full("varlen_fp8")
 
 
-def test_varlen_fp4_config_sampled():
-    case = syn.config_varlen_fp4()
-    G.banner(f"varlen fp4 rows={case.rows}")
-    _sampled(case, 10, 2)
+def test_varlen_fp4_config_full():
+    _full("varlen_fp4")

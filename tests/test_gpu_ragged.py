@@ -70,7 +70,7 @@ def test_decode_rows_equal_prefill_rows():
     keys gathered contiguously with ks = 0, ke = vis (bitwise: same tiles)."""
     case = syn.make_paged_case([1500, 700], [3, 2], seed=730, max_ctx=1536)
     dec = G.run_paged(case)
-    vis = syn.vis_per_row(case)
+    vis = oracle.visible_lengths(case)
     kv = case.kv_cache.numpy()
     B, D = case.block_kv, case.D
     bt = case.block_table.numpy()[0]
@@ -90,9 +90,20 @@ def test_decode_rows_equal_prefill_rows():
         np.testing.assert_array_equal(pre, dec[r, :n])
 
 
-def test_ragged_prefill_config_sampled():
+def _c5_rows(case, n_random: int, seed: int) -> np.ndarray:
+    """The first two and last two rows of every sequence plus n_random others."""
+    starts = np.unique(case.ks.numpy())
+    ends = np.append(starts[1:], case.M)
+    edge = np.concatenate([[a, a + 1, b - 2, b - 1] for a, b in zip(starts, ends)])
+    rest = np.setdiff1d(np.arange(case.M), edge)
+    pick = np.random.default_rng(seed).choice(rest, n_random, replace=False)
+    return np.sort(np.concatenate([edge, pick])).astype(np.int64)
+
+
+def test_ragged_prefill_config_rows():
     case = syn.config_ragged_prefill()
-    G.banner(f"ragged prefill 4x8192 M={case.M}")
+    rows = _c5_rows(case, 512, 3)
+    G.banner(f"ragged prefill 4x8192 M={case.M}: {len(rows)} rows against the oracle")
     t = _upload(case)
     out = run_ragged(case, t)[:, : case.N]
     # whole-output properties on the device: -inf exactly outside [ks, ke), finite inside
@@ -102,8 +113,33 @@ def test_ragged_prefill_config_sampled():
         inside = (cols[None, :] >= t["ks"][r0: r0 + 4096, None]) & (cols[None, :] < t["ke"][r0: r0 + 4096, None])
         assert bool(torch.isneginf(blk[~inside]).all())
         assert bool(torch.isfinite(blk[inside]).all())
-    rows = np.sort(np.random.default_rng(3).choice(case.M, 24, replace=False))
-    rows[:4] = [0, 8191, 8192, case.M - 1]
-    rows = np.sort(rows)
     ref = oracle.ragged_logits(case, rows=rows)
     G.assert_logits_close(out[torch.from_numpy(rows).to(G.dev())].cpu().numpy(), ref, case.weights[rows])
+
+
+def test_ragged_prefill_config_topk_full():
+    """top-k 2048 of all 32768 prefill rows on the GPU logits: bit for bit with
+    the oracle's top-k over the same values, and the acceptance against the
+    fp64 scores on the sampled rows (first and last rows of each sequence)."""
+    case = syn.config_ragged_prefill()
+    G.banner(f"ragged prefill top-k at full size M={case.M} k={case.topk}")
+    t = _upload(case)
+    out = run_ragged(case, t)
+    got = pml.top_k_per_row(out, t["ke"], case.topk, ks=t["ks"], max_width=case.N)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ks, ke = case.ks.numpy(), case.ke.numpy()
+    for r0 in range(0, case.M, 2048):
+        r1 = min(r0 + 2048, case.M)
+        L = out[r0:r1, : case.N].cpu().numpy()
+        np.testing.assert_array_equal(got[r0:r1], oracle.topk(L, ke[r0:r1], case.topk, ks=ks[r0:r1]),
+                                      err_msg=f"rows {r0}..{r1}")
+    rows = _c5_rows(case, 64, 5)
+    ref = oracle.ragged_logits(case, rows=rows)
+    # scores relative to each row's start, as the selection's positions are
+    rel = np.full((len(rows), case.N), -np.inf)
+    for i, r in enumerate(rows):
+        n = max(0, int(ke[r]) - int(ks[r]))
+        rel[i, :n] = ref[i, ks[r]: ks[r] + n]
+    G.topk_acceptance(got[rows], rel, np.maximum(ke[rows] - ks[rows], 0), case.topk,
+                      np.abs(case.weights[rows].double().numpy()).sum(1))

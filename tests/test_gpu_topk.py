@@ -176,26 +176,24 @@ def _acceptance(gpu: np.ndarray, ref: np.ndarray, lo: np.ndarray, hi: np.ndarray
         assert np.all(np.isin(must, sel))
 
 
-def test_decode_configs_topk():
-    for case, nrows in ((syn.config_tiny_decode(), None), (syn.config_varlen_fp8(), 5)):
-        G.banner(f"top-k decode rows={case.rows} k={case.topk}")
-        t = G.upload(case)
-        sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, None, indices=t["indices"])
-        logits = pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx,
-                                              t["indices"], kv_format=case.kv_format, block_kv=case.block_kv)
-        got = pml.top_k_per_row(logits, t["lens"], case.topk, max_width=case.max_ctx)
-        torch.cuda.synchronize()
-        got = got.cpu().numpy()
-        L = logits.cpu().numpy()[:, : case.max_ctx]
-        vis = syn.vis_per_row(case)
-        # shared input: bit-exact
-        want = oracle.topk(L.astype(np.float64), vis, case.topk)
-        np.testing.assert_array_equal(got, want)
-        # against the fp64 oracle logits on sampled rows
-        rows = np.arange(case.rows) if nrows is None else np.sort(np.random.default_rng(5).choice(case.rows, nrows, replace=False))
-        ref = G.oracle_rows(case, rows)
-        _acceptance(got[rows], ref, np.zeros(len(rows), dtype=np.int64), vis[rows], case.topk,
-                    np.abs(case.weights[rows].double().numpy()).sum(1))
+@pytest.mark.parametrize("name", ["tiny_decode", "varlen_fp8"])
+def test_decode_configs_topk(name):
+    case = G.named_case(name)
+    G.banner(f"top-k decode {name} rows={case.rows} k={case.topk}")
+    t = G.upload(case)
+    sched = pml.paged_mqa_logits_metadata(t["lens"], case.block_kv, None, indices=t["indices"])
+    logits = pml.fp8_fp4_paged_mqa_logits(t["q"], t["kv"], t["w"], t["lens"], t["bt"], sched, case.max_ctx,
+                                          t["indices"], kv_format=case.kv_format, block_kv=case.block_kv)
+    got = pml.top_k_per_row(logits, t["lens"], case.topk, max_width=case.max_ctx)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    L = logits.cpu().numpy()[:, : case.max_ctx]
+    vis = oracle.visible_lengths(case)
+    # shared input: bit-exact
+    np.testing.assert_array_equal(got, oracle.topk(L.astype(np.float64), vis, case.topk))
+    # every row against the fp64 oracle logits
+    ref = G.oracle_full(name)
+    G.topk_acceptance(got, ref, vis, case.topk, np.abs(case.weights.double().numpy()).sum(1))
 
 
 def test_prefill_topk_sampled():

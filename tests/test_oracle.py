@@ -9,6 +9,7 @@
 import json
 import math
 import os
+import types
 
 import numpy as np
 import pytest
@@ -130,7 +131,7 @@ def test_golden_fp8_paged_logits_and_topk():
     got = oracle.paged_logits(case)
     assert np.array_equal(got, want)
     assert np.array_equal(brute.paged_logits(case), want)
-    vis = syn.vis_per_row(case)
+    vis = oracle.visible_lengths(case)
     for key in ("expected_topk", "expected_topk_k3"):
         e = g["fp8_case"][key]
         assert oracle.topk(got, vis, e["k"]).tolist() == e["rows"]
@@ -167,7 +168,7 @@ def _dequant_torch(case):
 
 def _tokens_of_row(case, r):
     pages = _dequant_torch(case)
-    vis = int(syn.vis_per_row(case)[r])
+    vis = int(oracle.visible_lengths(case)[r])
     bt = case.block_table.numpy()[r // case.next_n]
     return np.concatenate([pages[bt[b]] for b in range(-(-vis // case.block_kv))])[:vis]
 
@@ -266,7 +267,7 @@ def test_decode_rows_equal_prefill_rows():
     """Decode rows == the same rows scored as non-paged rows over the gathered keys (ks = 0, ke = vis)."""
     case = syn.make_paged_case([150, 97], [3, 2], seed=41, H=4, max_ctx=160)
     dec = oracle.paged_logits(case)
-    vis = syn.vis_per_row(case)
+    vis = oracle.visible_lengths(case)
     for r in range(case.rows):
         bt = case.block_table.numpy()[r]
         kv = case.kv_cache.numpy()
@@ -311,8 +312,33 @@ def test_masked_cells_are_neg_inf_and_empty_rows():
     out = oracle.paged_logits(case)
     assert np.all(np.isneginf(out[0, 70:])) and np.all(np.isfinite(out[0, :70]))
     assert np.all(np.isneginf(out[1]))
-    tk = oracle.topk(out, syn.vis_per_row(case), 4)
+    tk = oracle.topk(out, oracle.visible_lengths(case), 4)
     assert tk[1].tolist() == [-1] * 4
+
+
+def test_visible_lengths_hand_worked():
+    """The row-length rule worked by hand: a 1-D length per batch entry with
+    next_n 3 gives row j of entry b len[b] - 3 + j + 1 (never below 0); 2-D
+    lengths and next_n 1 give each row its own length."""
+    def vis(lens, next_n, lens_2d, rows):
+        c = types.SimpleNamespace(context_lens=torch.tensor(lens, dtype=torch.int32), next_n=next_n,
+                                  lens_2d=lens_2d, rows=rows)
+        return oracle.visible_lengths(c).tolist()
+    assert vis([10, 3, 1], 3, False, 9) == [8, 9, 10, 1, 2, 3, 0, 0, 1]
+    assert vis([[4, 5, 6], [0, -2, 7]], 3, True, 6) == [4, 5, 6, 0, 0, 7]
+    assert vis([5, 0, 9], 1, False, 3) == [5, 0, 9]
+
+
+def test_visible_lengths_end_the_unmasked_span():
+    """On generated cases the rule's bound is where the oracle's own scores turn -inf."""
+    for case in (syn.make_paged_case([300, 5, 130], [3, 1, 2], seed=41, max_ctx=320),
+                 syn.make_paged_case([100, 70, 3], [3, 3, 3], seed=42, varlen=False, next_n=3, H=4, max_ctx=128),
+                 syn.make_paged_case([100, 70, 3], [3, 3, 3], seed=43, varlen=False, next_n=3, lens_2d=True, H=4,
+                                     max_ctx=128)):
+        out = oracle.paged_logits(case)
+        vis = oracle.visible_lengths(case)
+        cols = np.arange(case.max_ctx)[None, :]
+        assert np.array_equal(np.isneginf(out), cols >= vis[:, None])
 
 
 def test_topk_matches_numpy_and_torch():
