@@ -12,8 +12,11 @@ Inputs are resident in HBM before the timed region. Steps rotate over
 independent copies of the key cache (together larger than the 256 MB last-level
 cache), so each step streams its keys from HBM. HIP events on the launch stream
 time every kernel inside the timed region; the JSON line reports the whole-step
-rate plus the logits kernel against the HBM roofline, and a bounded sample of
-the same workload scored by the CPU oracle.
+rate (HIP-graph replays), per-kernel mean / median / min (eager launches), the
+logits call against the HBM roofline, the same rows scored without request
+grouping (indices = arange(rows), each row reading its keys alone), and the CPU
+oracle timed on a bounded sample of this workload and on each other workload,
+with the host's core count and CPU model.
 
   python bench.py [--steps K] [--warmup W] [--all]
 
@@ -51,7 +54,7 @@ def measured_traffic():
     """HBM bytes per launch of the fp8 decode-logits kernel on this workload, from the
     committed FETCH_SIZE + WRITE_SIZE summary; None when the kernel sources have changed
     since the counters were taken (or there is no summary)."""
-    from paged_mqa_logits_amd import profsum
+    import profsum
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -259,10 +262,23 @@ def run_graphs(graphs: list, steps: int, warmup: int) -> float:
     return time.perf_counter() - t0
 
 
+def _host() -> dict:
+    """Cores this process may run on, and the host CPU model."""
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
 def cpu_baseline(case: syn.PagedCase, target_s: float) -> dict:
     """The oracle (as it stands) on a bounded sample of rows of the same workload."""
     import oracle
-    vis = syn.vis_per_row(case)
+    vis = oracle.visible_lengths(case)
     rng = np.random.default_rng(0)
     order = rng.permutation(case.rows)
     # calibrate on one row, then take rows until the estimate reaches target_s
@@ -283,6 +299,86 @@ def cpu_baseline(case: syn.PagedCase, target_s: float) -> dict:
             "kind": "oracle",
             "sample": f"{len(rows)} of {case.rows} rows ({pairs} scored pairs) of the same workload, "
                       f"fp64 logits + top-k, {dt:.1f} s"}
+
+
+def _oracle_paged(case, rows=None) -> tuple[float, int]:
+    """Seconds for the oracle's logits + top-k of `rows` (all by default), and the pairs scored."""
+    import oracle
+    vis = oracle.visible_lengths(case)
+    rows = np.arange(case.rows) if rows is None else np.asarray(rows)
+    t0 = time.perf_counter()
+    sc = oracle.paged_logits(case, rows=rows)
+    oracle.topk(sc, vis[rows], case.topk)
+    return time.perf_counter() - t0, int(vis[rows].sum())
+
+
+def cpu_baseline_configs() -> dict:
+    """The oracle on each of the other workloads (whole, or a stated sample of it):
+    the tiny decode as the median of 5 runs plus one run on a single thread, the
+    uniform decode whole, 8 of the 64 MXFP4 requests (generated with the same
+    distributions), and 1024 of the 32768 ragged prefill rows."""
+    import oracle
+    out = {}
+    nthr = oracle.num_threads()
+    c1 = syn.config_tiny_decode()
+    ts = []
+    for _ in range(5):
+        dt, pairs = _oracle_paged(c1)
+        ts.append(dt)
+    oracle.set_num_threads(1)
+    try:
+        dt1, _ = _oracle_paged(c1)
+    finally:
+        oracle.set_num_threads(nthr)
+    med = float(np.median(ts))
+    out["tiny_decode"] = {"value": round(pairs / med / 1e3, 3), "unit": "K tokens/s", "cores": nthr,
+                          "seconds_median_of_5": round(med, 4), "seconds_1_thread": round(dt1, 4),
+                          "value_1_thread": round(pairs / dt1 / 1e3, 3), "sample": f"all {c1.rows} rows"}
+    c2 = syn.config_uniform_decode()
+    dt, pairs = _oracle_paged(c2)
+    out["uniform_decode_32k"] = {"value": round(pairs / dt / 1e3, 3), "unit": "K tokens/s", "cores": nthr,
+                                 "seconds": round(dt, 3), "sample": f"all {c2.rows} rows"}
+    c4 = syn.config_varlen_fp4(R=8)
+    dt, pairs = _oracle_paged(c4)
+    out["varlen_mxfp4_64k"] = {"value": round(pairs / dt / 1e3, 3), "unit": "K tokens/s", "cores": nthr,
+                               "seconds": round(dt, 3),
+                               "sample": f"8 of 64 requests ({c4.rows} rows) drawn from the same distributions"}
+    c5 = syn.config_ragged_prefill()
+    rows = np.sort(np.random.default_rng(0).choice(c5.M, 1024, replace=False))
+    ks, ke = c5.ks.numpy(), c5.ke.numpy()
+    t0 = time.perf_counter()
+    sc = oracle.ragged_logits(c5, rows=rows)
+    oracle.topk(sc, ke[rows], c5.topk, ks=ks[rows])
+    dt = time.perf_counter() - t0
+    pairs = int(np.maximum(ke[rows] - ks[rows], 0).sum())
+    out["ragged_prefill_4x8192"] = {"value": round(pairs / dt / 1e3, 3), "unit": "K tokens/s", "cores": nthr,
+                                    "seconds": round(dt, 3), "sample": f"1024 of {c5.M} rows"}
+    return out
+
+
+def grouping_comparison(case: syn.PagedCase, steps: int, warmup: int, copies: int) -> dict:
+    """The same rows scored with and without the request-id grouping: with
+    indices = arange(rows) every row is its own piece and reads its keys alone.
+    Schedule + logits only, eager launches with HIP events."""
+    out = {}
+    for name, idx in (("grouped", case.indices), ("arange", torch.arange(case.rows, dtype=torch.int32))):
+        c = syn.PagedCase(**{**case.__dict__, "indices": idx})
+        b = PagedBench(c, copies)
+        _, per = run_timed(b, steps, warmup)
+        t = per[:, 1]
+        # keys read: each request's tokens once when grouped, each row's own when not
+        tokens = int(syn.vis_per_row(c).sum()) if name == "arange" else b.req_tokens
+        kbytes = tokens * BYTES_PER_TOKEN[c.kv_format]
+        out[name] = {"ms_logits_mean": round(float(t.mean()), 4), "ms_logits_median": round(float(np.median(t)), 4),
+                     "ms_logits_min": round(float(t.min()), 4), "key_bytes_read": kbytes,
+                     "hbm_GBs": round(kbytes / (float(t.mean()) * 1e-3) / 1e9, 1)}
+        del b
+    out["speedup_of_grouping"] = round(out["arange"]["ms_logits_mean"] / out["grouped"]["ms_logits_mean"], 3)
+    return out
+
+
+def stats(x: np.ndarray) -> dict:
+    return {"mean": round(float(x.mean()), 4), "median": round(float(np.median(x)), 4), "min": round(float(x.min()), 4)}
 
 
 def describe(case: syn.PagedCase) -> dict:
@@ -350,10 +446,13 @@ def main():
                    "kv_copies_rotated": len(b.kv)},
         "breakdown_ms": {"schedule": round(s["ms_schedule"], 4), "logits": round(s["ms_logits"], 4),
                          "topk": round(s["ms_topk"], 4)},
+        "per_step_ms": {"schedule": stats(per[:, 0]), "logits": stats(per[:, 1]), "topk": stats(per[:, 2]),
+                        "step_eager": stats(per.sum(axis=1))},
         "logits_mfma_frac": round(s["logits_mfma_frac"], 4),
         "roofline": {"bound": "hbm", "achieved": round(s["logits_hbm_GBs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(s["logits_hbm_frac"], 4), "traffic": measured_traffic(),
-                     "kernel": "paged_logits_kernel<fp8, block_kv 64>",
+                     "kernel": "fp8_fp4_paged_mqa_logits (u-piece prep + paged_logits_kernel<fp8, block_kv 64>), "
+                               "HIP events around the call",
                      "bytes_per_launch": b.req_tokens * BYTES_PER_TOKEN[case.kv_format]},
     }
     if args.copy_calibration > 0:
@@ -365,11 +464,17 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] calibration copy of {args.copy_calibration} bytes done", file=sys.stderr, flush=True)
         del src, dst
+    del b
+    torch.cuda.empty_cache()
+    print("[bench] the same rows without request grouping (indices = arange)", file=sys.stderr, flush=True)
+    line["varlen_grouping"] = grouping_comparison(case, args.steps, args.warmup, args.copies)
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
-    del b
-    torch.cuda.empty_cache()
+        line["cpu_baseline"].update(_host())
+        print("[bench] timing the CPU oracle on the other workloads", file=sys.stderr, flush=True)
+        line["cpu_baseline"]["other_workloads"] = cpu_baseline_configs()
 
     if args.all:
         others = [("uniform_decode_fp8_32k", lambda: PagedBench(syn.config_uniform_decode(), args.copies * 2)),

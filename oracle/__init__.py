@@ -61,6 +61,8 @@ def _bind(path) -> ctypes.CDLL:
     L.pml_oracle_topk.restype = None
     L.pml_oracle_topk.argtypes = [u8p, ctypes.c_int, ctypes.c_int64, u8p, u8p, ctypes.c_int, u8p]
     L.pml_oracle_num_threads.restype = ctypes.c_int
+    L.pml_oracle_set_num_threads.restype = None
+    L.pml_oracle_set_num_threads.argtypes = [ctypes.c_int]
     L.pml_oracle_visible_lengths.restype = None
     L.pml_oracle_visible_lengths.argtypes = [u8p, ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p]
     L.pml_oracle_dcp_global_id.restype = ctypes.c_int64
@@ -228,3 +230,7 @@ def bf16_to_f32(bits) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().pml_oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().pml_oracle_set_num_threads(int(n))

@@ -311,6 +311,17 @@ int pml_oracle_num_threads(void)
 #endif
 }
 
+/* Threads of the parallel loops above from now on (n >= 1). */
+void pml_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---- exact merge of per-shard top-k candidates ---------------------------
  *
  * Decode context parallelism shards each request's key tokens over `world`

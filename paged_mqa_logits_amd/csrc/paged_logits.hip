@@ -127,7 +127,8 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
             }
             float v = (sr + M[G]) * scale;
             if (!okc) v = __builtin_nanf("");
-            if (s >= vis) v = -__builtin_inff();
+            if (col0 + BKV > vis)  // (wave-uniform: only a row's last block is masked)
+                if (s >= vis) v = -__builtin_inff();
             if (out_lane<BKV>(lane)) lds_st<float>(&sl.v[i][tok], v);
             if constexpr (CAND) {
                 // candidates (logit at or above the row's threshold) to the block's
@@ -155,16 +156,18 @@ constexpr int kPThreads = kPW * kWave;
 constexpr int kDepth = 1;          // key blocks in flight per wave while one is scored
 constexpr int kBufs = kDepth + 1;  // key-block buffers per wave
 
-// LDS of a logits workgroup.
+// LDS of a logits workgroup. (q last: the small arrays read per row sit
+// below 64 KB, within reach of an LDS instruction's immediate offset from one
+// base address.)
 template <int BKV>
 struct PagedShared {
-    uint8_t q[kGMax * kQBytes];
     float w[kGMax * PML_HEADS];
     uint8_t u[kGMax * kUBytes];
     uint8_t us[kGMax * kUScales];
-    WaveSlot<BKV> slot[kPW];
     int vis[kGMax];
     float th[kGMax];
+    WaveSlot<BKV> slot[kPW];
+    uint8_t q[kGMax * kQBytes];
 };
 
 // One piece (the whole workgroup): stage its rows, then every wave scores its

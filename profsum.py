@@ -7,10 +7,10 @@ HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
 same counter reads for a device-to-device copy of known size
 (``bench.py --copy-calibration`` issues one).
 
-  python -m paged_mqa_logits_amd.profsum stats  <kernel_stats.csv>
-  python -m paged_mqa_logits_amd.profsum trace  <kernel_trace.csv>
-  python -m paged_mqa_logits_amd.profsum pmc    <counter_collection.csv> <counter> <copy_bytes>
-  python -m paged_mqa_logits_amd.profsum digest
+  python profsum.py stats  <kernel_stats.csv>
+  python profsum.py trace  <kernel_trace.csv>
+  python profsum.py pmc    <counter_collection.csv> <counter> <copy_bytes>
+  python profsum.py digest
 
 ``trace`` groups the dispatches of a kernel trace by kernel and launch
 shape (grid and workgroup size), so one run over several workloads that share
@@ -27,7 +27,7 @@ import sys
 from collections import defaultdict
 from pathlib import Path
 
-CSRC = Path(__file__).resolve().parent / "csrc"
+CSRC = Path(__file__).resolve().parent / "paged_mqa_logits_amd" / "csrc"
 LOGITS_SOURCES = ("pml_device.h", "rows.h", "logits_core.h", "paged_logits.hip")
 COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
 
