@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=3, help="key-cache copies rotated over the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grouping", action="store_true",
+                    help="skip the run without request grouping (profiles of the headline step alone)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -81,6 +83,9 @@ def parse():
                          "reference for the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--all", action="store_true",
                     help="also time the other workloads (one JSON line each on stderr)")
+    ap.add_argument("--workload", choices=sorted(OTHERS), default=None,
+                    help="time only this other workload (its JSON line on stdout; for profiling one "
+                         "workload at a time)")
     return ap.parse_args()
 
 
@@ -401,6 +406,108 @@ def paged_summary(name: str, b: PagedBench, wall: float, per: np.ndarray, steps:
             "logits_out_bytes": c.rows * c.max_ctx * 4, **describe(c)}
 
 
+def _paged_other(mk, copies_mult: int = 2):
+    def run(args):
+        ob = PagedBench(mk(), args.copies * copies_mult)
+        w2, p2 = run_timed(ob, args.steps, args.warmup)
+        if not args.no_graph:
+            w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
+        return ob, w2, p2
+    return run
+
+
+def run_uniform(args):
+    ob, w2, p2 = _paged_other(syn.config_uniform_decode)(args)
+    return paged_summary("uniform_decode_fp8_32k", ob, w2, p2, args.steps)
+
+
+def run_mxfp4(args):
+    ob, w2, p2 = _paged_other(syn.config_varlen_fp4)(args)
+    return paged_summary("varlen_spec_decode_mxfp4_64k", ob, w2, p2, args.steps)
+
+
+def run_mxfp4_fp4q(args):
+    ob, w2, p2 = _paged_other(lambda: syn.config_varlen_fp4(q_fp4=True))(args)
+    return paged_summary("varlen_spec_decode_mxfp4_64k_fp4q", ob, w2, p2, args.steps)
+
+
+def run_tiny(args):
+    ob, w2, p2 = _paged_other(syn.config_tiny_decode, 0)(args)
+    return paged_summary("tiny_decode_fp8", ob, w2, p2, args.steps)
+
+
+def run_bf16(args):
+    ob = PagedBench(syn.config_varlen_fp8(), args.copies, bf16=True)
+    w2, p2 = run_timed(ob, args.steps, args.warmup)
+    if not args.no_graph:
+        w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
+    c = ob.case
+    t_log = float(p2[:, 1].mean()) * 1e-3
+    kbytes = ob.req_tokens * BYTES_PER_TOKEN[c.kv_format]
+    return {"workload": "varlen_spec_decode_fp8_120k_bf16_logits", "ms_per_step": w2 / args.steps * 1e3,
+            "ms_schedule": float(p2[:, 0].mean()), "ms_logits": t_log * 1e3,
+            "ms_upcast": float(p2[:, 2].mean()), "ms_topk": float(p2[:, 3].mean()),
+            "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
+            "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
+            "logits_out_bytes": c.rows * c.max_ctx * 2}
+
+
+def run_fused(args):
+    ob = PagedBench(syn.config_varlen_fp8(), args.copies, fused=True)
+    w2, p2 = run_timed(ob, args.steps, args.warmup)
+    if not args.no_graph:
+        w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
+    return {"workload": "varlen_spec_decode_fp8_120k_fused_logits_topk",
+            "ms_per_step": w2 / args.steps * 1e3, "ms_schedule": float(p2[:, 0].mean()),
+            "ms_fused_logits_topk": float(p2[:, 1].mean()),
+            "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3}
+
+
+def run_dcp(args):
+    db = DcpBench(syn.config_varlen_fp8())
+    w2, p2 = run_timed(db, args.steps, args.warmup)
+    t_m = float(p2[:, 2].mean()) * 1e-3
+    mbytes = db.world * db.rows * db.k * 8 + db.rows * db.k * 4
+    return {"workload": "dcp_topk_merge_8ranks_varlen120k", "rows": db.rows, "k": db.k,
+            "world": db.world, "local_width": db.local_w,
+            "ms_local_topk": float(p2[:, 0].mean()), "ms_pack": float(p2[:, 1].mean()),
+            "ms_merge": t_m * 1e3, "merge_bytes": mbytes,
+            "merge_GBs": mbytes / t_m / 1e9, "merge_hbm_frac": mbytes / t_m / 1e9 / PEAK_HBM_GBS}
+
+
+def run_ragged(args):
+    rb = RaggedBench(syn.config_ragged_prefill())
+    n = max(3, args.steps // 4)
+    w2, p2 = run_timed(rb, n, 2)
+    t_log = float(p2[:, 1].mean()) * 1e-3
+    return {"workload": "ragged_prefill_4x8192", "ms_per_step": w2 / n * 1e3,
+            "ms_logits": t_log * 1e3, "ms_topk": float(p2[:, 2].mean()),
+            "ms_logits_median": float(np.median(p2[:, 1])), "ms_logits_min": float(p2[:, 1].min()),
+            "scored_Ktok_s": rb.pairs / (w2 / n) / 1e3,
+            "logits_mfma_frac": rb.pairs * 2 * 64 * 128 / t_log / 1e12 / PEAK_FP8_TFLOPS,
+            "logits_write_GBs": rb.case.M * rb.case.N * 4 / t_log / 1e9}
+
+
+def calibration_copy(nbytes: int) -> None:
+    """One device-to-device copy of nbytes (a known-size reference for the byte counters)."""
+    if nbytes <= 0:
+        return
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+    del src, dst
+
+
+OTHERS = {"uniform_decode_fp8_32k": run_uniform, "varlen_spec_decode_mxfp4_64k": run_mxfp4,
+          "varlen_spec_decode_mxfp4_64k_fp4q": run_mxfp4_fp4q, "tiny_decode_fp8": run_tiny,
+          "varlen_spec_decode_fp8_120k_bf16": run_bf16, "varlen_spec_decode_fp8_120k_fused": run_fused,
+          "dcp_merge_8ranks": run_dcp, "ragged_prefill_4x8192": run_ragged}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -411,6 +518,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     pml.lib()  # fail loudly before generating data if the library is missing
+    if args.workload:
+        print(f"[bench] {args.workload}", file=sys.stderr, flush=True)
+        res = OTHERS[args.workload](args)
+        calibration_copy(args.copy_calibration)
+        print(json.dumps(res), flush=True)
+        return
 
     print("[bench] generating the varlen speculative-decode workload", file=sys.stderr, flush=True)
     case = syn.config_varlen_fp8()
@@ -455,20 +568,13 @@ def main():
                                "HIP events around the call",
                      "bytes_per_launch": b.req_tokens * BYTES_PER_TOKEN[case.kv_format]},
     }
-    if args.copy_calibration > 0:
-        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy of {args.copy_calibration} bytes done", file=sys.stderr, flush=True)
-        del src, dst
+    calibration_copy(args.copy_calibration)
     del b
     torch.cuda.empty_cache()
-    print("[bench] the same rows without request grouping (indices = arange)", file=sys.stderr, flush=True)
-    line["varlen_grouping"] = grouping_comparison(case, args.steps, args.warmup, args.copies)
-    torch.cuda.empty_cache()
+    if not args.no_grouping:
+        print("[bench] the same rows without request grouping (indices = arange)", file=sys.stderr, flush=True)
+        line["varlen_grouping"] = grouping_comparison(case, args.steps, args.warmup, args.copies)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
@@ -477,66 +583,10 @@ def main():
         line["cpu_baseline"]["other_workloads"] = cpu_baseline_configs()
 
     if args.all:
-        others = [("uniform_decode_fp8_32k", lambda: PagedBench(syn.config_uniform_decode(), args.copies * 2)),
-                  ("varlen_spec_decode_mxfp4_64k", lambda: PagedBench(syn.config_varlen_fp4(), args.copies * 2)),
-                  ("varlen_spec_decode_mxfp4_64k_fp4q",
-                   lambda: PagedBench(syn.config_varlen_fp4(q_fp4=True), args.copies * 2)),
-                  ("tiny_decode_fp8", lambda: PagedBench(syn.config_tiny_decode(), 1))]
-        for name, mk in others:
+        for name in OTHERS:
             print(f"[bench] {name}", file=sys.stderr, flush=True)
-            ob = mk()
-            w2, p2 = run_timed(ob, args.steps, args.warmup)
-            if not args.no_graph:
-                w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
-            print(json.dumps(paged_summary(name, ob, w2, p2, args.steps)), file=sys.stderr, flush=True)
-            del ob
-        print("[bench] varlen_spec_decode_fp8_120k_bf16", file=sys.stderr, flush=True)
-        ob = PagedBench(syn.config_varlen_fp8(), args.copies, bf16=True)
-        w2, p2 = run_timed(ob, args.steps, args.warmup)
-        if not args.no_graph:
-            w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
-        c = ob.case
-        t_log = float(p2[:, 1].mean()) * 1e-3
-        kbytes = ob.req_tokens * BYTES_PER_TOKEN[c.kv_format]
-        print(json.dumps({"workload": "varlen_spec_decode_fp8_120k_bf16_logits", "ms_per_step": w2 / args.steps * 1e3,
-                          "ms_schedule": float(p2[:, 0].mean()), "ms_logits": t_log * 1e3,
-                          "ms_upcast": float(p2[:, 2].mean()), "ms_topk": float(p2[:, 3].mean()),
-                          "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
-                          "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
-                          "logits_out_bytes": c.rows * c.max_ctx * 2}), file=sys.stderr, flush=True)
-        del ob
-        print("[bench] varlen_spec_decode_fp8_120k_fused", file=sys.stderr, flush=True)
-        ob = PagedBench(syn.config_varlen_fp8(), args.copies, fused=True)
-        w2, p2 = run_timed(ob, args.steps, args.warmup)
-        if not args.no_graph:
-            w2 = run_graphs(capture_steps(ob), args.steps, args.warmup)
-        print(json.dumps({"workload": "varlen_spec_decode_fp8_120k_fused_logits_topk",
-                          "ms_per_step": w2 / args.steps * 1e3, "ms_schedule": float(p2[:, 0].mean()),
-                          "ms_fused_logits_topk": float(p2[:, 1].mean()),
-                          "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3}), file=sys.stderr, flush=True)
-        del ob
-        print("[bench] dcp_merge_8ranks", file=sys.stderr, flush=True)
-        db = DcpBench(syn.config_varlen_fp8())
-        w2, p2 = run_timed(db, args.steps, args.warmup)
-        t_m = float(p2[:, 2].mean()) * 1e-3
-        mbytes = db.world * db.rows * db.k * 8 + db.rows * db.k * 4
-        print(json.dumps({"workload": "dcp_topk_merge_8ranks_varlen120k", "rows": db.rows, "k": db.k,
-                          "world": db.world, "local_width": db.local_w,
-                          "ms_local_topk": float(p2[:, 0].mean()), "ms_pack": float(p2[:, 1].mean()),
-                          "ms_merge": t_m * 1e3, "merge_bytes": mbytes,
-                          "merge_GBs": mbytes / t_m / 1e9, "merge_hbm_frac": mbytes / t_m / 1e9 / PEAK_HBM_GBS}),
-              file=sys.stderr, flush=True)
-        del db
-        print("[bench] ragged_prefill_4x8192", file=sys.stderr, flush=True)
-        rb = RaggedBench(syn.config_ragged_prefill())
-        w2, p2 = run_timed(rb, max(3, args.steps // 4), 2)
-        n = max(3, args.steps // 4)
-        t_log = float(p2[:, 1].mean()) * 1e-3
-        print(json.dumps({"workload": "ragged_prefill_4x8192", "ms_per_step": w2 / n * 1e3,
-                          "ms_logits": t_log * 1e3, "ms_topk": float(p2[:, 2].mean()),
-                          "scored_Ktok_s": rb.pairs / (w2 / n) / 1e3,
-                          "logits_mfma_frac": rb.pairs * 2 * 64 * 128 / t_log / 1e12 / PEAK_FP8_TFLOPS,
-                          "logits_write_GBs": rb.case.M * rb.case.N * 4 / t_log / 1e9}), file=sys.stderr, flush=True)
+            print(json.dumps(OTHERS[name](args)), file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
 
     print(json.dumps(line), flush=True)
 

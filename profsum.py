@@ -10,11 +10,16 @@ same counter reads for a device-to-device copy of known size
   python profsum.py stats  <kernel_stats.csv>
   python profsum.py trace  <kernel_trace.csv>
   python profsum.py pmc    <counter_collection.csv> <counter> <copy_bytes>
+  python profsum.py counters <counter_collection.csv>
   python profsum.py digest
 
 ``trace`` groups the dispatches of a kernel trace by kernel and launch
 shape (grid and workgroup size), so one run over several workloads that share
 kernels still gives each workload's durations.
+
+``counters`` prints, per kernel and launch shape, the mean per dispatch of every
+counter in a counter_collection.csv (raw values, summed over the hardware
+instances the CSV lists).
 
 ``digest`` prints a hash of the decode-logits kernel sources; a traffic
 figure is only valid for the sources it was measured on.
@@ -81,6 +86,27 @@ def counter_means(path: str, counter: str) -> dict[str, tuple[int, float]]:
     return {k: (len(v), sum(v.values()) / len(v)) for k, v in per.items()}
 
 
+def counters_by_shape(path: str) -> tuple[list[str], list[dict]]:
+    """(counter names, rows): per (kernel, grid, workgroup) the dispatch count and
+    each counter's mean per dispatch (instances of one dispatch summed)."""
+    per = defaultdict(lambda: defaultdict(dict))  # shape -> counter -> dispatch -> value
+    names = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Workgroup_Size"]))
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            d = per[key][c]
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    rows = []
+    for (name, grid, wg), cs in per.items():
+        n = max(len(v) for v in cs.values())
+        rows.append({"name": name, "grid": grid, "wg": wg, "n": n,
+                     **{c: sum(v.values()) / len(v) for c, v in cs.items()}})
+    return names, rows
+
+
 def calibrated(path: str, counter: str, copy_bytes: int) -> tuple[float, dict[str, tuple[int, float, float]]]:
     """(scale, kernel -> (dispatches, KiB per dispatch, calibrated bytes per dispatch)).
 
@@ -99,7 +125,7 @@ def calibrated(path: str, counter: str, copy_bytes: int) -> tuple[float, dict[st
 
 
 def _main(argv: list[str]) -> None:
-    if not argv or argv[0] not in ("stats", "trace", "pmc", "digest"):
+    if not argv or argv[0] not in ("stats", "trace", "pmc", "counters", "digest"):
         print(__doc__)
         raise SystemExit(2)
     if argv[0] == "digest":
@@ -111,6 +137,13 @@ def _main(argv: list[str]) -> None:
             g = "x".join(str(v) for v in r["grid"])
             print(f"{r['name'][:70]:70s} {g:>22s} {r['wg'][0]:5d} {r['calls']:6d} {r['avg_us']:10.2f} "
                   f"{r['min_us']:10.2f} {r['max_us']:10.2f}")
+    elif argv[0] == "counters":
+        names, rows = counters_by_shape(argv[1])
+        for r in sorted(rows, key=lambda r: (r["name"], r["grid"])):
+            print(f"{r['name'][:100]}  grid {r['grid']} wg {r['wg']}  dispatches {r['n']}")
+            for c in names:
+                if c in r:
+                    print(f"    {c:34s} {r[c]:16.6g}")
     elif argv[0] == "stats":
         print(f"{'kernel':90s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'time%':>7s}")
         for r in kernel_stats(argv[1]):
