@@ -101,8 +101,10 @@ enum pml_kv_format { PML_KV_FP8 = 0, PML_KV_MXFP4 = 1 };
  *                    equal cost; entry c < num_CUs is the (first row of its
  *                    row-piece, block offset) where range c starts, and entry
  *                    num_CUs is (num_rows, 0). A row-piece is at most 8
- *                    consecutive rows of one group; units are weighted by
- *                    (4 + rows in the piece) so ranges cost about the same.
+ *                    consecutive rows of one group; a key block is a step of
+ *                    max(block_kv, 64) tokens (a 32-token cache is scored two
+ *                    pages per step); units are weighted by (4 + rows in the
+ *                    piece) so ranges cost about the same.
  *                    The logits calls only read it, so one schedule serves any
  *                    number of calls, concurrent ones included.
  * The schedule is valid only for the same context_lens, indices, next_n,
@@ -312,8 +314,8 @@ int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint8_t *q_scal
  *              call's workspace, then, each region 256-B aligned: thresholds
  *              fp32 [num_rows], widths int32 [num_rows], done flags int32
  *              [num_rows], candidate counts int32 [num_rows][nb], then
- *              candidate lists fp32 [num_rows][nb * block_kv][2], with
- *              nb = ceil(max_ctx / block_kv).
+ *              candidate lists fp32 [num_rows][nb * S][2], with
+ *              S = max(block_kv, 64) tokens per step and nb = ceil(max_ctx / S).
  * How: a first kernel scores an evenly spaced sample of each wide row's blocks
  * and sets a threshold that about 2k of the row's columns are expected to
  * reach (rows of at most 4k columns take every finite logit). The logits

@@ -11,7 +11,8 @@ content is this library's own definition, stated here in plain Python:
   without, a group is the ``next_n`` rows of one batch entry.
 * A group is cut into pieces of at most ``G_MAX`` consecutive rows.
 * A piece's extent is the largest visible length among its rows; it has
-  ``nblk = ceil(extent / block_kv)`` key blocks, each costing ``COST_BASE + g``
+  ``nblk = ceil(extent / step)`` key blocks of ``step = max(block_kv, 64)``
+  tokens (a step of a 32-token cache is two pages), each costing ``COST_BASE + g``
   (g = rows in the piece: a page read and the fixed work of a step, then g
   rows of scoring; a one-row block takes about half the time of a six-row
   one).
@@ -28,6 +29,11 @@ import numpy as np
 
 G_MAX = 8
 COST_BASE = 4
+MIN_STEP = 64  # tokens per unit: a block_kv 32 cache is taken two pages at a time
+
+
+def step_tokens(block_kv: int) -> int:
+    return max(block_kv, MIN_STEP)
 
 
 def visible_lengths(context_lens: np.ndarray, num_rows: int, next_n: int, lens_2d: bool) -> np.ndarray:
@@ -66,7 +72,7 @@ def piece_table(context_lens, num_rows, next_n, lens_2d, indices, block_kv):
     table = []
     for s, g in pieces(num_rows, next_n, idx):
         ext = int(vis[s: s + g].max())
-        nblk = -(-ext // block_kv)
+        nblk = -(-ext // step_tokens(block_kv))
         table.append((s, g, nblk, nblk * (COST_BASE + g)))
     return table
 

@@ -94,6 +94,35 @@ __device__ __forceinline__ void load_page(const uint8_t *pg, KeyRegs<FP4, BKV> &
     if (!FP4) k.sc[0] = *(const uint32_t *)(pg + C::VBYTES + 4 * out_token<BKV>(lane));
 }
 
+// A block of BKV tokens from BKV / PG cache pages of PG tokens each (pg[i]
+// holds tokens PG * i .. PG * i + PG - 1), in the register layout load_page
+// gives a page of BKV tokens: slice t comes from page t / (PG / 16), and an
+// fp8 lane's token scale from the page of the token it finishes.
+template <bool FP4, int BKV, int PG>
+__device__ __forceinline__ void load_pages(const uint8_t *const *pg, KeyRegs<FP4, BKV> &k) {
+    using C = BlockCfg<FP4, BKV>;
+    constexpr int PVB = PG * C::TOKB;  // values region of one page
+    constexpr int SPP = PG / 16;       // slices per page
+    const int lane = lane_id();
+    const int tl = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+        const uint8_t *p = pg[t / SPP];
+        const int tok = 16 * (t % SPP) + tl;
+        if constexpr (FP4) {
+            k.v[t][0] = *(const v4i *)(p + tok * C::TOKB + 16 * grp);
+            k.sc[t] = *(const uint32_t *)(p + PVB + tok * 4) >> (8 * grp);
+        } else {
+            k.v[t][0] = *(const v4i *)(p + tok * C::TOKB + 16 * grp);
+            k.v[t][1] = *(const v4i *)(p + tok * C::TOKB + 64 + 16 * grp);
+        }
+    }
+    if constexpr (!FP4) {
+        const int s = out_token<BKV>(lane);
+        k.sc[0] = *(const uint32_t *)(pg[s / PG] + PVB + 4 * (s % PG));
+    }
+}
+
 // Load keys [t0, t0 + 64) of a contiguous fp8 key array k[N][D] and their fp32
 // scales. Tokens at or past N are read as token N - 1 (their logits are never
 // stored), so no load leaves the arrays.

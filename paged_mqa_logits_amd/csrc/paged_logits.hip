@@ -68,15 +68,34 @@ __device__ __forceinline__ void store_v2f_async(float *p, float x, float y) {
     asm volatile("global_store_dwordx2 %0, %1, off" ::"v"(p), "v"(v) : "memory");
 }
 
-// Load block b of the piece whose table row is bt_row; false (and page 0 is
-// read) when the table entry is unusable, then the block scores NaN.
-template <bool FP4, int BKV>
-__device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, int b, KeyRegs<FP4, BKV> &k) {
-    int32_t e = -1;
-    if (b < a.bt_cols) e = sload(a.bt, bt_row * a.bt_ld + b);
-    const bool ok = e >= 0 && e < a.num_pages;
-    load_page<FP4, BKV>(a.kv + (ok ? (int64_t)e : 0) * a.page_stride, k);
-    return ok;
+// Load block b (BKV tokens) of the piece whose table row is bt_row, from its
+// BKV / PG pages: table entries b * (BKV / PG) + i. Bit i of the result says
+// page i's entry is usable; an unusable entry reads page 0 instead, and its
+// tokens score NaN.
+template <bool FP4, int BKV, int PG = BKV>
+__device__ __forceinline__ int fetch_block(const PagedArgs &a, int64_t bt_row, int b, KeyRegs<FP4, BKV> &k) {
+    constexpr int NP = BKV / PG;
+    if constexpr (NP == 1) {
+        int32_t e = -1;
+        if (b < a.bt_cols) e = sload(a.bt, bt_row * a.bt_ld + b);
+        const bool ok = e >= 0 && e < a.num_pages;
+        load_page<FP4, BKV>(a.kv + (ok ? (int64_t)e : 0) * a.page_stride, k);
+        return ok ? 1 : 0;
+    } else {
+        const uint8_t *pg[NP];
+        int ok = 0;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int pb = b * NP + i;
+            int32_t e = -1;
+            if (pb < a.bt_cols) e = sload(a.bt, bt_row * a.bt_ld + pb);
+            const bool oki = e >= 0 && e < a.num_pages;
+            pg[i] = a.kv + (oki ? (int64_t)e : 0) * a.page_stride;
+            ok |= (oki ? 1 : 0) << i;
+        }
+        load_pages<FP4, BKV, PG>(pg, k);
+        return ok;
+    }
 }
 
 // One step of a wave's block loop: wait for block b, store the previous
@@ -87,16 +106,16 @@ __device__ __forceinline__ bool fetch_block(const PagedArgs &a, int64_t bt_row, 
 // the block. Rows whose visible length ends before the block are skipped
 // (their tail is filled separately). Lane i of vis_lane holds the visible
 // length of row i.
-template <bool FP4, int BKV, typename OT, bool Q4, bool CAND, bool PF>
+template <bool FP4, int BKV, int PG, typename OT, bool Q4, bool CAND, bool PF>
 __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int64_t bt_row, int b,
-                                          const KeyRegs<FP4, BKV> &kc, bool okc, int bp, KeyRegs<FP4, BKV> &kp,
-                                          bool &okp, const uint8_t *s_q, const float *s_w, const uint8_t *s_u,
+                                          const KeyRegs<FP4, BKV> &kc, int okc, int bp, KeyRegs<FP4, BKV> &kp,
+                                          int &okp, const uint8_t *s_q, const float *s_w, const uint8_t *s_u,
                                           const uint8_t *s_us, int vis_lane, WaveSlot<BKV> &sl, int &mask,
                                           int &col0p, const float *s_th) {
     using C = BlockCfg<FP4, BKV>;
     touch<FP4, BKV>(kc);
     flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
-    if constexpr (PF) okp = fetch_block<FP4, BKV>(a, bt_row, bp, kp);
+    if constexpr (PF) okp = fetch_block<FP4, BKV, PG>(a, bt_row, bp, kp);
     const int lane = lane_id();
     const int col0 = b * BKV;
     const int tok = out_token<BKV>(lane);
@@ -126,7 +145,7 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
                 sr = score_row<FP4, BKV, Q4>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS);
             }
             float v = (sr + M[G]) * scale;
-            if (!okc) v = __builtin_nanf("");
+            if (!((okc >> (tok / PG)) & 1)) v = __builtin_nanf("");  // the token's page is unusable
             if (col0 + BKV > vis)  // (wave-uniform: only a row's last block is masked)
                 if (s >= vis) v = -__builtin_inff();
             if (out_lane<BKV>(lane)) lds_st<float>(&sl.v[i][tok], v);
@@ -178,16 +197,16 @@ struct PagedShared {
 // The caller has requested the first block (kb0) before it knew the piece's
 // size, so that load overlaps the length reads; the piece's q, w and pieces
 // are then staged, so those round trips overlap too.
-template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
+template <bool FP4, int BKV, int PG, typename OT, bool Q4, bool CAND>
 __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int64_t bt_row, int b0, int nmy,
-                                          const KeyRegs<FP4, BKV> &kb0, bool okb0, PagedShared<BKV> &sh,
+                                          const KeyRegs<FP4, BKV> &kb0, int okb0, PagedShared<BKV> &sh,
                                           WaveSlot<BKV> &sl) {
     constexpr int NB = kBufs;
     static_assert(kDepth == 1, "the first block comes from the caller");
     const int tid = threadIdx.x;
     const int last = nmy - 1;
     KeyRegs<FP4, BKV> kb[NB];
-    bool okb[NB];
+    int okb[NB];
     kb[0] = kb0;
     okb[0] = okb0;
     // The piece's loads (q, w, pieces, lengths) are all issued before the
@@ -213,7 +232,7 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 #pragma unroll
             for (int u = 0; u < NB; ++u) {
                 if (j + u >= nmy) break;
-                wave_step<FP4, BKV, OT, Q4, CAND, true>(a, r0, g, bt_row, b0 + kPW * (j + u), kb[u], okb[u],
+                wave_step<FP4, BKV, PG, OT, Q4, CAND, true>(a, r0, g, bt_row, b0 + kPW * (j + u), kb[u], okb[u],
                                                         b0 + kPW * min(j + u + kDepth, last), kb[(u + kDepth) % NB],
                                                         okb[(u + kDepth) % NB], sh.q, sh.w, sh.u, sh.us, vis_lane,
                                                         sl, mask, col0p, sh.th);
@@ -224,7 +243,7 @@ __device__ __forceinline__ void run_piece(const PagedArgs &a, int r0, int g, int
 }
 
 // The units from (r0, blk_lo) up to (end_r, end_b) (the whole workgroup).
-template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
+template <bool FP4, int BKV, int PG, typename OT, bool Q4, bool CAND>
 __device__ __forceinline__ void run_range(const PagedArgs &a, int r0, int blk_lo, int end_r, int end_b,
                                           PagedShared<BKV> &sh, WaveSlot<BKV> &sl) {
     const int tid = threadIdx.x;
@@ -241,14 +260,14 @@ __device__ __forceinline__ void run_range(const PagedArgs &a, int r0, int blk_lo
         // table entry and page are read but not used)
         const int b0 = blk_lo + wave;
         KeyRegs<FP4, BKV> kb0;
-        const bool okb0 = fetch_block<FP4, BKV>(a, bt_row, b0, kb0);
+        const int okb0 = fetch_block<FP4, BKV, PG>(a, bt_row, b0, kb0);
         int g, nblk;
         piece_at<BKV>(a.rows, r0, g, nblk);
         const int blk_hi = r0 == end_r ? min(end_b, nblk) : nblk;
         if (blk_lo < blk_hi) {
             // (run_piece holds the barrier after which the previous piece's rows are free)
             const int nmy = b0 < blk_hi ? (blk_hi - b0 + kPW - 1) / kPW : 0;
-            run_piece<FP4, BKV, OT, Q4, CAND>(a, r0, g, bt_row, b0, nmy, kb0, okb0, sh, sl);
+            run_piece<FP4, BKV, PG, OT, Q4, CAND>(a, r0, g, bt_row, b0, nmy, kb0, okb0, sh, sl);
         }
         r0 += g;
         blk_lo = 0;
@@ -262,7 +281,7 @@ __device__ __forceinline__ void run_range(const PagedArgs &a, int r0, int blk_lo
 // drawing from its pool's counter until the pool is empty. So workgroups
 // that run fast (on a compute unit shared with lighter work, say) take more
 // of them. The counters are zeroed by the call's first kernel.
-template <bool FP4, int BKV, typename OT, bool Q4, bool CAND>
+template <bool FP4, int BKV, int PG, typename OT, bool Q4, bool CAND>
 __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedArgs a) {
     __shared__ __attribute__((aligned(16))) PagedShared<BKV> sh;
     __shared__ int s_take;
@@ -277,7 +296,7 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     int r0 = sload(a.sched, 2 * c), b0 = sload(a.sched, 2 * c + 1);
     int r1 = sload(a.split, 2 * c), b1 = sload(a.split, 2 * c + 1);
     for (;;) {
-        run_range<FP4, BKV, OT, Q4, CAND>(a, r0, b0, r1, b1, sh, sh.slot[wave]);
+        run_range<FP4, BKV, PG, OT, Q4, CAND>(a, r0, b0, r1, b1, sh, sh.slot[wave]);
         __syncthreads();  // every wave is done reading s_take
         if (tid == 0) s_take = atomicAdd(a.pools + kPoolStride * x, 1);
         __syncthreads();
@@ -297,9 +316,13 @@ __global__ __launch_bounds__(kPThreads, 8 / kPW) void paged_logits_kernel(PagedA
     }
 }
 
+// block_kv 64: steps of one 64-token page; block_kv 32: steps of 64 tokens
+// from two 32-token pages (step_tokens), which doubles a wave's bytes in
+// flight and halves the per-step work per token.
 template <bool FP4, int BKV, typename OT, bool Q4 = false, bool CAND = false>
 static int launch_paged(const PagedArgs &a, int W, hipStream_t st) {
-    hipLaunchKernelGGL((paged_logits_kernel<FP4, BKV, OT, Q4, CAND>), dim3(W), dim3(kPThreads), 0, st, a);
+    constexpr int S = BKV < kMinStep ? kMinStep : BKV;
+    hipLaunchKernelGGL((paged_logits_kernel<FP4, S, BKV, OT, Q4, CAND>), dim3(W), dim3(kPThreads), 0, st, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
@@ -596,7 +619,7 @@ static int paged_logits(const void *q, const uint8_t *q_scale, int num_rows, int
     if (st0 != PML_OK || empty) return st0;
     if (q_scale && bf16) return PML_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
-    const int rp = launch_pieces(a, block_kv, num_CUs, st);
+    const int rp = launch_pieces(a, pml::step_tokens(block_kv), num_CUs, st);
     if (rp != PML_OK) return rp;
     if (q_scale)
         return block_kv == 64 ? pml::launch_paged<true, 64, float, true>(a, num_CUs, st)
@@ -728,18 +751,19 @@ extern "C" int fp8_fp4_paged_mqa_logits_fp4q(const uint8_t *q_values, const uint
 
 // Workspace of the fused call: the logits call's workspace, then thresholds,
 // row widths and done flags (fp32 / int32 [num_rows] each), the candidate
-// counts (int32 [num_rows][ceil(max_ctx / block_kv)]) and the candidate lists
-// (fp32 [num_rows][ceil(max_ctx / block_kv) * block_kv][2]); every region
-// 256-B aligned.
+// counts (int32 [num_rows][nb]) and the candidate lists (fp32
+// [num_rows][nb * S][2]), S = max(block_kv, 64) tokens per step and
+// nb = ceil(max_ctx / S); every region 256-B aligned.
 extern "C" size_t fp8_fp4_paged_mqa_logits_topk_workspace_size(int num_rows, int max_ctx, int block_kv, int k,
                                                                int num_CUs) {
     if (num_rows < 0 || max_ctx < 0 || (block_kv != 32 && block_kv != 64) || k < 1 || k > PML_MAX_TOPK ||
         num_CUs < 1)
         return 0;
     const size_t rows = (size_t)num_rows;
-    const size_t nb = ((size_t)max_ctx + block_kv - 1) / block_kv;
+    const size_t S = (size_t)pml::step_tokens(block_kv);  // candidate regions are per step
+    const size_t nb = ((size_t)max_ctx + S - 1) / S;
     return fp8_fp4_paged_mqa_logits_workspace_size(num_rows, num_CUs) + 3 * region256(4 * rows) +
-           region256(rows * nb * 4) + region256(rows * nb * block_kv * 8);
+           region256(rows * nb * 4) + region256(rows * nb * S * 8);
 }
 
 extern "C" int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int next_n, int num_heads,
@@ -765,7 +789,8 @@ extern "C" int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int ne
     if (workspace_bytes < fp8_fp4_paged_mqa_logits_topk_workspace_size(num_rows, max_ctx, block_kv, k, num_CUs))
         return PML_ERR_WORKSPACE;
     const size_t rows = (size_t)num_rows;
-    const int64_t nb = ((int64_t)max_ctx + block_kv - 1) / block_kv;
+    const int S = pml::step_tokens(block_kv);  // candidate regions are per step
+    const int64_t nb = ((int64_t)max_ctx + S - 1) / S;
     uint8_t *ws = (uint8_t *)workspace + fp8_fp4_paged_mqa_logits_workspace_size(num_rows, num_CUs);
     const size_t reg = region256(4 * rows);
     float *theta = (float *)ws;
@@ -777,11 +802,11 @@ extern "C" int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int ne
     a.ccount = count;
     a.cand = cand;
     a.count_ld = nb;
-    a.cand_ld = nb * block_kv;
+    a.cand_ld = nb * S;
     const int cap = pml::kCandPerK * k;
     hipStream_t st = (hipStream_t)stream;
     const dim3 tg(num_rows), tb(pml::kThThreads);
-    int rc = launch_pieces(a, block_kv, num_CUs, st);
+    int rc = launch_pieces(a, pml::step_tokens(block_kv), num_CUs, st);
     if (rc != PML_OK) return rc;
     if (kv_format == PML_KV_FP8) {
         if (block_kv == 64) {
@@ -801,7 +826,7 @@ extern "C" int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int ne
         }
     }
     if (rc != PML_OK) return rc;
-    pml::CandSelectArgs cs{cand, count, width, nb, nb * block_kv, block_kv, cap, k, topk, topk_ld, done};
+    pml::CandSelectArgs cs{cand, count, width, nb, nb * S, S, cap, k, topk, topk_ld, done};
     rc = pml::launch_cand_select(cs, num_rows, st);
     if (rc != PML_OK) return rc;
     // rows the candidates could not settle: the full top-k over the written logits

@@ -22,6 +22,11 @@ constexpr int kWave = 64;
 constexpr int kGMax = PML_GMAX;  // rows of one piece scored against a shared key block
 constexpr int kCostBase = 4;    // schedule weight of a block: kCostBase + rows
 
+// Tokens per unit of work (one step of a wave): a block_kv 32 cache is scored
+// two pages at a time, so every step covers 64 tokens.
+constexpr int kMinStep = 64;
+__host__ __device__ inline int step_tokens(int block_kv) { return block_kv < kMinStep ? kMinStep : block_kv; }
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Wave-uniform copy of x (lane 0's value, in a scalar register).

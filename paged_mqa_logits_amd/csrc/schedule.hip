@@ -5,7 +5,9 @@
 // (a caller reads the worker count back as schedule.shape[0] - 1) and that a
 // row slice needs its own ("vllm.model_executor.layers.sparse_attn_indexer",
 // _varlen_decode_rows). Content (this library's): units are ordered by piece
-// then block; a block of a piece with g rows costs kCostBase + g. The work is
+// then block (a block is a step of max(block_kv, 64) tokens: a 32-token cache
+// is scored two pages per step); a block of a piece with g rows costs
+// kCostBase + g. The work is
 // cut into W = num_CUs ranges: entry c is the unit holding cost offset
 // floor(c * T / W) of the total T, as (first row of its piece, block offset),
 // and entry W is (num_rows, 0). Logits workgroup c scores the units from
@@ -236,8 +238,9 @@ extern "C" int paged_mqa_logits_metadata(const int32_t *context_lens, int num_ro
     pml::RowView v{context_lens, indices, context_lens_2d ? 1 : 0, next_n, num_rows};
     const int W = num_CUs;
     const int blocks = std::min((W + pml::kSchedThreads - 1) / pml::kSchedThreads, pml::kSchedMaxBlocks);
+    // units are steps of max(block_kv, 64) tokens: a 32-token cache is scored two pages at a time
     hipLaunchKernelGGL(pml::schedule_kernel, dim3(blocks), dim3(pml::kSchedThreads), 0, (hipStream_t)stream, v,
-                       block_kv, W, schedule);
+                       pml::step_tokens(block_kv), W, schedule);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 

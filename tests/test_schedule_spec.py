@@ -28,7 +28,7 @@ def _check(lens, num_rows, next_n, lens_2d, indices, bkv, W):
     vis = S.visible_lengths(lens, num_rows, next_n, lens_2d)
     for s, g, nblk, cost in table:
         assert 1 <= g <= S.G_MAX
-        assert nblk == -(-int(vis[s:s + g].max()) // bkv)
+        assert nblk == -(-int(vis[s:s + g].max()) // max(bkv, 64))
         if indices is not None:
             assert len(set(np.asarray(indices)[s:s + g].tolist())) == 1
         else:
