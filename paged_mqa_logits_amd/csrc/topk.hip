@@ -9,7 +9,7 @@
 // ascending without a sort:
 //  * When every row has at most 8192 columns (max_width <= 8192) a compact
 //    256-thread kernel holds the row's keys in registers and selects there
-//    (topk_small_kernel: 4.6 KB of LDS, six rows per CU).
+//    (topk_small_kernel: 8.7 KB of LDS, six rows per CU).
 //  * Otherwise a row that fits the LDS candidate list is read once into it.
 //  * A row of 16K columns or more first takes a sampled pass: a histogram of
 //    the top 11 key bits over each wave's first 512 positions (16 places
@@ -564,15 +564,33 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     }
 }
 
+// order_key(f) + 1 (see select.h): -0 as +0, a NaN 1, every number at least
+// 0x00800000 (the key of -inf plus one).
+__device__ __forceinline__ uint32_t held_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t t = (uint32_t)((int32_t)u >> 31) | 0x80000000u;  // negative: all bits; else the sign
+    return __builtin_isnan(f) ? 1u : (u ^ t) + 1u;
+}
+
 // Rows of at most 8192 columns (max_width <= 8192): each thread holds the keys
 // of positions j * NT + tid (j < 32) in registers, loaded together, so the
-// row costs one memory round trip. The first radix pass histograms them as
-// they arrive; the later passes read the registers again (bin counts never
-// pass 8192, so the histogram keeps two 16-bit counters per word, 4 KB of
-// LDS). The placement walks the row in chunks of 64 positions (round j, wave
-// w): per chunk two ballots give every lane its count of greater and equal
-// keys before it, on top of the chunk's base from one block scan over all
-// chunks' counts, so selected positions go to consecutive slots in order.
+// row costs one memory round trip. The kernel is bound by VALU issue (six rows
+// per CU), so the per-key work is kept small:
+//  * A held key is the order key plus one, and 0 for a slot past the row's
+//    end (the order key of -inf is 0x007fffff, so 1, a NaN, and 0 sit below
+//    every number). Validity is then decided once, when the key is formed.
+//  * Every pass histograms bins of 32-bit counters (8 KB of LDS). Empty slots
+//    land in bin 0 of a pass whose fixed bits are all zero, and their count
+//    is taken back out of that bin before it is searched.
+//  * When the picked bin is taken whole (the usual end), the selected keys
+//    are exactly those at or above its lower bound: one compare per key, whose
+//    ballot gives both the 64-position chunk's count and each lane's slot.
+//    Ties at the k-th key (a bin of equal keys only partly taken) take two
+//    ballots per chunk, greater and equal, as before.
+// Chunk (j, w) covers positions j * NT + 64 w + [0, 64); one block scan over
+// the chunks' counts gives each chunk its first output slot, so selected
+// positions go to consecutive slots in ascending order.
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
@@ -580,8 +598,9 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int kPer = kMaxCols / NT;  // keys per thread
     constexpr int kChunks = kPer * NW;   // 64-position chunks of a full row
     static_assert(kChunks <= NT, "one chunk count per thread in the scan");
-    __shared__ uint32_t s_hist[kBins / 2];
-    __shared__ uint32_t s_base[kChunks];  // packed (greater | equal << 16) before each chunk
+    static_assert(kPer <= kWave, "one chunk count per lane of a wave");
+    __shared__ uint32_t s_hist[kBins];
+    __shared__ uint32_t s_base[kChunks];  // first output slot of each chunk (packed greater | equal << 16 on ties)
     __shared__ uint32_t s_wave[NW];
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
@@ -607,75 +626,122 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
         return;
     }
     const float *row = a.logits + (int64_t)r * a.ld + lo;
+    const int nj = (n + NT - 1) / NT;        // rounds j holding positions (uniform)
+    // a fresh opaque copy of nj for each loop: the per-round tests are then
+    // scalar compares in every loop, not 32 lane masks kept alive in SGPRs
+    auto rounds = [nj]() {
+        int v = nj;
+        asm volatile("" : "+s"(v));
+        return v;
+    };
+    const uint32_t empty = (uint32_t)(nj * NT - n);  // slots of those rounds past the row's end
     uint32_t key[kPer];
     {
         float x[kPer];
+        const int nj0 = rounds();
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-            if (j * NT < n) x[j] = row[min(j * NT + tid, n - 1)];
-        for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
+            if (j < nj0) x[j] = row[min(j * NT + tid, n - 1)];
+        for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         __syncthreads();
+        const int nj1 = rounds();
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             key[j] = 0;
-            if (j * NT < n && j * NT + tid < n) {
-                key[j] = order_key(x[j]);
-                const uint32_t bin = key[j] >> 21;
-                atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
+            if (j < nj1) {
+                key[j] = tid < n - j * NT ? held_key(x[j]) : 0u;
+                atomicAdd(&s_hist[key[j] >> 21], 1u);
             }
         }
+        if (tid == 0 && empty) atomicSub(&s_hist[0], empty);
     }
     __syncthreads();
-    uint32_t prefix = 0, mask = 0, kk = (uint32_t)k;
-    auto count = [&](int b) { return (s_hist[b >> 1] >> ((b & 1) << 4)) & 0xffffu; };
+    uint32_t prefix = 0, mask = 0, kk = (uint32_t)k, cnt = 0;
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
         const int nbins = pass == 2 ? 1024 : 2048;
         if (pass > 0) {
-            for (int b = tid; b < kBins / 2; b += NT) s_hist[b] = 0;
+            for (int b = tid; b < nbins; b += NT) s_hist[b] = 0;
             __syncthreads();
+            const int njp = rounds();
 #pragma unroll
             for (int j = 0; j < kPer; ++j)
-                if (j * NT < n && j * NT + tid < n && (key[j] & mask) == prefix) {
-                    const uint32_t bin = (key[j] >> shift) & (nbins - 1);
-                    atomicAdd(&s_hist[bin >> 1], 1u << ((bin & 1) << 4));
-                }
+                if (j < njp && (key[j] & mask) == prefix) atomicAdd(&s_hist[(key[j] >> shift) & (nbins - 1)], 1u);
+            if (tid == 0 && prefix == 0 && empty) atomicSub(&s_hist[0], empty);
             __syncthreads();
         }
-        pick_bin_by<NT>(count, nbins, kk, s_wave, s_pick);
-        const uint32_t cnt = count((int)s_pick[0]);
+        pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+        cnt = s_hist[s_pick[0]];
         prefix |= s_pick[0] << shift;
         mask |= (uint32_t)(nbins - 1) << shift;
         kk -= s_pick[1];
         __syncthreads();
-        if (cnt == kk) break;  // the picked bin is taken whole: keys compare under mask
+        if (cnt == kk) break;  // the picked bin is taken whole
     }
+    const int nch = nj * NW;  // chunks holding positions
+    if (cnt == kk) {
+        // selected: key >= the picked bin's lower bound (at least 1: empty slots never)
+        const uint32_t T = max(prefix, 1u);
+        uint32_t mine = 0;  // lane j: this wave's count in round j
+        int njl = rounds();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (j >= njl) continue;
+            const uint32_t c = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j] >= T));
+            mine = lane == j ? c : mine;
+        }
+        if (lane < nj) s_base[lane * NW + wave] = mine;
+        __syncthreads();
+        const uint32_t v = tid < nch ? s_base[tid] : 0u;
+        uint32_t tot;
+        const uint32_t excl = block_scan<NT>(v, s_wave, &tot) - v;
+        if (tid < nch) s_base[tid] = excl;
+        __syncthreads();
+        // recompute the compares rather than keep 32 lane masks in SGPRs across the scan
+        uint32_t T2 = T;
+        asm volatile("" : "+s"(T2));
+        njl = rounds();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (j >= njl) continue;
+            const uint32_t base = s_base[j * NW + wave];
+            const bool sel = key[j] >= T2;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(sel);
+            const uint32_t slot =
+                base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (sel && slot < (uint32_t)k) out[slot] = j * NT + tid;  // (the counts give slot < k)
+        }
+        return;
+    }
+    // ties: every bit is fixed (mask is all ones), T >= 1, and `need` of the
+    // keys equal to T are taken, in position order
     const uint32_t T = prefix;
-    const uint32_t need = kk;  // keys in T's bin that are taken (>= 1)
-    // chunk (j, w) = positions j * NT + 64 w + [0, 64): counts, one block scan, placement
-    auto greater = [&](int j) { return j * NT < n && j * NT + tid < n && (key[j] & mask) > T; };
-    auto equal = [&](int j) { return j * NT < n && j * NT + tid < n && (key[j] & mask) == T; };
-    uint32_t mine = 0;  // thread t < kChunks: packed counts of chunk t
+    const uint32_t need = kk;
+    uint32_t mine = 0;
+    int njl = rounds();
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        if (j * NT >= n) break;
-        const uint32_t g = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(greater(j)));
-        const uint32_t e = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(equal(j)));
-        if (lane == 0) s_base[j * NW + wave] = g | (e << 16);
+        if (j >= njl) continue;
+        const uint32_t g = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j] > T));
+        const uint32_t e = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(key[j] == T));
+        mine = lane == j ? (g | (e << 16)) : mine;
     }
+    if (lane < nj) s_base[lane * NW + wave] = mine;
     __syncthreads();
-    const int nch = ((n + NT - 1) / NT) * NW;  // chunks written above
-    if (tid < nch) mine = s_base[tid];
+    const uint32_t v = tid < nch ? s_base[tid] : 0u;
     uint32_t tot;
-    const uint32_t excl = block_scan<NT>(mine, s_wave, &tot) - mine;
+    const uint32_t excl = block_scan<NT>(v, s_wave, &tot) - v;
     if (tid < nch) s_base[tid] = excl;
     __syncthreads();
+    uint32_t T2 = T;
+    asm volatile("" : "+s"(T2));
+    njl = rounds();
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-        if (j * NT >= n) break;
+        if (j >= njl) continue;
         const uint32_t base = s_base[j * NW + wave];
-        const bool gt = greater(j), eq = equal(j);
+        const bool gt = key[j] > T2, eq = key[j] == T2;
         const uint64_t gm = __builtin_amdgcn_ballot_w64(gt), em = __builtin_amdgcn_ballot_w64(eq);
         const uint32_t gb = (base & 0xffffu) +
                             __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));

@@ -57,11 +57,19 @@ def test_adversarial_rows():
     r[7] = np.nan                                             # NaN ranks lowest
     rows.append(r)
     rows.append(np.arange(W, dtype=np.float64)[::-1].copy())  # descending
+    r = rng.standard_normal(W)
+    r[rng.random(W) < 0.7] = np.nan                           # the k-th among the NaNs
+    rows.append(r)
+    rows.append(np.full(W, np.nan))                           # all NaN
+    r = np.full(W, -np.inf)
+    r[rng.random(W) < 0.5] = np.nan                           # -inf above NaN
+    rows.append(r)
     L = np.stack(rows)
     n = L.shape[0]
     G.banner("top-k adversarial")
     for k, ke in ((1, [W] * n), (64, [W] * n), (2048, [W] * n), (4096, [W] * n),
-                  (100, [100, 99, 101, 50, 0, 100, 5000, 1])):
+                  (100, [100, 99, 101, 50, 0, 100, 5000, 1, 4999, 257, 256]),
+                  (2048, [5000, 4097, 2049, 4000, 3000, 2300, 4999, 2048, 4095, 4096, 2500])):
         _shared_input_check(L, ke, k)
 
 
