@@ -17,25 +17,26 @@
 //    row's keys at or above it, by the sample's share). Then one streaming
 //    pass, which starts from the sample's registers, appends in position
 //    order every element whose top digit is >= b into its wave's region of
-//    the list (each wave's span of the row is contiguous), and the regions are
-//    packed together. Any key outside the list is then below every key in
-//    it, so if the list holds at least k keys the top k are among them and
-//    the selection finishes in the list. When the sample holds, the row is
-//    read once rather than three times. The pass is bound by
-//    instruction issue, one row per CU, so when the bucket lies above -inf it
-//    walks the row in words (lane l holds positions r + 64 j + l): per word
-//    index one float compare, a ballot whose popcount advances the wave's
-//    count, and, for the candidates only, a slot from mbcnt and one LDS
-//    store of value and position. Order keys are formed only for the list,
-//    when the regions are packed.
+//    the list (each wave's span of the row is contiguous). Any key outside
+//    the regions is then below every key in them, so if they hold at least k
+//    keys the top k are among them: every wave lifts its region into
+//    registers (forming the order keys there), and the selection and the
+//    placement run on those registers, placing by ballots over 64-entry
+//    chunks in (wave, entry) order, which is position order. When the sample
+//    holds, the row is read once rather than three times. When the bucket
+//    lies above -inf the pass walks the row in words (lane l holds positions
+//    r + 64 j + l): per word index one float compare, a ballot whose popcount
+//    advances the wave's count, and, for the candidates only, a slot from
+//    mbcnt and one LDS store of value and position.
 //  * Narrower rows, and rows where the sample misjudges (fewer than k
 //    candidates, or a region overflows), take the exact streaming passes: a
 //    full histogram fixes b, then every wave counts, then appends, the
 //    candidates.
-//  * The remaining key bits are selected inside the list: radix digits from
-//    the highest bit where the live keys differ, until the picked bin is
-//    taken whole or holds at most 64 keys (one wave then sorts those). One
-//    block scan over the list places every selected element.
+//  * The key bits are selected among the candidates (registers or list):
+//    radix digits from the highest bit where the live keys differ, until the
+//    picked bin is taken whole or holds at most 64 keys (one wave then sorts
+//    those). One block scan over the candidates' counts places every selected
+//    element.
 //  * If the candidates overflow the list (heavy ties), the selection finishes
 //    with passes over the row itself.
 #include "select.h"
@@ -216,6 +217,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     bool in_list = true;
     bool ranged = false;  // the list's key range (max of key and of ~key) is known from the pack
     uint32_t rkmax = 0, rnkmin = 0;
+    // After a sampled pass that holds, every wave keeps its region of the list
+    // in registers (entry lane + 64 u in rk[u] / rp[u]) and the selection runs
+    // there: no pack, and the placement by ballots over 64-entry chunks.
+    constexpr int kRegs = Cfg::RCAP / kWave;
+    uint32_t rk[kRegs];
+    int32_t rp[kRegs];
+    uint32_t rcnt = 0;  // entries of this wave's region (wave-uniform)
+    bool regs = false;
 
     // this wave's share of the 16-B groups covering [lo, hi)
     const int gq0 = lo >> 2, gq1 = (hi + 3) >> 2;
@@ -311,40 +320,32 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             over |= c > (uint32_t)RCAP;
         }
         if (!over && total >= (uint32_t)k) {
-            // pack the regions: every wave lifts its entries, then puts them at base
-            constexpr int kPer = RCAP / kWave;
-            uint32_t kv[kPer];
-            int32_t pv[kPer];
+            // every wave lifts its region into registers (order keys formed here)
             uint32_t lmax = 0, lnmin = 0;
 #pragma unroll
-            for (int u = 0; u < kPer; ++u) {
+            for (int u = 0; u < kRegs; ++u) {
                 const uint32_t i = lane + u * kWave;
+                rk[u] = 0;
+                rp[u] = 0;
                 if (i < cnt) {
-                    kv[u] = s_key[wave * RCAP + i];
-                    if (raw) kv[u] = order_key(__uint_as_float(kv[u]));
-                    pv[u] = s_pos[wave * RCAP + i];
-                    lmax = max(lmax, kv[u]);
-                    lnmin = max(lnmin, ~kv[u]);
+                    rk[u] = s_key[wave * RCAP + i];
+                    if (raw) rk[u] = order_key(__uint_as_float(rk[u]));
+                    rp[u] = s_pos[wave * RCAP + i];
+                    lmax = max(lmax, rk[u]);
+                    lnmin = max(lnmin, ~rk[u]);
                 }
             }
-            // the list's key range rides on the pack's barriers (read after the next one)
+            // the candidates' key range (read after the next barrier)
             lmax = wave_max_to_last(lmax);
             lnmin = wave_max_to_last(lnmin);
             if (lane == kWave - 1) {
                 s_wave[wave] = lmax;
                 s_wave[NW + wave] = lnmin;
             }
-            __syncthreads();
-#pragma unroll
-            for (int u = 0; u < kPer; ++u) {
-                const uint32_t i = lane + u * kWave;
-                if (i < cnt) {
-                    s_key[base + i] = kv[u];
-                    s_pos[base + i] = pv[u];
-                }
-            }
-            m = (int)total;  // all three digits are selected inside the list
+            rcnt = __builtin_amdgcn_readfirstlane(cnt);
+            m = (int)total;  // all three digits are selected among the candidates
             ranged = true;
+            regs = true;
         }
         __syncthreads();
         if (ranged) {
@@ -413,6 +414,125 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         }
         __syncthreads();
         }  // exact passes
+    }
+
+    if (regs) {
+        // Radix digits over the registers, from the highest bit where the
+        // candidates differ, until the picked bin is taken whole or holds at
+        // most 64 keys (one wave sorts those); then the placement.
+        const int nu = (int)((rcnt + kWave - 1) / kWave);  // register rows holding entries (uniform)
+        auto rows_ = [nu]() {  // an opaque copy per loop: scalar tests, no lane masks kept alive
+            int v = __builtin_amdgcn_readfirstlane(nu);
+            asm volatile("" : "+s"(v));
+            return v;
+        };
+        const uint32_t diff = rkmax ^ ~rnkmin;
+        if (diff == 0) {
+            prefix = rkmax;  // every candidate equal
+            mask = 0xffffffffu;
+        } else {
+            int top = 31 - __builtin_clz(diff);
+            mask = top == 31 ? 0u : ~((2u << top) - 1u);
+            prefix = rkmax & mask;
+#pragma unroll 1
+            for (;;) {
+                const int shift = max(top - 10, 0);
+                const int nbins = 1 << (top - shift + 1);
+                for (int b = tid; b < nbins; b += NT) s_hist[b] = 0;
+                __syncthreads();
+                const int nh = rows_();
+#pragma unroll
+                for (int u = 0; u < kRegs; ++u)
+                    if (u < nh && lane + u * kWave < rcnt && (rk[u] & mask) == prefix)
+                        atomicAdd(&s_hist[(rk[u] >> shift) & (nbins - 1)], 1u);
+                __syncthreads();
+                pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+                const uint32_t cnt = s_hist[s_pick[0]];
+                prefix |= s_pick[0] << shift;
+                mask |= (uint32_t)(nbins - 1) << shift;
+                kk -= s_pick[1];
+                if (tid == 0) s_nsmall = 0;
+                __syncthreads();
+                if (cnt == kk || shift == 0) break;
+                if (cnt <= (uint32_t)kWave) {
+                    const int ng = rows_();
+#pragma unroll
+                    for (int u = 0; u < kRegs; ++u)
+                        if (u < ng && lane + u * kWave < rcnt && (rk[u] & mask) == prefix)
+                            s_small[atomicAdd(&s_nsmall, 1u)] = rk[u];
+                    __syncthreads();
+                    if (wave == 0) {
+                        uint32_t v = (uint32_t)lane < cnt ? s_small[lane] : 0u;  // 0: below every key
+#pragma unroll
+                        for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+                            for (int j = size >> 1; j > 0; j >>= 1) {
+                                const uint32_t o = (uint32_t)lane_xor((int32_t)v, j);
+                                const bool keep_max = ((lane & size) == 0) == ((lane & j) == 0);
+                                v = keep_max ? max(v, o) : min(v, o);
+                            }
+                        }
+                        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, (int)kk - 1);
+                        const uint32_t above = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v > t));
+                        if (lane == 0) {
+                            s_pick[0] = t;
+                            s_pick[1] = kk - above;
+                        }
+                    }
+                    __syncthreads();
+                    prefix = s_pick[0];
+                    mask = 0xffffffffu;
+                    kk = s_pick[1];
+                    break;
+                }
+                top = shift - 1;
+            }
+        }
+        // placement: chunk (wave, u) holds entries lane + 64 u of the wave's
+        // region; chunks in (wave, u) order are in position order. Per chunk
+        // the ballots of greater and equal keys give its counts, one block scan
+        // gives each chunk its first slots, and mbcnt each lane's.
+        const uint32_t T = prefix, need = kk;
+        uint32_t *const s_base = s_hist;  // NW * kRegs packed (greater | equal << 16) counts
+        uint32_t mine = 0;
+        const int nc = rows_();
+#pragma unroll
+        for (int u = 0; u < kRegs; ++u) {
+            if (u >= nc) continue;
+            const bool v = lane + u * kWave < rcnt;
+            const uint32_t key = rk[u] & mask;
+            const uint32_t g = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v && key > T));
+            const uint32_t e = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(v && key == T));
+            mine = lane == u ? (g | (e << 16)) : mine;
+        }
+        if (lane < kRegs) s_base[wave * kRegs + lane] = mine;
+        __syncthreads();
+        const uint32_t cv = tid < NW * kRegs ? s_base[tid] : 0u;
+        uint32_t tot;
+        const uint32_t excl = block_scan<NT>(cv, s_wave, &tot) - cv;
+        if (tid < NW * kRegs) s_base[tid] = excl;
+        __syncthreads();
+        uint32_t T2 = __builtin_amdgcn_readfirstlane(T);
+        asm volatile("" : "+s"(T2));  // the compares again, rather than 24 lane masks kept in SGPRs
+        const int np = rows_();
+#pragma unroll
+        for (int u = 0; u < kRegs; ++u) {
+            if (u >= np) continue;
+            const uint32_t base = s_base[wave * kRegs + u];
+            const bool v = lane + u * kWave < rcnt;
+            const uint32_t key = rk[u] & mask;
+            const bool gt = v && key > T2, eq = v && key == T2;
+            const uint64_t gm = __builtin_amdgcn_ballot_w64(gt), em = __builtin_amdgcn_ballot_w64(eq);
+            const uint32_t gb = (base & 0xffffu) +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
+            const uint32_t eb = (base >> 16) +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
+            if (gt)
+                out[gb + min(eb, need)] = rp[u];
+            else if (eq && eb < need)
+                out[gb + eb] = rp[u];
+        }
+        return;
     }
 
     // remaining radix digits. In the list, the live keys (those in the bin
