@@ -10,9 +10,9 @@
 // blocks that intersect the union of the rows' key ranges in turn, loading 64
 // keys at a time into VGPRs (three buffers deep) and scoring them with the
 // core of logits_core.h, as in the paged kernel. The chunk's other columns of
-// its rows are
-// filled with -inf and nothing is read for them, so a causal prefill does
-// about half the work of the dense product.
+// its rows are filled with -inf, a slice per block step, and nothing is read
+// for them, so a causal prefill does about half the work of the dense
+// product.
 #include <type_traits>
 
 #include "logits_core.h"
@@ -37,6 +37,63 @@ struct RaggedArgs {
     int chunk;  // key blocks per workgroup
 };
 
+// A wave's share of a piece's -inf columns, written a slice per step of its
+// block loop, so the fill's stores spread over the scoring instead of
+// preceding it (they go out before the step's key loads, like the logit
+// stores). The wave takes rows i = wave, wave + kCW, ... of the piece; each
+// row has a left region [c0, lend) and a right region [rs, re), both starting
+// on a multiple of 64 columns, re a multiple of 4 (a row's last columns past
+// re are stored at set-up). One store instruction covers 256 columns of a
+// region. All fields are wave-uniform.
+struct NegFill {
+    float *out;
+    int64_t out_ld;
+    int row0, g, wave;
+    int c0, lend, rs, re;  // the piece's regions (the same for every row)
+    int item;              // next region: row wave + kCW * (item / 2), side item % 2
+    float *base;           // current row
+    int col, end;          // current region [col, end)
+    bool active;
+
+    __device__ bool next_region() {
+        while (true) {
+            const int i = wave + kCW * (item >> 1);
+            if (i >= g) return false;
+            const int side = item & 1;
+            ++item;
+            const int s = side ? rs : c0, e = side ? re : lend;
+            if (e > s) {
+                base = out + (int64_t)(row0 + i) * out_ld;
+                col = s;
+                end = e;
+                return true;
+            }
+        }
+    }
+    // store instructions for all of this wave's regions
+    __device__ int count() const {
+        const int rows = g > wave ? (g - wave + kCW - 1) / kCW : 0;
+        const int per_row = (max(lend - c0, 0) + 255) / 256 + (max(re - rs, 0) + 255) / 256;
+        return rows * per_row;
+    }
+    __device__ void init() {
+        item = 0;
+        active = next_region();
+    }
+    // up to n store instructions
+    __device__ void slice(int n) {
+        const int lane = lane_id();
+        const float ninf = -__builtin_inff();
+        const v4f pat = {ninf, ninf, ninf, ninf};
+        for (int t = 0; t < n && active; ++t) {
+            const int c = col + 4 * lane;
+            if (c < end) store_v4f_async(base + c, pat);
+            col += 256;
+            if (col >= end) active = next_region();
+        }
+    }
+};
+
 // One step of a wave's block loop (see wave_step of the paged kernel); every
 // row of the piece is stored, -inf outside its [lo, hi) (lane i of lo_lane /
 // hi_lane holds the bounds of row i). Rows go in quads, the linear half of a
@@ -46,9 +103,10 @@ __device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g
                                             const KeyRegs<false, 64> &kc, int bp, KeyRegs<false, 64> &kp,
                                             const uint8_t *s_q, const float *s_w, const uint8_t *s_u,
                                             const uint8_t *s_us, int lo_lane, int hi_lane, WaveSlot<64> &sl,
-                                            int &mask, int &col0p) {
+                                            int &mask, int &col0p, NegFill &fill, int fill_per) {
     touch<false, 64>(kc);
     flush_slot<64>(sl, mask, row0, col0p, a.N, a.out, a.out_ld);
+    fill.slice(fill_per);
     if constexpr (PF) load_contig(a.k, a.k_scale, a.N, bp * 64, kp);
     const int lane = lane_id();
     const int s = b * 64 + lane;
@@ -111,18 +169,20 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
         if (u_hi < u_lo) u_hi = u_lo;
     }
 
-    // -inf on the chunk's columns that are not scored
+    // -inf on the chunk's columns that are not scored: all at once when
+    // nothing is scored, else a slice per step (NegFill) plus, here, each
+    // row's last columns past a multiple of 4
     const int cend = min(c1 * BKV, N);
-    for (int i = 0; i < g; ++i) {
-        float *row = a.out + (int64_t)(row0 + i) * a.out_ld;
-        if (u_hi > u_lo) {
-            fill_neg_inf(row, c0 * BKV, u_lo * BKV);
-            fill_neg_inf(row, min(u_hi * BKV, cend), cend);
-        } else {
-            fill_neg_inf(row, c0 * BKV, cend);
-        }
+    if (u_hi <= u_lo) {
+        for (int i = 0; i < g; ++i) fill_neg_inf(a.out + (int64_t)(row0 + i) * a.out_ld, c0 * BKV, cend);
+        return;
     }
-    if (u_hi <= u_lo) return;
+    const int rs = min(u_hi * BKV, cend);       // a multiple of 64, or cend
+    const int re = max(rs, cend & ~3);
+    if (tid < g * 4 && re + (tid & 3) < cend)    // at most 3 columns a row
+        a.out[(int64_t)(row0 + (tid >> 2)) * a.out_ld + re + (tid & 3)] = -__builtin_inff();
+    NegFill fill{a.out, a.out_ld, row0, g, wave, c0 * BKV, u_lo * BKV, rs, re};
+    fill.init();
 
     stage_rows(a.q, a.w, row0, g, s_q, s_w);
     if (tid < g) {
@@ -137,14 +197,18 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
     const int lo_lane = lds_ld<int>(&s_lo[lane_id() % kGMax]);  // lane i: bounds of row i
     const int hi_lane = lds_ld<int>(&s_hi[lane_id() % kGMax]);
     const int b0 = u_lo + wave;
-    if (b0 >= u_hi) return;
+    if (b0 >= u_hi) {
+        fill.slice(fill.count());  // no blocks for this wave: its share of the fill at once
+        return;
+    }
     const int nmy = (u_hi - b0 + kCW - 1) / kCW;  // this wave's blocks
+    const int fill_per = (fill.count() + nmy - 1) / nmy;  // fill stores per step
     WaveSlot<BKV> &sl = s_slot[wave];
     KeyRegs<false, BKV> k0, k1, k2;
     int mask = 0, col0p = 0;
     auto step = [&](const KeyRegs<false, BKV> &kc, int j, KeyRegs<false, BKV> &kp, auto pf) {
         ragged_step<decltype(pf)::value>(a, row0, g, b0 + kCW * j, kc, b0 + kCW * (j + 2), kp, s_q, s_w, s_u, s_us,
-                                         lo_lane, hi_lane, sl, mask, col0p);
+                                         lo_lane, hi_lane, sl, mask, col0p, fill, fill_per);
     };
     constexpr std::true_type PF{};
     constexpr std::false_type NOPF{};
@@ -182,6 +246,7 @@ __global__ __launch_bounds__(kLThreads, 2) void ragged_logits_kernel(RaggedArgs 
         if (nmy > 1) step(k1, 1, k2, NOPF);
     }
     flush_slot<BKV>(sl, mask, row0, col0p, N, a.out, a.out_ld);
+    fill.slice(fill.count());  // (nothing is left: every step took its share)
 }
 
 }  // namespace pml

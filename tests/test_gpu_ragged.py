@@ -52,6 +52,26 @@ def test_arbitrary_bounds():
     G.assert_logits_close(gpu, oracle.ragged_logits(case), case.weights)
 
 
+def test_multi_chunk_bounds():
+    """Several key chunks per row (fewer pieces than the grid aims for), N not a
+    multiple of 4, and bounds that leave -inf on both sides of a row's span, in
+    every chunk: the -inf columns are written a slice per block step."""
+    case = syn.make_ragged_case([1100, 1103], seed=730)
+    rng = np.random.default_rng(731)
+    ks = rng.integers(-40, case.N, case.M)
+    ke = ks + rng.integers(-10, 1500, case.M)
+    ks[:3] = 0
+    ke[:3] = case.N + 5
+    case.ks.copy_(torch.from_numpy(ks.astype(np.int32)))
+    case.ke.copy_(torch.from_numpy(ke.astype(np.int32)))
+    rows = np.sort(np.concatenate([np.arange(12), np.arange(case.M - 12, case.M),
+                                   rng.choice(case.M, 200, replace=False)]))
+    rows = np.unique(rows)
+    G.banner(f"ragged multi-chunk N={case.N} rows={len(rows)}")
+    gpu = run_ragged(case).cpu().numpy()[rows, : case.N]
+    G.assert_logits_close(gpu, oracle.ragged_logits(case, rows=rows), case.weights[torch.from_numpy(rows)])
+
+
 def test_exact_arithmetic():
     """Exactly representable inputs: the oracle within the mass bound (tests/_gpu.py, MASS_FRAC)."""
     case = syn.make_ragged_case([600, 77], seed=720)
