@@ -33,15 +33,38 @@ constexpr int kSchedWaves = kSchedThreads / kWave;
 constexpr int kHalo = kGMax;  // rows past a tile that a piece starting in it may cover
 constexpr int kSchedMaxBlocks = 64;  // workgroups that share out the entries (each walks all rows)
 
-// Block-wide inclusive scan: wave shuffles, then one pass over the wave totals.
+// x of the lane the DPP control CTRL names (row shifts and row broadcasts),
+// or ident where it names none or the row is outside ROWMASK.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_from(int ident, int x) {
+    return __builtin_amdgcn_update_dpp(ident, x, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ long long dpp_from(long long ident, long long x) {
+    const int lo = dpp_from<CTRL, ROWMASK>((int)ident, (int)x);
+    const int hi = dpp_from<CTRL, ROWMASK>((int)(ident >> 32), (int)(x >> 32));
+    return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+
+// Inclusive scan over the wave by DPP moves, no LDS traffic: shifts by 1, 2,
+// 4, 8 lanes inside each row of 16, then row 0's and row 2's last lanes into
+// rows 1 and 3, then lane 31 into rows 2 and 3.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_scan_dpp(T x, Op op, T ident) {
+    x = op(x, dpp_from<0x111, 0xf>(ident, x));  // row_shr:1
+    x = op(x, dpp_from<0x112, 0xf>(ident, x));  // row_shr:2
+    x = op(x, dpp_from<0x114, 0xf>(ident, x));  // row_shr:4
+    x = op(x, dpp_from<0x118, 0xf>(ident, x));  // row_shr:8
+    x = op(x, dpp_from<0x142, 0xa>(ident, x));  // row_bcast:15
+    x = op(x, dpp_from<0x143, 0xc>(ident, x));  // row_bcast:31
+    return x;
+}
+
+// Block-wide inclusive scan: a DPP scan per wave, then one pass over the wave totals.
 template <typename T, typename Op>
 __device__ __forceinline__ T block_scan_incl(T x, T *s_w, Op op, T ident) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const T y = __shfl_up(x, off, kWave);
-        if (lane >= off) x = op(x, y);
-    }
+    x = wave_scan_dpp(x, op, ident);
     if (lane == kWave - 1) s_w[wave] = x;
     __syncthreads();
     T pre = ident;
@@ -102,9 +125,11 @@ __device__ __forceinline__ long long tile_cost(const RowView &v, int block_kv, i
 }
 
 // Start offset of chunk c: floor(c * T / C) = c * qC + floor(c * rC / C)
-// with T = qC * C + rC, so no product passes 2^63 (c <= C <= 2^23).
+// with T = qC * C + rC, so no product passes 2^63 (c <= C <= 2^23). c * rC
+// < C^2, so for C <= 46340 the quotient is a 32-bit division.
 __device__ __forceinline__ long long chunk_start(long long c, long long qC, long long rC, int C) {
-    return c * qC + c * rC / C;
+    const long long f = C <= 46340 ? (long long)((uint32_t)(c * rC) / (uint32_t)C) : c * rC / C;
+    return c * qC + f;
 }
 
 // First chunk c whose start offset is at least x (0 <= x <= T): a double
@@ -123,16 +148,19 @@ __device__ __forceinline__ long long first_chunk_at(long long x, long long T, lo
 // running cost sh.incl exceeds t (a binary search over the tile), and t's
 // block is (t - that piece's start offset) / (kCostBase + g).
 __device__ __forceinline__ void write_tile(int32_t *sched, int C, long long T, long long carry, long long tile_total,
-                                           int base, const SchedShared &sh) {
+                                           int base, int n_tile, const SchedShared &sh) {
     const long long qC = T / C, rC = T % C;
     const long long lo = first_chunk_at(carry, T, qC, rC, C);
     const long long hi = first_chunk_at(carry + tile_total, T, qC, rC, C);
     // the workgroups take consecutive equal shares of [lo, hi), so each writes whole lines
     const long long per = (hi - lo + gridDim.x - 1) / gridDim.x;
     const long long c0 = lo + per * blockIdx.x, c1 = c0 + per < hi ? c0 + per : hi;
+    // (incl of the rows past the last live one equals the tile's total, which
+    // no chunk start in the tile reaches)
+    const int live = min(kSchedThreads, n_tile);
     for (long long c = c0 + threadIdx.x; c < c1; c += kSchedThreads) {
         const long long t = chunk_start(c, qC, rC, C);
-        int l = 0, h = kSchedThreads - 1;
+        int l = 0, h = live - 1;
         while (l < h) {
             const int m = (l + h) >> 1;
             if (sh.incl[m] > t)
@@ -173,7 +201,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
                 sched[2 * W] = n;
                 sched[2 * W + 1] = 0;
             }
-            write_tile(sched, W, total, 0, total, 0, sh);
+            write_tile(sched, W, total, 0, total, 0, n, sh);
             return;
         }
     } else {
@@ -206,7 +234,7 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(RowView v, int 
                 sh.gs[tid] = g;
                 __syncthreads();
                 const long long tile_total = sh.incl[kSchedThreads - 1] - carry;
-                write_tile(sched, W, total, carry, tile_total, base, sh);
+                write_tile(sched, W, total, carry, tile_total, base, n - base, sh);
                 __syncthreads();
                 if (tid == kSchedThreads - 1) sh.cost_carry = carry + tile_total;
                 __syncthreads();

@@ -42,7 +42,7 @@ def test_schedule_varlen_matches_spec(seed):
     lens = np.concatenate([np.maximum(c - n + np.arange(n) + 1, 0) for c, n in zip(ctx, runs)])
     ids = np.repeat(rng.permutation(R) % max(1, R // 2), runs)
     G.banner(f"schedule varlen seed={seed} rows={len(lens)}")
-    for W in (1, 7, 256, 512, 3000):
+    for W in (1, 7, 256, 512, 3000, 50000):  # (chunk offsets in 32-bit arithmetic up to 46340 workers)
         _sched_case(lens, 1, ids, int(rng.choice([32, 64])), W)
 
 
