@@ -502,6 +502,27 @@ def calibration_copy(nbytes: int) -> None:
     del src, dst
 
 
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """The achievable HBM rate on this machine: a device-to-device copy of nbytes
+    (larger than the 256 MB MALL), bytes read plus written over the median time."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del src, dst
+    return {"copy_GBs": round(2 * nbytes / ms / 1e6, 1), "copy_bytes": nbytes, "ms_median": round(ms, 4),
+            "note": "device-to-device copy, read + write bytes over the median of %d events" % reps}
+
+
 OTHERS = {"uniform_decode_fp8_32k": run_uniform, "varlen_spec_decode_mxfp4_64k": run_mxfp4,
           "varlen_spec_decode_mxfp4_64k_fp4q": run_mxfp4_fp4q, "tiny_decode_fp8": run_tiny,
           "varlen_spec_decode_fp8_120k_bf16": run_bf16, "varlen_spec_decode_fp8_120k_fused": run_fused,
@@ -571,6 +592,9 @@ def main():
     calibration_copy(args.copy_calibration)
     del b
     torch.cuda.empty_cache()
+    ach = copy_bandwidth()
+    line["roofline"]["achievable"] = ach
+    line["roofline"]["frac_of_achievable"] = round(line["roofline"]["achieved"] / ach["copy_GBs"], 4)
     if not args.no_grouping:
         print("[bench] the same rows without request grouping (indices = arange)", file=sys.stderr, flush=True)
         line["varlen_grouping"] = grouping_comparison(case, args.steps, args.warmup, args.copies)
