@@ -279,58 +279,69 @@ __device__ __forceinline__ void stage_pieces(const uint8_t *codes, const uint8_t
     }
 }
 
-// u[d] = sum_h w_h q_h[d] (fp32, heads in order) of the staged rows 0 .. g-1
-// and its four pieces, written to the LDS image (s_u, s_us). Piece p of a
-// 32-element block takes the e8m0 scale 2^e with e = floor(log2 m) - 7 for the
-// largest magnitude m of what the earlier pieces left (so its codes stay
-// below 256, within e4m3), rounds the rest over 2^e to fp8 and subtracts the
-// rounded value, which is exact in fp32. Each piece removes about 4 significant
-// bits, so after four the remainder is about 2^-16 of the element or less.
+// u[d] = sum_h w_h q_h[d] (fp32) of the staged rows 0 .. g-1 and its four
+// pieces, written to the LDS image (s_u, s_us). Threads 0..255 run it, one row
+// at a time: thread 8 dq + hp sums heads 8 hp .. 8 hp + 7 (in order) of
+// elements 4 dq .. 4 dq + 3, and the 8 head parts of an element are added by
+// lanes xor 1, 2, 4 (every lane of the group gets the same bits), so each row
+// costs 8 dependent steps per thread instead of 64. Every path that derives
+// pieces uses this order, so a row's pieces do not depend on which kernel made
+// them. Piece p of a 32-element block (one wave: dq 8c .. 8c + 7) takes the
+// e8m0 scale 2^e with e = floor(log2 m) - 7 for the largest magnitude m of what
+// the earlier pieces left (so its codes stay below 256, within e4m3), rounds
+// the rest over 2^e to fp8 and subtracts the rounded value, which is exact in
+// fp32. Each piece removes about 4 significant bits, so after four the
+// remainder is about 2^-16 of the element or less.
 // Q4: q is fp4 (values and e8m0 scales, stage_rows_q4's image).
-// The workgroup (NTH threads) runs it; callers put a barrier between the
-// staging of q / w and this, and between this and reads of the image.
+// Callers put a barrier between the staging of q / w and this, and between
+// this and reads of the image.
 template <bool Q4, int NTH = kLThreads>
 __device__ __forceinline__ void derive_pieces(const uint8_t *s_q, const float *s_w, int g, uint8_t *s_u,
                                               uint8_t *s_us) {
-    static_assert(NTH % 32 == 0, "32 threads per row");
+    static_assert(NTH >= 256, "256 threads per row");
     const int tid = threadIdx.x;
-    for (int it = tid; it < kGMax * 32; it += NTH) {
-        const int row = it >> 5, dq = it & 31;  // elements d = 4 dq .. 4 dq + 3 of row `row`
-        const bool live = row < g;
+    if (tid >= 256) return;
+    const int dq = tid >> 3, hp = tid & 7;  // elements 4 dq .. 4 dq + 3, heads 8 hp .. 8 hp + 7
+    for (int row = 0; row < g; ++row) {
+        const uint8_t *qr = s_q + row * kQBytes;
+        const float *wr = s_w + row * PML_HEADS;
         float u[4] = {0.f, 0.f, 0.f, 0.f};
-        if (live) {
-            const uint8_t *qr = s_q + row * kQBytes;
-            const float *wr = s_w + row * PML_HEADS;
-#pragma unroll 8
-            for (int h = 0; h < PML_HEADS; ++h) {
-                const float wh = lds_ld<float>(wr + h);
-                float qv[4];
-                if constexpr (Q4) {
-                    const int c = dq >> 3;  // 32-element block
-                    const int sb = lds_ld<uint8_t>(qr + kQ4Values + 4 * h + c);
-                    const float sc = sb == 255 ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(1.0f, sb - 127);
-                    const uint32_t two = lds_ld<uint16_t>(qr + q4_lds_off(h, c) + 2 * (dq & 7));
-                    const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 0);
-                    const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 1);
-                    qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
-                } else {
-                    const uint32_t four = lds_ld<uint32_t>(qr + q_lds_off(h, dq >> 2) + 4 * (dq & 3));
-                    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(four, false);
-                    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(four, true);
-                    qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
-                }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) u[j] = __builtin_fmaf(wh, qv[j], u[j]);
+        for (int j = 0; j < 8; ++j) {
+            const int h = 8 * hp + j;
+            const float wh = lds_ld<float>(wr + h);
+            float qv[4];
+            if constexpr (Q4) {
+                const int c = dq >> 3;  // 32-element block
+                const int sb = lds_ld<uint8_t>(qr + kQ4Values + 4 * h + c);
+                const float sc = sb == 255 ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(1.0f, sb - 127);
+                const uint32_t two = lds_ld<uint16_t>(qr + q4_lds_off(h, c) + 2 * (dq & 7));
+                const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 0);
+                const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, sc, 1);
+                qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
+            } else {
+                const uint32_t four = lds_ld<uint32_t>(qr + q_lds_off(h, dq >> 2) + 4 * (dq & 3));
+                const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(four, false);
+                const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(four, true);
+                qv[0] = lo[0]; qv[1] = lo[1]; qv[2] = hi[0]; qv[3] = hi[1];
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = __builtin_fmaf(wh, qv[e], u[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[e] += __shfl_xor(u[e], 1, kWave);
+            u[e] += __shfl_xor(u[e], 2, kWave);
+            u[e] += __shfl_xor(u[e], 4, kWave);
         }
 #pragma unroll
         for (int p = 0; p < kPieces; ++p) {
             float m = fmaxf(fmaxf(__builtin_fabsf(u[0]), __builtin_fabsf(u[1])),
                             fmaxf(__builtin_fabsf(u[2]), __builtin_fabsf(u[3])));
-            // the 8 threads of a 32-element block are 8 consecutive lanes
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            // the 8 elements-of-4 of a 32-element block are lanes xor 8, 16, 32 of one wave
+            m = fmaxf(m, __shfl_xor(m, 8, kWave));
+            m = fmaxf(m, __shfl_xor(m, 16, kWave));
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
             int e = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 8 : -127;  // m in [2^(e+7), 2^(e+8))
             e = max(e, -127);
             const float inv = __builtin_amdgcn_ldexpf(1.0f, -e);
@@ -342,7 +353,7 @@ __device__ __forceinline__ void derive_pieces(const uint8_t *s_q, const float *s
             u[1] -= __builtin_amdgcn_ldexpf(d01[1], e);
             u[2] -= __builtin_amdgcn_ldexpf(d23[0], e);
             u[3] -= __builtin_amdgcn_ldexpf(d23[1], e);
-            if (live) {
+            if (hp == 0) {
                 const int ph = kPieces * row + p;  // pseudo-head
                 lds_st<int>(s_u + q_lds_off(ph, dq >> 2) + 4 * (dq & 3), codes);
                 if ((dq & 7) == 0) lds_st<uint8_t>(s_us + ph * 4 + (dq >> 3), (uint8_t)(e + 127));

@@ -384,14 +384,15 @@ __device__ __forceinline__ void range_split(const PagedArgs &a, int block_kv, in
     }
 }
 
-// First kernel of every logits call. Workgroups [0, ceil(rows / kGMax)):
-// the pieces of u = sum_h w_h q_h for kGMax rows each, written to the
-// workspace for the logits kernel to stage with q. The following workgroups:
-// one split point per range (a thread each), and the pool counters set to zero.
+// First kernel of every logits call. Workgroups [0, rows): the pieces of
+// u = sum_h w_h q_h of one row each (a short chain per workgroup: the row's q
+// staged, 8 head steps per thread, the pieces written), to the workspace for
+// the logits kernel to stage with q. The following workgroups: one split point
+// per range (a thread each), and the pool counters set to zero.
 template <bool Q4>
 __global__ __launch_bounds__(kPThreads) void pieces_kernel(PagedArgs a, uint8_t *codes, uint8_t *scales,
                                                            int block_kv, int W) {
-    const int nrow_wg = (a.rows.num_rows + kGMax - 1) / kGMax;
+    const int nrow_wg = a.rows.num_rows;
     if ((int)blockIdx.x >= nrow_wg) {
         const int e = (blockIdx.x - nrow_wg) * kPThreads + threadIdx.x;
         if (e < W) {
@@ -403,12 +404,12 @@ __global__ __launch_bounds__(kPThreads) void pieces_kernel(PagedArgs a, uint8_t 
         if (blockIdx.x == nrow_wg && threadIdx.x < kPools) a.pools[kPoolStride * threadIdx.x] = 0;
         return;
     }
-    __shared__ __attribute__((aligned(16))) uint8_t s_q[kGMax * kQBytes];
-    __shared__ __attribute__((aligned(16))) float s_w[kGMax * PML_HEADS];
-    __shared__ __attribute__((aligned(16))) uint8_t s_u[kGMax * kUBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t s_us[kGMax * kUScales];
-    const int r0 = blockIdx.x * kGMax;
-    const int g = min(kGMax, a.rows.num_rows - r0);
+    __shared__ __attribute__((aligned(16))) uint8_t s_q[kQBytes];
+    __shared__ __attribute__((aligned(16))) float s_w[PML_HEADS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_u[kUBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t s_us[kUScales];
+    const int r0 = blockIdx.x;
+    const int g = 1;
     if constexpr (Q4)
         stage_rows_q4<kPThreads>(a.q, a.qs, a.w, r0, g, s_q, s_w);
     else
@@ -592,7 +593,7 @@ static int prepare_paged(pml::PagedArgs &a, bool &empty, const void *q, const ui
 // The first kernel of each logits call: every row's pieces, every range's
 // split point and zeroed pool counters, into the workspace.
 static int launch_pieces(const pml::PagedArgs &a, int block_kv, int W, hipStream_t st) {
-    const dim3 grid((a.rows.num_rows + pml::kGMax - 1) / pml::kGMax + (W + pml::kPThreads - 1) / pml::kPThreads);
+    const dim3 grid(a.rows.num_rows + (W + pml::kPThreads - 1) / pml::kPThreads);
     uint8_t *codes = (uint8_t *)a.ucodes, *scales = (uint8_t *)a.uscales;
     if (a.qs)
         hipLaunchKernelGGL(pml::pieces_kernel<true>, grid, dim3(pml::kPThreads), 0, st, a, codes, scales, block_kv, W);
