@@ -599,6 +599,11 @@ def main():
         print("[bench] the same rows without request grouping (indices = arange)", file=sys.stderr, flush=True)
         line["varlen_grouping"] = grouping_comparison(case, args.steps, args.warmup, args.copies)
         torch.cuda.empty_cache()
+        # the ungrouped call reads 3.4x the bytes with the same kernel: its rate shows what this
+        # read pattern reaches when nothing else limits it, a higher bar than the copy
+        ach["read_GBs_ungrouped_call"] = line["varlen_grouping"]["arange"]["hbm_GBs"]
+        line["roofline"]["frac_of_achievable"] = round(
+            line["roofline"]["achieved"] / max(ach["copy_GBs"], ach["read_GBs_ungrouped_call"]), 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
