@@ -111,7 +111,10 @@ __device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g
     const int lane = lane_id();
     const int s = b * 64 + lane;
     const float scale = 0.5f * __uint_as_float(kc.sc[0]);  // 1/2: see score_row
-    for (int q0 = 0; q0 < g; q0 += 4) {
+    // (both quads unrolled: the rows' LDS operand addresses become immediates)
+#pragma unroll
+    for (int q0 = 0; q0 < kGMax; q0 += 4) {
+        if (q0 >= g) break;
         float M[4];
 #pragma unroll
         for (int G = 0; G < 4; ++G) {
@@ -123,7 +126,8 @@ __device__ __forceinline__ void ragged_step(const RaggedArgs &a, int row0, int g
                                                                         s_u, s_us, q0 >> 2, M)
                                     : score_row<false, 64>(kc, s_q + i * kQBytes, s_w + i * PML_HEADS);
             float v = (sr + M[G]) * scale;
-            if (s < lo || s >= hi) v = -__builtin_inff();
+            if (b * 64 < lo || b * 64 + 64 > hi)  // (wave-uniform: only blocks that cross a bound are masked)
+                if (s < lo || s >= hi) v = -__builtin_inff();
             lds_st<float>(&sl.v[i][lane], v);
         }
     }
