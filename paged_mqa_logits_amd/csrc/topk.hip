@@ -9,7 +9,7 @@
 // ascending without a sort:
 //  * When every row has at most 8192 columns (max_width <= 8192) a compact
 //    256-thread kernel holds the row's keys in registers and selects there
-//    (topk_small_kernel: 8.7 KB of LDS, six rows per CU).
+//    (topk_small_kernel: 8.7 KB of LDS and 48 VGPRs per 256-thread row).
 //  * Otherwise a row that fits the LDS candidate list is read once into it.
 //  * A row of 16K columns or more first takes a sampled pass: a histogram of
 //    the top 11 key bits over each wave's first 512 positions (16 places
@@ -695,8 +695,8 @@ __device__ __forceinline__ uint32_t held_key(float f) {
 
 // Rows of at most 8192 columns (max_width <= 8192): each thread holds the keys
 // of positions j * NT + tid (j < 32) in registers, loaded together, so the
-// row costs one memory round trip. The kernel is bound by VALU issue (six rows
-// per CU), so the per-key work is kept small:
+// row costs one memory round trip. The kernel is bound by VALU issue (several
+// rows share a CU), so the per-key work is kept small:
 //  * A held key is the order key plus one, and 0 for a slot past the row's
 //    end (the order key of -inf is 0x007fffff, so 1, a NaN, and 0 sit below
 //    every number). Validity is then decided once, when the key is formed.
