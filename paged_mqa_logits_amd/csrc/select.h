@@ -125,6 +125,45 @@ __device__ __forceinline__ void pick_bin_by(C count, int nbins, uint32_t kk, uin
     __syncthreads();
 }
 
+// pick_bin for nbins = NT * PER (PER 2, 4 or 8): thread t's bins, the PER
+// consecutive ones ending at nbins - t * PER, read once with 8- or 16-byte
+// loads and kept in registers for both the sum and the search (pick_bin reads
+// each bin twice, one word at a time). Same result as pick_bin.
+template <int NT, int PER>
+__device__ __forceinline__ void pick_bin_vec(const uint32_t *s_hist, uint32_t kk, uint32_t *s_wave,
+                                             uint32_t *s_pick) {
+    static_assert(PER == 2 || PER == 4 || PER == 8, "8- or 16-byte loads");
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const int base = (NT - 1 - (int)threadIdx.x) * PER;  // bins [base, base + PER)
+    uint32_t h[PER];
+    if constexpr (PER == 2) {
+        const u2 v = *(const u2 *)(s_hist + base);
+        h[0] = v[0];
+        h[1] = v[1];
+    } else {
+#pragma unroll
+        for (int c = 0; c < PER / 4; ++c) {
+            const u4 v = *(const u4 *)(s_hist + base + 4 * c);
+            h[4 * c] = v[0]; h[4 * c + 1] = v[1]; h[4 * c + 2] = v[2]; h[4 * c + 3] = v[3];
+        }
+    }
+    uint32_t own = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) own += h[j];
+    uint32_t tot;
+    uint32_t above = block_scan<NT>(own, s_wave, &tot) - own;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {  // descending bins
+        if (above < kk && kk <= above + h[j]) {
+            s_pick[0] = (uint32_t)(base + j);
+            s_pick[1] = above;
+        }
+        above += h[j];
+    }
+    __syncthreads();
+}
+
 template <int NT>
 __device__ __forceinline__ void pick_bin(const uint32_t *s_hist, int nbins, uint32_t kk, uint32_t *s_wave,
                                          uint32_t *s_pick) {

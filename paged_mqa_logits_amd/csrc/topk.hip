@@ -263,7 +263,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         __syncthreads();
         // the bucket of the t-th largest sampled key: 1.5 k scaled to the sample, + 16
         const uint32_t t = (uint32_t)((3ull * (uint64_t)k * ns) / (2ull * (uint64_t)n)) + 16;
-        pick_bin<NT>(s_hist, kBins, t, s_wave, s_pick);
+        pick_bin_vec<NT, kBins / NT>(s_hist, t, s_wave, s_pick);
         const uint32_t sprefix = s_pick[0] << 21;
         // one pass: ordered append into the wave's region [wave * RCAP, +RCAP).
         // Above the key of -inf the bucket test is one float compare per
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                 if (ok[e]) atomicAdd(&s_hist[key[e] >> 21], 1u);
         });
         __syncthreads();
-        pick_bin<NT>(s_hist, kBins, kk, s_wave, s_pick);
+        pick_bin_vec<NT, kBins / NT>(s_hist, kk, s_wave, s_pick);
         prefix = s_pick[0] << 21;
         mask = 0x7ffu << 21;
         kk -= s_pick[1];
@@ -446,7 +446,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                     if (u < nh && lane + u * kWave < rcnt && (rk[u] & mask) == prefix)
                         atomicAdd(&s_hist[(rk[u] >> shift) & (nbins - 1)], 1u);
                 __syncthreads();
-                pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+                if (nbins == kBins)
+                    pick_bin_vec<NT, kBins / NT>(s_hist, kk, s_wave, s_pick);
+                else
+                    pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
                 const uint32_t cnt = s_hist[s_pick[0]];
                 prefix |= s_pick[0] << shift;
                 mask |= (uint32_t)(nbins - 1) << shift;
@@ -571,7 +574,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                     if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
                 }
                 __syncthreads();
-                pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+                if (nbins == kBins)
+                    pick_bin_vec<NT, kBins / NT>(s_hist, kk, s_wave, s_pick);
+                else
+                    pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
                 const uint32_t cnt = s_hist[s_pick[0]];
                 prefix |= s_pick[0] << shift;
                 mask |= (uint32_t)(nbins - 1) << shift;
@@ -626,7 +632,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
                 if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
             }
             __syncthreads();
-            pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+            if (nbins == kBins)
+                    pick_bin_vec<NT, kBins / NT>(s_hist, kk, s_wave, s_pick);
+                else
+                    pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
             prefix |= s_pick[0] << shift;
             mask |= (uint32_t)(nbins - 1) << shift;
             kk -= s_pick[1];
@@ -791,7 +800,10 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
             if (tid == 0 && prefix == 0 && empty) atomicSub(&s_hist[0], empty);
             __syncthreads();
         }
-        pick_bin<NT>(s_hist, nbins, kk, s_wave, s_pick);
+        if (pass < 2)
+            pick_bin_vec<NT, kBins / NT>(s_hist, kk, s_wave, s_pick);
+        else
+            pick_bin_vec<NT, kBins / 2 / NT>(s_hist, kk, s_wave, s_pick);
         cnt = s_hist[s_pick[0]];
         prefix |= s_pick[0] << shift;
         mask |= (uint32_t)(nbins - 1) << shift;
