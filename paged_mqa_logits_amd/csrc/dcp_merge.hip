@@ -74,9 +74,9 @@ __device__ __forceinline__ void select_k_ids(const uint32_t (&key)[P], const int
                                              int k, int32_t *out_row) {
     constexpr int NT = kMergeThreads;
     constexpr int NS = kSortThreads * E;  // sorted entries (>= k)
-    __shared__ uint32_t s_hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2048];
     __shared__ int32_t s_ids[NS];
-    __shared__ uint32_t s_wave[kMergeWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wave[kMergeWaves];
     __shared__ uint32_t s_pick[2];
     __shared__ uint32_t s_nsel;
     const int tid = threadIdx.x;
@@ -227,8 +227,8 @@ __global__ __launch_bounds__(kMergeThreads) void cand_select_kernel(CandSelectAr
     constexpr int PB = kSelectMaxBlocks / NT;  // blocks per thread in the scan
     __shared__ int32_t s_off[kSelectMaxBlocks + 1];
     __shared__ uint16_t s_blk[P * NT];  // block of each candidate
-    __shared__ uint32_t s_hist[2048];
-    __shared__ uint32_t s_wave[2 * kMergeWaves];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wave[2 * kMergeWaves];
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
     const int r = blockIdx.x;

@@ -452,8 +452,8 @@ __global__ __launch_bounds__(kThThreads) void threshold_kernel(PagedArgs a, int 
     __shared__ __attribute__((aligned(16))) uint8_t s_u[kUBytes];
     __shared__ __attribute__((aligned(16))) uint8_t s_us[kUScales];
     __shared__ uint32_t s_key[kSampleTokens];
-    __shared__ uint32_t s_hist[2048];
-    __shared__ uint32_t s_wave[NW];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wave[NW];
     __shared__ uint32_t s_pick[2];
     const int r = blockIdx.x;
     const int tid = threadIdx.x;

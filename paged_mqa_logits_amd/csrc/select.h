@@ -128,7 +128,8 @@ __device__ __forceinline__ void pick_bin_by(C count, int nbins, uint32_t kk, uin
 // pick_bin for nbins = NT * PER (PER 2, 4 or 8): thread t's bins, the PER
 // consecutive ones ending at nbins - t * PER, read once with 8- or 16-byte
 // loads and kept in registers for both the sum and the search (pick_bin reads
-// each bin twice, one word at a time). Same result as pick_bin.
+// each bin twice, one word at a time). Same result as pick_bin. s_hist must be
+// 16-byte aligned.
 template <int NT, int PER>
 __device__ __forceinline__ void pick_bin_vec(const uint32_t *s_hist, uint32_t kk, uint32_t *s_wave,
                                              uint32_t *s_pick) {

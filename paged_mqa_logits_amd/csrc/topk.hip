@@ -176,11 +176,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     using Cfg = TopkCfg<NT>;
     constexpr int NW = Cfg::NW;
     constexpr int CAP = Cfg::CAP;
-    __shared__ uint32_t s_hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kBins];
     __shared__ uint32_t s_list[2 * CAP];  // keys, then positions: one array, so an entry's
     uint32_t *const s_key = s_list;       // two stores share an address
     int32_t *const s_pos = (int32_t *)(s_list + CAP);
-    __shared__ uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
+    __shared__ __attribute__((aligned(16))) uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
     __shared__ uint32_t s_small[kWave];  // the keys of a small picked bin
@@ -728,9 +728,9 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int kChunks = kPer * NW;   // 64-position chunks of a full row
     static_assert(kChunks <= NT, "one chunk count per thread in the scan");
     static_assert(kPer <= kWave, "one chunk count per lane of a wave");
-    __shared__ uint32_t s_hist[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kBins];
     __shared__ uint32_t s_base[kChunks];  // first output slot of each chunk (packed greater | equal << 16 on ties)
-    __shared__ uint32_t s_wave[NW];
+    __shared__ __attribute__((aligned(16))) uint32_t s_wave[NW];
     __shared__ uint32_t s_pick[2];
     const int tid = threadIdx.x;
     const int lane = lane_id();
