@@ -293,16 +293,20 @@ __device__ __forceinline__ void stage_pieces(const uint8_t *codes, const uint8_t
 // fp32. Each piece removes about 4 significant bits, so after four the
 // remainder is about 2^-16 of the element or less.
 // Q4: q is fp4 (values and e8m0 scales, stage_rows_q4's image).
+// With NTH >= 512 the rows are taken NTH / 256 at a time (thread t serves
+// rows t / 256, t / 256 + NTH / 256, ...), each in the same order.
 // Callers put a barrier between the staging of q / w and this, and between
 // this and reads of the image.
 template <bool Q4, int NTH = kLThreads>
 __device__ __forceinline__ void derive_pieces(const uint8_t *s_q, const float *s_w, int g, uint8_t *s_u,
                                               uint8_t *s_us) {
     static_assert(NTH >= 256, "256 threads per row");
+    constexpr int kPar = NTH / 256;  // rows at a time
     const int tid = threadIdx.x;
-    if (tid >= 256) return;
-    const int dq = tid >> 3, hp = tid & 7;  // elements 4 dq .. 4 dq + 3, heads 8 hp .. 8 hp + 7
-    for (int row = 0; row < g; ++row) {
+    if (tid >= 256 * kPar) return;
+    const int t8 = tid & 255;
+    const int dq = t8 >> 3, hp = t8 & 7;  // elements 4 dq .. 4 dq + 3, heads 8 hp .. 8 hp + 7
+    for (int row = tid >> 8; row < g; row += kPar) {
         const uint8_t *qr = s_q + row * kQBytes;
         const float *wr = s_w + row * PML_HEADS;
         float u[4] = {0.f, 0.f, 0.f, 0.f};
@@ -523,7 +527,7 @@ __device__ __forceinline__ float score_row(const KeyRegs<FP4, BKV> &k_, const ui
     // LDS operands in the order of use (the linear half's, then head tile 0,
     // 1, ...): compiler barriers keep the reads in this order, so each MFMA
     // waits only for the reads before it
-    [[maybe_unused]] v8i al;
+    [[maybe_unused]] v8i al = {};
     int sl = 0;
     if constexpr (LIN) {
         al = load_a<false>(s_u, m);

@@ -112,7 +112,6 @@ __device__ __forceinline__ void wave_step(const PagedArgs &a, int r0, int g, int
                                           int &okp, const uint8_t *s_q, const float *s_w, const uint8_t *s_u,
                                           const uint8_t *s_us, int vis_lane, WaveSlot<BKV> &sl, int &mask,
                                           int &col0p, const float *s_th) {
-    using C = BlockCfg<FP4, BKV>;
     touch<FP4, BKV>(kc);
     flush_slot<BKV, OT>(sl, mask, r0, col0p, a.max_ctx, (OT *)a.out, a.out_ld);
     if constexpr (PF) okp = fetch_block<FP4, BKV, PG>(a, bt_row, bp, kp);

@@ -312,10 +312,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         }
         if (lane == 0) s_wcnt[wave] = cnt;
         __syncthreads();
-        uint32_t base = 0, total = 0, over = 0;
+        uint32_t total = 0, over = 0;
         for (int w = 0; w < NW; ++w) {
             const uint32_t c = s_wcnt[w];
-            if (w < wave) base += c;
             total += c;
             over |= c > (uint32_t)RCAP;
         }
