@@ -17,18 +17,19 @@
 // the epilogue, not the matrix core, set the speed of the two-instruction
 // ReLU-and-weight form.
 //
-// Work split (gfx950): a workgroup of 4 waves scores a row-piece (up to kGMax
-// rows of one request) against key blocks; q and w of the piece sit in LDS,
-// shared by the 4 waves. Each wave takes whole key blocks on its own: the
-// block's keys go from HBM straight into VGPRs, already laid out as the B
-// operand of v_mfma_f32_16x16x128_f8f6f4 (lane l holds token l % 16 of a
-// 16-token slice), two buffers deep so one block is in flight while one is
-// scored. For every row the wave runs 4 head tiles x (BKV / 16) token
-// slices of MFMAs, folds ReLU and w into per-lane partial sums in registers,
-// and a transpose-reduce with v_permlane32/16_swap leaves one finished token
-// per lane; the block's logits wait in LDS and go out as coalesced
-// 4-byte-per-lane row segments one step later. No barrier is taken per
-// block, only at piece changes.
+// Work split of the paged kernel (gfx950; the ragged kernel instead gives each
+// wave one row, see ragged_logits.hip): a workgroup of 4 waves scores a
+// row-piece (up to kGMax rows of one request) against key blocks; q and w of
+// the piece sit in LDS, shared by the 4 waves. Each wave takes whole key
+// blocks on its own: the block's keys go from HBM straight into VGPRs,
+// already laid out as the B operand of v_mfma_f32_16x16x128_f8f6f4 (lane l
+// holds token l % 16 of a 16-token slice), two buffers deep so one block is
+// in flight while one is scored. For every row the wave runs 4 head tiles x
+// (BKV / 16) token slices of MFMAs, folds ReLU and w into per-lane partial
+// sums in registers, and a transpose-reduce with v_permlane32/16_swap leaves
+// one finished token per lane; the block's logits wait in LDS and go out one
+// step later as coalesced row segments, 16 bytes per lane and four rows per
+// store instruction. No barrier is taken per block, only at piece changes.
 #pragma once
 
 #include "pml_device.h"
