@@ -13,8 +13,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 constexpr int kWave = 64;
 #ifndef PML_GMAX
 #define PML_GMAX 8
@@ -34,48 +32,9 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 
 // Workgroup barrier that only orders LDS: waits for this wave's LDS traffic,
 // then s_barrier. Unlike __syncthreads it does not drain outstanding global
-// loads, so direct-to-LDS prefetches stay in flight across it.
+// loads, so key blocks requested ahead stay in flight across it.
 __device__ __forceinline__ void barrier_lds() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// LDS reads the compiler does not track: it would otherwise drain every
-// direct-to-LDS load in flight before each read. Callers wait with
-// wait_lgkm0() before using the results.
-__device__ __forceinline__ v4i lds_read_b128(uint32_t addr) {
-    v4i r;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-    return r;
-}
-__device__ __forceinline__ uint32_t lds_read_u8(uint32_t addr) {
-    uint32_t r;
-    asm volatile("ds_read_u8 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-    return r;
-}
-__device__ __forceinline__ float lds_read_f32(uint32_t addr) {
-    float r;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-    return r;
-}
-
-__device__ __forceinline__ int lds_read_i32(uint32_t addr) {
-    int r;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(r) : "v"(addr) : "memory");
-    return r;
-}
-__device__ __forceinline__ void lds_write_f32(uint32_t addr, float v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
-}
-__device__ __forceinline__ void lds_write_i32(uint32_t addr, int v) {
-    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 // Plain (compiler-tracked) loads from LDS through a generic pointer that
@@ -88,21 +47,6 @@ __device__ __forceinline__ T lds_ld(const void *p) {
 template <typename T>
 __device__ __forceinline__ void lds_st(void *p, T v) {
     *(__attribute__((address_space(3))) T *)(__attribute__((address_space(3))) void *)p = v;
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const lds_void *)p;
-}
-
-// 16 bytes per lane from global memory straight into LDS; the wave's 64 lanes
-// fill 1 KB starting at lds_wave_base (lane i at +16 i).
-__device__ __forceinline__ void dma16(const void *gsrc, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 16, 0, 0);
-}
-
-// 4 bytes per lane from global memory straight into LDS (lane i at +4 i).
-__device__ __forceinline__ void dma4(const void *gsrc, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(gsrc, (lds_void *)lds_wave_base, 4, 0, 0);
 }
 
 // D = A(16x128 fp8) * B(128x16 fp8), fresh accumulator (unscaled opcode).
@@ -139,12 +83,6 @@ __device__ __forceinline__ void swap16(float &x, float &y) {
     auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(y), false, false);
     x = __int_as_float(r[0]);
     y = __int_as_float(r[1]);
-}
-
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-    return v;
 }
 
 }  // namespace pml
