@@ -22,7 +22,7 @@ with the host's core count and CPU model.
 
 --all adds one line per further workload, each timed the same way: uniform
 decode, MXFP4 keys, MXFP4 keys with fp4 q, the tiny decode, the 120K decode
-with bf16 logits plus the upcast, the fused logits + top-k call, the exact
+with bf16 logits (the top-k reads them directly), the fused logits + top-k call, the exact
 top-k merge over 8 context-parallel ranks, and ragged prefill logits.
 """
 from __future__ import annotations
@@ -91,8 +91,7 @@ def parse():
 
 class PagedBench:
     """Device copies of one paged case and the three calls of one step. With bf16,
-    the logits are written as bf16 and upcast over each row's span for the top-k
-    (four calls)."""
+    the logits are written as bf16 and the top-k reads them as they are."""
 
     def __init__(self, case: syn.PagedCase, copies: int, num_cus: int | None = None, bf16: bool = False,
                  fused: bool = False):
@@ -111,7 +110,7 @@ class PagedBench:
         self.logits = torch.empty(case.rows, pml.logits_ld(case.max_ctx), dtype=torch.float32, device=d)
         self.bf16 = bf16
         self.fused = fused
-        self.nev = 5 if bf16 else (3 if fused else 4)
+        self.nev = 3 if fused else 4
         if fused:
             need = pml.fused_topk_workspace_size(case.rows, case.max_ctx, case.block_kv, case.topk, self.num_cus)
             self.ws = torch.empty(need, dtype=torch.uint8, device=d)
@@ -119,7 +118,6 @@ class PagedBench:
             assert case.next_n == 1
             ld = (case.max_ctx + 7) // 8 * 8
             self.logits_bf16 = torch.empty(case.rows, ld, dtype=torch.bfloat16, device=d)
-            self.logits = torch.empty(case.rows, ld, dtype=torch.float32, device=d)
         self.topk = torch.empty(case.rows, case.topk, dtype=torch.int32, device=d)
         self.req_tokens = int(sum(case.req_ctx))
         self.pairs = syn.scored_pairs(case)
@@ -146,11 +144,8 @@ class PagedBench:
                                      q_scale=self.q_scale, workspace=self.ws)
         if ev is not None:
             ev[2].record()
-        if self.bf16:
-            pml.as_fp32_logits(self.logits_bf16, self.lens, out=self.logits, cols=c.max_ctx)
-            if ev is not None:
-                ev[3].record()
-        pml.top_k_per_row(self.logits, self.lens, c.topk, next_n=c.next_n, max_width=c.max_ctx, out=self.topk)
+        pml.top_k_per_row(self.logits_bf16 if self.bf16 else self.logits, self.lens, c.topk, next_n=c.next_n,
+                          max_width=c.max_ctx, out=self.topk)
         if ev is not None:
             ev[self.nev - 1].record()
 
@@ -446,7 +441,7 @@ def run_bf16(args):
     kbytes = ob.req_tokens * BYTES_PER_TOKEN[c.kv_format]
     return {"workload": "varlen_spec_decode_fp8_120k_bf16_logits", "ms_per_step": w2 / args.steps * 1e3,
             "ms_schedule": float(p2[:, 0].mean()), "ms_logits": t_log * 1e3,
-            "ms_upcast": float(p2[:, 2].mean()), "ms_topk": float(p2[:, 3].mean()),
+            "ms_topk": float(p2[:, 2].mean()),
             "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
             "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
             "logits_out_bytes": c.rows * c.max_ctx * 2}

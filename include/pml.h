@@ -234,6 +234,24 @@ int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const in
                   int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * top_k_per_row_bf16 - top_k_per_row over bf16 logits (as
+ * fp8_fp4_paged_mqa_logits_bf16 writes them; the SM100 kernel's logits dtype,
+ * sparse_attn_indexer page, the logits buffer of _varlen_decode_rows), with no
+ * fp32 copy in between.
+ *
+ *   logits     bf16 bits [num_rows][logits_ld] (uint16_t), 16-B aligned,
+ *              logits_ld a multiple of 8 (else PML_ERR_ALIGN /
+ *              PML_ERR_STRIDE).
+ *
+ * Every other argument, check and result is as for top_k_per_row: the
+ * selection is that of top_k_per_row over the exact fp32 values of the bf16
+ * logits (as_fp32_logits), bit for bit.
+ */
+int top_k_per_row_bf16(const uint16_t *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
+                       const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
+                       int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * fp8_fp4_paged_mqa_logits_noalloc - fp8_fp4_paged_mqa_logits without the
  * workspace arguments, for callers that cannot allocate device memory (code
  * under graph capture, tight serving loops, harnesses that forbid it). The

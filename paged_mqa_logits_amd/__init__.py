@@ -83,11 +83,13 @@ def lib() -> ctypes.CDLL:
             L.top_k_per_row_workspace_size.argtypes = [I, I, I]
             L.top_k_per_row_workspace_size.restype = SZ
             L.top_k_per_row.argtypes = [P, I, I64, P, P, I, I, I, P, I64, P, SZ, P]
+        if hasattr(L, "top_k_per_row_bf16"):
+            L.top_k_per_row_bf16.argtypes = L.top_k_per_row.argtypes
         if hasattr(L, "stable_topk_from_gathered_candidates"):
             L.pack_dcp_topk_candidates.argtypes = [P, I, I64, P, P, I64, I, I, I, I, P, P]
             L.stable_topk_from_gathered_candidates.argtypes = [P, I, I, I, P, I64, P]
         for name in ("paged_mqa_logits_metadata", "fp8_fp4_paged_mqa_logits", "mqa_logits", "top_k_per_row",
-                     "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
+                     "top_k_per_row_bf16", "pack_dcp_topk_candidates", "stable_topk_from_gathered_candidates",
                      "fp8_fp4_paged_mqa_logits_bf16", "as_fp32_logits", "fp8_fp4_paged_mqa_logits_fp4q",
                      "fp8_fp4_paged_mqa_logits_topk", "fp8_fp4_paged_mqa_logits_noalloc"):
             if hasattr(L, name):
@@ -329,8 +331,9 @@ def top_k_per_row(logits: torch.Tensor, ke: torch.Tensor, k: int, ks: torch.Tens
                   next_n: int = 1, max_width: int | None = None, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None) -> torch.Tensor:
     """int32 [rows, k]: per row the positions (minus ks) of the k largest logits
-    among columns [ks, ke), ascending, then -1."""
-    _dev(logits, "logits", _F32)
+    among columns [ks, ke), ascending, then -1. fp32 or bf16 logits (bf16 are
+    selected by their exact fp32 values: the same result as on as_fp32_logits)."""
+    _dev(logits, "logits", (torch.float32, torch.bfloat16))
     _dev(ke, "ke", _I32)
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be 2-D with unit inner stride")
@@ -345,8 +348,9 @@ def top_k_per_row(logits: torch.Tensor, ke: torch.Tensor, k: int, ks: torch.Tens
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().top_k_per_row(_p(logits), rows, logits.stride(0), _p(ks), _p(ke.contiguous()), next_n, k,
-                               max_width, _p(out), out.stride(0), _p(workspace), wbytes, _stream()),
+    fn = lib().top_k_per_row_bf16 if logits.dtype == torch.bfloat16 else lib().top_k_per_row
+    _check(fn(_p(logits), rows, logits.stride(0), _p(ks), _p(ke.contiguous()), next_n, k,
+              max_width, _p(out), out.stride(0), _p(workspace), wbytes, _stream()),
            "top_k_per_row")
     return out
 

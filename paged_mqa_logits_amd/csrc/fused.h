@@ -7,7 +7,7 @@
 namespace pml {
 
 struct TopkArgs {
-    const float *logits;
+    const void *logits;  // fp32, or bf16 bits when bf16 is set
     int64_t ld;
     const int32_t *ks;
     const int32_t *ke;
@@ -17,6 +17,7 @@ struct TopkArgs {
     int32_t *out;
     int64_t out_ld;
     const int32_t *skip;  // rows r with skip[r] != 0 are left as they are (NULL: none)
+    int bf16;             // the logits are bf16 bits (uint16_t), not fp32
 };
 
 // Per-row top-k over the logits (top_k_per_row's kernels).

@@ -57,6 +57,29 @@ constexpr int kSmallMaxCols = 8192;  // rows up to this wide take topk_small_ker
 constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled path (measured:
                                     // 32K-64K rows 47 -> 35 us; narrower rows gain nothing)
 
+// Logit elements: fp32, or bf16 bits (E = uint16_t). A bf16 is the upper half
+// of the fp32 with the same value, so the selection on bf16 logits is the
+// selection on their exact fp32 values.
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+template <typename E>
+__device__ __forceinline__ float elem(const E *p, int64_t i) {
+    return to_f32(p[i]);
+}
+// The 4 elements at 4q .. 4q + 3 (16 bytes of fp32, 8 of bf16: element 4q in
+// the low half of the first word).
+template <typename E>
+__device__ __forceinline__ v4f group4(const E *base, int64_t q) {
+    if constexpr (sizeof(E) == 4) {
+        return *(const v4f *)(base + 4 * q);
+    } else {
+        typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+        const v2u32 u = *(const v2u32 *)(base + 4 * q);
+        return v4f{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                   __uint_as_float(u[1] & 0xffff0000u)};
+    }
+}
+
 
 // Float4 walk of one wave's share [q0, q1) of the row's 16-B groups:
 // f(q, x, all_in) gets every group index q (lanes at or past q1 included: they
@@ -69,8 +92,8 @@ constexpr int kSampledMin = 16384;  // rows at least this wide take the sampled 
 // has a round in flight. Loads are unconditional, with addresses clamped to
 // the share's last group, which keeps the compiler's wait counts exact:
 // processing a round waits for that round only.
-template <typename F>
-__device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int q1, F &&f) {
+template <typename E, typename F>
+__device__ __forceinline__ void wave_walk_raw(const E *rowbase, int q0, int q1, F &&f) {
     if (q0 >= q1) return;
     const int lane = lane_id();
     const int qlast = q1 - 1;
@@ -78,7 +101,7 @@ __device__ __forceinline__ void wave_walk_raw(const float *rowbase, int q0, int 
     auto load = [&](v4f *x, int g) {
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j)
-            x[j] = *(const v4f *)(rowbase + 4 * (int64_t)min(g + j * kWave + lane, qlast));
+            x[j] = group4(rowbase, (int64_t)min(g + j * kWave + lane, qlast));
     };
     auto process = [&](const v4f *x, int g) {
 #pragma unroll
@@ -109,20 +132,21 @@ constexpr int kRound = kWave * kWords;
 constexpr int kSampleWords = 8;  // of a wave's first round, the words the bucket is sampled from
 
 // The round of words at r, for r < pe (addresses clamped to pe - 1 in a round that reaches pe).
-__device__ __forceinline__ void load_words(const float *rowbase, int r, int pe, float *x) {
+template <typename E>
+__device__ __forceinline__ void load_words(const E *rowbase, int r, int pe, float *x) {
     const int lane = lane_id();
     if (r + kRound <= pe) {
-        const float *src = rowbase + r + lane;
+        const E *src = rowbase + r + lane;
 #pragma unroll
-        for (int j = 0; j < kWords; ++j) x[j] = src[j * kWave];
+        for (int j = 0; j < kWords; ++j) x[j] = elem(src, j * kWave);
     } else {
 #pragma unroll
-        for (int j = 0; j < kWords; ++j) x[j] = rowbase[min(r + j * kWave + lane, pe - 1)];
+        for (int j = 0; j < kWords; ++j) x[j] = elem(rowbase, min(r + j * kWave + lane, pe - 1));
     }
 }
 
-template <typename F>
-__device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, int pe, int bias, float *xa, F &&f) {
+template <typename E, typename F>
+__device__ __forceinline__ void wave_walk_words(const E *rowbase, int ps, int pe, int bias, float *xa, F &&f) {
     if (ps >= pe) return;
     const int lane = lane_id();
     auto load = [&](float *x, int r) { load_words(rowbase, r, pe, x); };
@@ -149,8 +173,8 @@ __device__ __forceinline__ void wave_walk_words(const float *rowbase, int ps, in
 
 // The same walk with order keys and validity: f(p, key, valid) for the 4
 // elements at positions p .. p + 3.
-template <typename F>
-__device__ __forceinline__ void wave_walk(const float *rowbase, int lo, int hi, int q0, int q1, F &&f) {
+template <typename E, typename F>
+__device__ __forceinline__ void wave_walk(const E *rowbase, int lo, int hi, int q0, int q1, F &&f) {
     wave_walk_raw(rowbase, q0, q1, [&](int q, const v4f &x, bool) {
         uint32_t key[4];
         bool ok[4];
@@ -171,7 +195,7 @@ __device__ __forceinline__ float key_floor_float(uint32_t prefix) {
     return (prefix & 0x80000000u) ? __uint_as_float(prefix & 0x7fffffffu) : __uint_as_float(~prefix);
 }
 
-template <int NT>
+template <int NT, typename E>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     using Cfg = TopkCfg<NT>;
     constexpr int NW = Cfg::NW;
@@ -204,7 +228,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     const int n = hi - lo;
     const int k = a.k;
     int32_t *out = a.out + (int64_t)r * a.out_ld;
-    const float *rowbase = a.logits + (int64_t)r * a.ld;  // 16-B aligned
+    const E *rowbase = (const E *)a.logits + (int64_t)r * a.ld;  // 16-B aligned
 
     if (n <= k) {
         for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
@@ -233,7 +257,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
 
     if (n <= CAP) {
         for (int i = tid; i < n; i += NT) {
-            s_key[i] = order_key(rowbase[lo + i]);
+            s_key[i] = order_key(elem(rowbase, lo + i));
             s_pos[i] = i;
         }
         m = n;
@@ -627,7 +651,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
             __syncthreads();
             for (int i = lo + tid; i < hi; i += NT) {
-                const uint32_t key = order_key(rowbase[i]);
+                const uint32_t key = order_key(elem(rowbase, i));
                 if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & (nbins - 1)], 1u);
             }
             __syncthreads();
@@ -676,7 +700,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
             const int i = base + tid;
             uint32_t key = 0;
             const bool valid = i < n;
-            if (valid) key = order_key(rowbase[lo + i]);
+            if (valid) key = order_key(elem(rowbase, lo + i));
             const uint32_t gt = valid && key > T;
             const uint32_t eq = valid && key == T;
             uint32_t tot;
@@ -719,7 +743,7 @@ __device__ __forceinline__ uint32_t held_key(float f) {
 // Chunk (j, w) covers positions j * NT + 64 w + [0, 64); one block scan over
 // the chunks' counts gives each chunk its first output slot, so selected
 // positions go to consecutive slots in ascending order.
-template <int NT>
+template <int NT, typename E>
 __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
     constexpr int NW = NT / kWave;
     constexpr int kMaxCols = kSmallMaxCols;
@@ -753,7 +777,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
         for (int j = tid; j < k; j += NT) out[j] = j < n ? j : -1;
         return;
     }
-    const float *row = a.logits + (int64_t)r * a.ld + lo;
+    const E *row = (const E *)a.logits + (int64_t)r * a.ld + lo;
     const int nj = (n + NT - 1) / NT;        // rounds j holding positions (uniform)
     // a fresh opaque copy of nj for each loop: the per-round tests are then
     // scalar compares in every loop, not 32 lane masks kept alive in SGPRs
@@ -769,7 +793,7 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
         const int nj0 = rounds();
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-            if (j < nj0) x[j] = row[min(j * NT + tid, n - 1)];
+            if (j < nj0) x[j] = elem(row, min(j * NT + tid, n - 1));
         for (int b = tid; b < kBins; b += NT) s_hist[b] = 0;
         __syncthreads();
         const int nj1 = rounds();
@@ -886,11 +910,19 @@ __global__ __launch_bounds__(NT) void topk_small_kernel(TopkArgs a) {
 }
 
 // Launch the top-k over num_rows rows (arguments validated by the caller).
-int launch_topk(const TopkArgs &a, int num_rows, hipStream_t st) {
+template <typename E>
+static void launch_topk_as(const TopkArgs &a, int num_rows, hipStream_t st) {
     if (a.max_width <= kSmallMaxCols)
-        hipLaunchKernelGGL(topk_small_kernel<256>, dim3(num_rows), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((topk_small_kernel<256, E>), dim3(num_rows), dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(topk_kernel<1024>, dim3(num_rows), dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((topk_kernel<1024, E>), dim3(num_rows), dim3(1024), 0, st, a);
+}
+
+int launch_topk(const TopkArgs &a, int num_rows, hipStream_t st) {
+    if (a.bf16)
+        launch_topk_as<uint16_t>(a, num_rows, st);
+    else
+        launch_topk_as<float>(a, num_rows, st);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }
 
@@ -903,11 +935,9 @@ extern "C" size_t top_k_per_row_workspace_size(int num_rows, int max_width, int 
     return 0;
 }
 
-extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
-                             const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
-                             int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream) {
-    (void)workspace;
-    (void)workspace_bytes;
+static int top_k_rows(const void *logits, bool bf16, int num_rows, int64_t logits_ld, const int32_t *ks,
+                      const int32_t *ke, int next_n, int k, int max_width, int32_t *out, int64_t out_ld,
+                      void *stream) {
     if (num_rows < 0 || next_n < 1 || max_width < 0 || logits_ld < 0) return PML_ERR_SHAPE;
     if (k < 1 || k > PML_MAX_TOPK) return PML_ERR_K;
     if (ks && next_n != 1) return PML_ERR_UNSUPPORTED;
@@ -916,7 +946,23 @@ extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_l
     if (!logits || !ke || !out) return PML_ERR_NULL;
     if (out_ld < k) return PML_ERR_STRIDE;
     if (((uintptr_t)logits & 15) != 0) return PML_ERR_ALIGN;
-    if (logits_ld % 4 != 0) return PML_ERR_STRIDE;
-    pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld, nullptr};
+    if (logits_ld % (bf16 ? 8 : 4) != 0) return PML_ERR_STRIDE;  // 16-byte rows
+    pml::TopkArgs a{logits, logits_ld, ks, ke, next_n, k, max_width, out, out_ld, nullptr, bf16 ? 1 : 0};
     return pml::launch_topk(a, num_rows, (hipStream_t)stream);
+}
+
+extern "C" int top_k_per_row(const float *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
+                             const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
+                             int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return top_k_rows(logits, false, num_rows, logits_ld, ks, ke, next_n, k, max_width, out, out_ld, stream);
+}
+
+extern "C" int top_k_per_row_bf16(const uint16_t *logits, int num_rows, int64_t logits_ld, const int32_t *ks,
+                                  const int32_t *ke, int next_n, int k, int max_width, int32_t *out,
+                                  int64_t out_ld, void *workspace, size_t workspace_bytes, void *stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    return top_k_rows(logits, true, num_rows, logits_ld, ks, ke, next_n, k, max_width, out, out_ld, stream);
 }

@@ -280,3 +280,22 @@ def test_noalloc_limits_and_validation_without_gpu():
     assert pml.status_string(12) != "unknown status"
     # the checks of the main call, before any device query
     assert _noalloc(rows=0) == 0 and _noalloc(rows=-1) == 2 and _noalloc(H=32, rows=0) == 2
+
+def _topk_bf16(**kw):
+    a = dict(logits=FAKE, rows=4, ld=1024, ks=None, ke=FAKE, next_n=1, k=64, max_width=1024, out=FAKE, out_ld=64,
+             ws=None, wbytes=0, stream=None)
+    a.update(kw)
+    return pml.lib().top_k_per_row_bf16(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), 2), (dict(next_n=0), 2), (dict(max_width=-1), 2), (dict(k=0), 7), (dict(k=4097), 7),
+    (dict(logits=None), 1), (dict(ke=None), 1), (dict(out=None), 1), (dict(out_ld=63), 5),
+    (dict(ld=1020), 5), (dict(ld=1028), 5), (dict(logits=P(0x1008)), 6),
+])
+def test_topk_bf16_validation(kw, code):
+    assert _topk_bf16(**kw) == code
+
+
+def test_topk_bf16_zero_rows():
+    assert _topk_bf16(rows=0) == 0

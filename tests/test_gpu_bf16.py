@@ -8,7 +8,8 @@
 * On exactly representable inputs, the oracle's value within the mass bound plus bf16 rounding.
 * The upcast equals the bf16 definition on each row's span and writes nothing else.
 * bf16 logits -> upcast -> top-k meets the top-k acceptance against the oracle
-  with the bf16 tolerance, at the 120K varlen decode size on every row.
+  with the bf16 tolerance, at the 120K varlen decode size on every row, and
+  the top-k over the bf16 logits themselves selects the same, bit for bit.
 """
 import numpy as np
 import pytest
@@ -112,8 +113,10 @@ def test_bf16_decode_path_topk_at_full_size():
     ends = torch.from_numpy(vis.astype(np.int32)).to(G.dev())
     f32 = pml.as_fp32_logits(b16, ends, cols=case.max_ctx)
     got = pml.top_k_per_row(f32, ends, case.topk, max_width=case.max_ctx)
+    direct = pml.top_k_per_row(b16, ends, case.topk, max_width=case.max_ctx)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
+    np.testing.assert_array_equal(direct.cpu().numpy(), got)
     b = b16.view(torch.int16).cpu().numpy().view(np.uint16)[:, : case.max_ctx]
     # shared input: the upcast values, bit-exact top-k
     up = oracle.bf16_to_f32(b).astype(np.float64)
