@@ -26,8 +26,9 @@
 //    holds, the row is read once rather than three times. When the bucket
 //    lies above -inf the pass walks the row in words (lane l holds positions
 //    r + 64 j + l): per word index one float compare, a ballot whose popcount
-//    advances the wave's count, and, for the candidates only, a slot from
-//    mbcnt and one LDS store of value and position.
+//    advances the wave's count, a slot from mbcnt and one LDS store of value
+//    and position (lanes that are not candidates store into a spare entry of
+//    their own, so no word takes a branch).
 //  * Narrower rows, and rows where the sample misjudges (fewer than k
 //    candidates, or a region overflows), take the exact streaming passes: a
 //    full histogram fixes b, then every wave counts, then appends, the
@@ -201,9 +202,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
     constexpr int NW = Cfg::NW;
     constexpr int CAP = Cfg::CAP;
     __shared__ __attribute__((aligned(16))) uint32_t s_hist[kBins];
-    __shared__ uint32_t s_list[2 * CAP];  // keys, then positions: one array, so an entry's
-    uint32_t *const s_key = s_list;       // two stores share an address
-    int32_t *const s_pos = (int32_t *)(s_list + CAP);
+    // keys, then positions: one array, so an entry's two stores share an
+    // address; entries CAP + lane take the sampled append's non-candidates
+    __shared__ uint32_t s_list[2 * (CAP + kWave)];
+    uint32_t *const s_key = s_list;
+    int32_t *const s_pos = (int32_t *)(s_list + CAP + kWave);
     __shared__ __attribute__((aligned(16))) uint32_t s_wave[2 * NW];  // (block_max2 uses two words per wave)
     __shared__ uint32_t s_wcnt[NW];
     __shared__ uint32_t s_pick[2];
@@ -297,21 +300,21 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkArgs a) {
         if (raw) {
             // Word walk over the wave's positions: for each word index the
             // ballot of the candidates gives every candidate its slot (the
-            // count before it), so only candidates are stored. A slot past the
-            // region is clamped to its last entry: the count then exceeds the
-            // region and the list is not used. Order keys are formed in the pack.
+            // count before it). Every lane stores, without a branch: a
+            // non-candidate into a spare entry of its own (CAP + lane). A slot
+            // past the region is clamped to its last entry: the count then
+            // exceeds the region and the list is not used. Order keys are
+            // formed when the regions are lifted into registers.
             const float tf = key_floor_float(sprefix);
             const uint32_t rbase = (uint32_t)wave * RCAP, rlast = rbase + RCAP - 1;
             wave_walk_words(rowbase, ps, pe, lo, x0, [&](int pl, float x, bool full) {
                 const bool c = x >= tf && (full || pl < pe - lo);
                 const uint64_t bm = __builtin_amdgcn_ballot_w64(c);
-                if (c) {
-                    const uint32_t at = __builtin_amdgcn_mbcnt_hi(
-                        (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, rbase + cnt));
-                    const uint32_t slot = min(at, rlast);
-                    s_key[slot] = __float_as_uint(x);
-                    s_pos[slot] = pl;
-                }
+                const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, rbase + cnt));
+                const uint32_t slot = c ? min(at, rlast) : (uint32_t)(CAP + lane);
+                s_key[slot] = __float_as_uint(x);
+                s_pos[slot] = pl;
                 cnt = __builtin_amdgcn_readfirstlane(cnt + (uint32_t)__builtin_popcountll(bm));
             });
         } else {
