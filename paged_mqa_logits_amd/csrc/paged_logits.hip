@@ -3,18 +3,18 @@
 //
 // Design (gfx950):
 //  * Persistent grid of num_CUs workgroups. The schedule cuts the ordered
-//    (row-piece, key-block) units into chunks of about equal cost, several
-//    per workgroup; workgroups take chunks in turn from a device-wide counter
-//    and walk each one's contiguous run of units, so the grid stays balanced
-//    whatever slows one workgroup down. A row-piece is up to 8 rows of one
-//    request ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a request are
-//    processed together), so each key page is read from HBM once for all of
-//    them.
-//  * The 4 waves split the current piece's blocks into contiguous quarters.
-//    Each loads its pages from HBM straight into VGPRs, two buffers deep
-//    (one block in flight while one is scored), and scores them against
-//    every row of the piece, whose q and w sit in LDS. Waves meet at a
-//    barrier only when the piece changes.
+//    (row-piece, key-block) units into one range of about equal cost per
+//    workgroup; workgroup c walks range c up to its split point, and the
+//    ranges' last eighths are dealt out at run time from 8 counters in the
+//    call's workspace, so the grid stays balanced whatever slows one
+//    workgroup down. A row-piece is up to 8 rows of one request
+//    ("[Bugfix][GLM-5.3-Flash] ...", Purpose: rows of a request are processed
+//    together), so each key page is read from HBM once for all of them.
+//  * The 4 waves take the current piece's blocks in turn (wave w: blocks
+//    w, w + 4, ...). Each loads its pages from HBM straight into VGPRs, two
+//    buffers deep (one block in flight while one is scored), and scores them
+//    against every row of the piece, whose q and w sit in LDS. Waves meet at
+//    a barrier only when the piece changes.
 //  * Logit stores are issued as inline asm one step after the block is
 //    scored, so the compiler waits for a page exactly and the page behind
 //    it stays in flight.

@@ -21,8 +21,9 @@ kernels still gives each workload's durations.
 counter in a counter_collection.csv (raw values, summed over the hardware
 instances the CSV lists).
 
-``digest`` prints a hash of the decode-logits kernel sources; a traffic
-figure is only valid for the sources it was measured on.
+``digest`` prints a hash of the decode-logits kernel sources (their code:
+comments and blank lines are left out, so editing a comment keeps it); a
+traffic figure is only valid for the code it was measured on.
 """
 from __future__ import annotations
 
@@ -37,12 +38,36 @@ LOGITS_SOURCES = ("pml_device.h", "rows.h", "logits_core.h", "paged_logits.hip")
 COPY_KERNEL = "copyBuffer"  # the runtime's device-to-device copy kernel
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines
+    (string and character literals are kept whole)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def source_digest() -> str:
-    """sha256 (first 16 hex digits) over the decode-logits kernel sources."""
+    """sha256 (first 16 hex digits) over the code of the decode-logits kernel sources."""
     h = hashlib.sha256()
     for name in LOGITS_SOURCES:
         h.update(name.encode())
-        h.update((CSRC / name).read_bytes())
+        h.update(_code_only((CSRC / name).read_text()).encode())
     return h.hexdigest()[:16]
 
 
