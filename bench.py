@@ -22,7 +22,8 @@ with the host's core count and CPU model.
 
 --all adds one line per further workload, each timed the same way: uniform
 decode, MXFP4 keys, MXFP4 keys with fp4 q, the tiny decode, the 120K decode
-with bf16 logits (the top-k reads them directly), the fused logits + top-k call, the exact
+with bf16 logits (the top-k reads them directly; the valid-span upcast to fp32 is
+timed beside the step), the fused logits + top-k call, the exact
 top-k merge over 8 context-parallel ranks, and ragged prefill logits.
 """
 from __future__ import annotations
@@ -439,12 +440,29 @@ def run_bf16(args):
     c = ob.case
     t_log = float(p2[:, 1].mean()) * 1e-3
     kbytes = ob.req_tokens * BYTES_PER_TOKEN[c.kv_format]
+    # The valid-span upcast of the same bf16 logits, outside the step (the
+    # step's top-k reads bf16 directly): 2 bytes read and 4 written per column
+    # below each row's end.
+    lb = ob.logits_bf16
+    up = torch.empty_strided(lb.shape, (lb.stride(0), 1), dtype=torch.float32, device=lb.device)
+    for _ in range(max(args.warmup, 1)):
+        pml.as_fp32_logits(lb, ob.lens, out=up, cols=c.max_ctx)
+    uev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in uev:
+        e0.record()
+        pml.as_fp32_logits(lb, ob.lens, out=up, cols=c.max_ctx)
+        e1.record()
+    torch.cuda.synchronize()
+    t_up = float(np.mean([e0.elapsed_time(e1) for e0, e1 in uev])) * 1e-3
+    ubytes = 6 * int(ob.lens.clamp(0, c.max_ctx).sum())
     return {"workload": "varlen_spec_decode_fp8_120k_bf16_logits", "ms_per_step": w2 / args.steps * 1e3,
             "ms_schedule": float(p2[:, 0].mean()), "ms_logits": t_log * 1e3,
             "ms_topk": float(p2[:, 2].mean()),
             "scored_Ktok_s": ob.pairs / (w2 / args.steps) / 1e3,
             "logits_hbm_GBs": kbytes / t_log / 1e9, "logits_hbm_frac": kbytes / t_log / 1e9 / PEAK_HBM_GBS,
-            "logits_out_bytes": c.rows * c.max_ctx * 2}
+            "logits_out_bytes": c.rows * c.max_ctx * 2,
+            "ms_upcast": t_up * 1e3, "upcast_bytes": ubytes, "upcast_GBs": ubytes / t_up / 1e9,
+            "upcast_hbm_frac": ubytes / t_up / 1e9 / PEAK_HBM_GBS}
 
 
 def run_fused(args):
