@@ -193,8 +193,8 @@ int fp8_fp4_paged_mqa_logits(const void *q, const uint8_t *q_scale, int num_rows
  *   cu_seqlen_ks, cu_seqlen_ke  int32 [M]; bounds are clamped to [0, N].
  *   logits   fp32 [M][logits_ld], logits_ld >= N, a multiple of 4, 16-B aligned.
  *            Columns [0, N) of every row are written; [N, logits_ld) are not.
- * M <= 524280 (else PML_ERR_SHAPE). M == 0 or N == 0 returns PML_OK and
- * launches nothing.
+ * M <= 524280 and N <= 2^31 - 257 (else PML_ERR_SHAPE). M == 0 or N == 0
+ * returns PML_OK and launches nothing.
  */
 int mqa_logits(const void *q, int M, int num_heads, int head_dim, const void *k,
                const float *k_scale, int N, const float *weights, const int32_t *cu_seqlen_ks,
@@ -361,7 +361,9 @@ int fp8_fp4_paged_mqa_logits_topk(const void *q, int num_rows, int next_n, int n
  * the row's end are converted, and the row stride is kept).
  *   logits     bf16 bits [num_rows][logits_ld], 16-B aligned, logits_ld a
  *              multiple of 8 and >= cols.
- *   cols       the logits width (max_ctx); row ends are clamped to [0, cols].
+ *   cols       the logits width (max_ctx), at most 134215680 (65535 chunks of
+ *              2048 columns; else PML_ERR_SHAPE); row ends are clamped to
+ *              [0, cols].
  *   row_ends   int32 [num_rows].
  *   out        fp32 [num_rows][out_ld], 16-B aligned, out_ld a multiple of 4
  *              and >= cols. Columns [0, row_end) receive the exact fp32 value

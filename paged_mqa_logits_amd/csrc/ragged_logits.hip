@@ -323,6 +323,9 @@ extern "C" int mqa_logits(const void *q, int M, int num_heads, int head_dim, con
                           const int32_t *cu_seqlen_ks, const int32_t *cu_seqlen_ke, float *logits,
                           int64_t logits_ld, void *stream) {
     if (M < 0 || N < 0) return PML_ERR_SHAPE;
+    // (pieces of 8 rows fill at most 65535 grid rows; key positions plus a
+    // block stay inside int32)
+    if (M > 65535 * pml::kGMax || N > 0x7fffffff - 256) return PML_ERR_SHAPE;
     if (num_heads != PML_HEADS || head_dim != PML_HEAD_DIM) return PML_ERR_SHAPE;
     if (M == 0 || N == 0) return PML_OK;  // nothing to write
     if (!q || !k || !k_scale || !weights || !cu_seqlen_ks || !cu_seqlen_ke || !logits) return PML_ERR_NULL;
@@ -343,7 +346,6 @@ extern "C" int mqa_logits(const void *q, int M, int num_heads, int head_dim, con
     pml::RaggedArgs a{(const uint8_t *)q, weights, (const uint8_t *)k, k_scale, N, cu_seqlen_ks,
                       cu_seqlen_ke, M, logits, logits_ld, chunk};
     const dim3 grid((nb + chunk - 1) / chunk, pieces);
-    if (grid.y > 65535) return PML_ERR_SHAPE;
     hipLaunchKernelGGL(pml::ragged_rows_kernel, grid, dim3(pml::kRThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }

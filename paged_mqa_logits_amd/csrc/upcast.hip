@@ -57,9 +57,10 @@ extern "C" int as_fp32_logits(const uint16_t *logits, int num_rows, int64_t logi
     if (!logits || !row_ends || !out) return PML_ERR_NULL;
     if (logits_ld < cols || out_ld < cols || logits_ld % 8 != 0 || out_ld % 4 != 0) return PML_ERR_STRIDE;
     if (((uintptr_t)logits & 15) != 0 || ((uintptr_t)out & 15) != 0) return PML_ERR_ALIGN;
+    const int64_t chunks = ((int64_t)cols + pml::kUpCols - 1) / pml::kUpCols;
+    if (chunks > 65535) return PML_ERR_SHAPE;
     pml::UpcastArgs a{logits, logits_ld, cols, row_ends, out, out_ld};
-    const dim3 grid(num_rows, (cols + pml::kUpCols - 1) / pml::kUpCols);
-    if (grid.y > 65535) return PML_ERR_SHAPE;
+    const dim3 grid(num_rows, (unsigned)chunks);
     hipLaunchKernelGGL(pml::upcast_kernel, grid, dim3(pml::kUpThreads), 0, (hipStream_t)stream, a);
     return hipGetLastError() == hipSuccess ? PML_OK : PML_ERR_HIP;
 }

@@ -203,9 +203,35 @@ def _upcast(**kw):
     (dict(rows=-1), 2), (dict(cols=-1), 2), (dict(src=None), 1), (dict(ends=None), 1), (dict(out=None), 1),
     (dict(ld=1020), 5), (dict(ld=996), 5), (dict(out_ld=998), 5), (dict(out_ld=996), 5),
     (dict(src=P(0x1008)), 6), (dict(out=P(0x1004)), 6),
+    # one chunk past 65535 x 2048 columns
+    (dict(cols=134215681, ld=134215688, out_ld=134215688), 2),
 ])
 def test_upcast_validation(kw, code):
     assert _upcast(**kw) == code
+
+
+def _ragged(**kw):
+    a = dict(q=FAKE, M=16, heads=64, dim=128, k=FAKE, k_scale=FAKE, N=1000, w=FAKE, ks=FAKE, ke=FAKE,
+             out=FAKE, ld=1000, stream=None)
+    a.update(kw)
+    return pml.lib().mqa_logits(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(M=-1), 2), (dict(N=-1), 2), (dict(heads=32), 2), (dict(dim=64), 2),
+    (dict(M=524281), 2), (dict(N=2 ** 31 - 256, ld=2 ** 31), 2),
+    (dict(q=None), 1), (dict(k_scale=None), 1), (dict(ke=None), 1), (dict(out=None), 1),
+    (dict(ld=996), 5), (dict(ld=1002), 5),
+    (dict(q=P(0x1008)), 6), (dict(k=P(0x1004)), 6), (dict(out=P(0x1008)), 6), (dict(k_scale=P(0x1002)), 6),
+])
+def test_ragged_validation(kw, code):
+    assert _ragged(**kw) == code
+
+
+def test_ragged_empty_is_ok_without_gpu():
+    assert _ragged(M=0) == 0
+    assert _ragged(N=0) == 0
+    assert _ragged(M=0, q=None, out=None) == 0
 
 
 def test_upcast_empty_is_ok():
