@@ -7,8 +7,10 @@
  * Plain C, one loop per definition, fp64 accumulation, OpenMP over output
  * cells. Every function states the passage it follows.
  *
- * Score (the indexer's MQA logit; the pages name it but never write it, so
- * the statement of the indexer score in the problem definition fixes it):
+ * Score (the indexer's MQA logit: the pages name it and pass its inputs, q,
+ * the per-token key scale and the per-head weights, but never write it out;
+ * this is the plain weighted-ReLU reading of those inputs, with no other
+ * constants):
  *     logit[r, s] = sum_h w[r,h] * max(0, scale_k[s] * <q[r,h,:], k[s,:]>)
  * for visible key tokens s, and -inf for masked ones.
  */
