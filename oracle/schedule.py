@@ -28,7 +28,7 @@ from __future__ import annotations
 import numpy as np
 
 G_MAX = 8
-COST_BASE = 4
+COST_BASE = 3
 MIN_STEP = 64  # tokens per unit: a block_kv 32 cache is taken two pages at a time
 
 

@@ -18,7 +18,7 @@ constexpr int kWave = 64;
 #define PML_GMAX 8
 #endif
 constexpr int kGMax = PML_GMAX;  // rows of one piece scored against a shared key block
-constexpr int kCostBase = 4;    // schedule weight of a block: kCostBase + rows
+constexpr int kCostBase = 3;    // schedule weight of a block: kCostBase + rows (3 measured best of 1, 2, 3, 4, 8)
 
 // Tokens per unit of work (one step of a wave): a block_kv 32 cache is scored
 // two pages at a time, so every step covers 64 tokens.

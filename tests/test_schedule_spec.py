@@ -43,7 +43,7 @@ def test_hand_example():
     table = S.piece_table(lens, 4, 1, False, idx, 64)
     assert table == [(0, 3, 3, 3 * (S.COST_BASE + 3)), (3, 1, 1, S.COST_BASE + 1)]
     sched = _check(lens, 4, 1, False, idx, 64, 2)
-    # (COST_BASE 4) total = 21 + 5 = 26; chunk 1 starts at offset 13 -> piece 0, block 13 // 7 = 1
+    # (COST_BASE 3) total = 18 + 4 = 22; chunk 1 starts at offset 11 -> piece 0, block 11 // 6 = 1
     assert sched.tolist() == [[0, 0], [0, 1], [4, 0]]
 
 
